@@ -1,0 +1,174 @@
+/*
+ * nomas.h -- C ABI of libnomas: segment-causal attention over a lifelong INT8
+ * KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (Hy-Nomas pages, cited by title and section):
+ *  - "Hy-Nomas：腾讯混元交互式世界模型，8 步生成 720p 可控视频" (comfyui-wiki news),
+ *    section 一个世界，分段生成: video is generated segment by segment; each
+ *    segment attends to the key/value cache of every earlier segment, and
+ *    attention is causal between segments (a segment never needs a later one).
+ *  - same page, section 模型内部: 16 heads x 128, 3D RoPE with axis sizes
+ *    [16, 56, 56] and theta 256, latent patch 1x1x1 (880 tokens per 1280x704
+ *    latent frame); camera extrinsics injected by cross-attention.
+ *  - same page, section 单张 4090 配置, and "Hy-Nomas:8B 参数、单张 4090 跑 60 秒
+ *    可控世界" (huaweicloud blog), section 3.5 table: cached keys and values are
+ *    stored as INT8 while attention is computed in BF16.
+ *  - huaweicloud blog, section 2.1: the text and video K,V of each segment are
+ *    cached and handed to the next segment.
+ *  - comfyui-wiki news, section 相机控制作为一等输入: c2w [N,4,4], normalised,
+ *    grouped per 4 video frames into 64-d inputs that video tokens query by
+ *    cross-attention; translation scale 1.0 and rotation scale 2.5.
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers marked "device" are caller-owned device memory (HBM) on
+ *    the current HIP device; pointers marked "host" are ordinary host memory.
+ *    The library never frees or keeps caller pointers.
+ *  - bf16 tensors hold raw bfloat16 bit patterns (nomas_bf16).  Token-major
+ *    tensors are [L][H][128] (token, head, channel), 16-byte aligned.
+ *  - The INT8 cache is head-major: codes [H][cap][128] (int8), scales
+ *    [H][cap] (float32), one scale per (token, head).  Keys are cached after
+ *    RoPE, so cached entries carry no position.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it; they never synchronise.
+ *  - Arguments are checked on the host before anything is enqueued.  A
+ *    non-zero return means nothing was launched and no output was written:
+ *      NOMAS_EINVAL       null pointer, bad size, misaligned pointer, token
+ *                         counts that disagree with the segment descriptors
+ *      NOMAS_ECAPACITY    the cache cannot hold the appended tokens
+ *      NOMAS_EUNSUPPORTED a size outside the library's fixed limits
+ *      NOMAS_EHIP         a HIP runtime call or launch failed
+ *    A fault inside a kernel surfaces at the caller's next synchronisation.
+ *  - The only memory the library owns is a RoPE cos/sin table per device,
+ *    built on first use and kept until the process ends.
+ *  - Token layout of a segment: its n_text text tokens first, then its
+ *    T*Hg*Wg video tokens in (t, h, w) row-major order, t in [t0, t0+T).
+ *    Text tokens are not rotated; video token (t, h, w) uses t as the
+ *    absolute latent-frame index and h, w counted from 0.
+ */
+#ifndef NOMAS_H
+#define NOMAS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t nomas_bf16;
+
+/* One segment of tokens: [n_text text | T*Hg*Wg video, (t,h,w) row-major]. */
+typedef struct {
+    int32_t n_text, t0, T, Hg, Wg;
+} nomas_seg;
+
+enum {
+    NOMAS_OK = 0,
+    NOMAS_EINVAL = -1,
+    NOMAS_ECAPACITY = -2,
+    NOMAS_EHIP = -3,
+    NOMAS_EUNSUPPORTED = -4
+};
+
+#define NOMAS_HEAD_DIM 128
+#define NOMAS_MAX_SEGS 64          /* segments per call (new or packed)        */
+#define NOMAS_MAX_T 16384          /* latent-frame positions t < NOMAS_MAX_T   */
+#define NOMAS_MAX_HW 1024          /* grid positions h, w < NOMAS_MAX_HW       */
+#define NOMAS_MAX_CAM 128          /* camera tokens per call                   */
+
+/*
+ * 3D RoPE (comfyui-wiki news, 模型内部: axes [16, 56, 56], theta 256).
+ * Channels [0,16) turn with t, [16,72) with h, [72,128) with w.  In a chunk
+ * of width d, pair (2i, 2i+1) turns by phi = p * 256^(-2i/d):
+ *   (x0, x1) -> (x0 cos phi - x1 sin phi, x0 sin phi + x1 cos phi).
+ * x, y: device, [L][H][128] bf16 with L = sum of the segments' token counts;
+ * y may equal x (in place).  The rotation is evaluated in double precision
+ * and rounded once to bf16 (nearest even).  Text tokens are copied unchanged.
+ */
+int nomas_rope3d(const nomas_bf16* x, nomas_bf16* y, const nomas_seg* segs, int n_segs,
+                 int H, void* stream);
+
+/*
+ * INT8 quantise-and-append of a segment's K and V into the lifelong cache
+ * (cached K/V stored as INT8: comfyui-wiki news, 单张 4090 配置; huaweicloud
+ * blog, section 3.5).  For every (token i, head h) row of 128 values:
+ *   a = max |x|,  s = fl32(a / 127),  q = clamp(rne(x / s), -127, 127)
+ * with the exact quotient x/s (a = 0 gives s = 0 and q = 0).  Row (i, h) of
+ * k_rot goes to k_codes[h][len+i][:] / k_scale[h][len+i]; likewise v.
+ * k_rot, v: device, [L][H][128] bf16 (keys already rotated).
+ * k_codes, v_codes: device, [H][cap][128] int8.  k_scale, v_scale: device,
+ * [H][cap] float32.  len: host, in = tokens already cached, out = len + L.
+ * L = 0 is a no-op.  ECAPACITY if len + L > cap (nothing written, len kept).
+ */
+int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t L, int H,
+                          int8_t* k_codes, int8_t* v_codes, float* k_scale, float* v_scale,
+                          int64_t cap, int64_t* len, void* stream);
+
+/*
+ * Segment-causal joint attention of the current segment(s) (comfyui-wiki
+ * news, 一个世界，分段生成; huaweicloud blog, section 2.1).
+ * Query i of new segment a attends to every cached token and to the new
+ * tokens of segments 0..a: bidirectional inside its own segment, never to a
+ * later segment.  With one new segment this is inference; several new
+ * segments pack a training sequence (block-causal).
+ *   s_ij = sm_scale * <RoPE(q_i), K_j>,  o_i = softmax_j(s_ij) . V_j
+ * over the allowed j; lse_i = ln sum_j exp(s_ij).
+ * BF16 compute: RoPE(q), RoPE(k_new) are rounded to bf16; cached entries
+ * enter as bf16(fl32(code * scale)); products accumulate in fp32.
+ * q, k_new, v_new: device, [Ln][H][128] bf16, q and k_new BEFORE RoPE
+ *   (rotated on load), Ln = sum of the new segments' token counts.
+ * k_codes, v_codes, k_scale, v_scale: device cache as for
+ *   nomas_kv_quant_append; its first cache_len entries are used (may be 0,
+ *   then the cache pointers may be NULL).
+ * sm_scale > 0 (1/sqrt(128) for the model).
+ * out: device, [Ln][H][128] bf16.  lse: device [H][Ln] float32 or NULL.
+ * n_new_segs in [1, NOMAS_MAX_SEGS].
+ */
+int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,
+                   const nomas_seg* new_segs, int n_new_segs,
+                   const int8_t* k_codes, const int8_t* v_codes,
+                   const float* k_scale, const float* v_scale,
+                   int64_t cap, int64_t cache_len, int H, float sm_scale,
+                   nomas_bf16* out, float* lse, void* stream);
+
+/*
+ * Camera tokens of one turn (comfyui-wiki news, 相机控制作为一等输入).
+ * Poses are made relative to the first frame (R0^T R_k, R0^T (t_k - t0)),
+ * translations are multiplied by translation_scale and rotation angles
+ * (axis-angle) by rotation_scale; 4 consecutive 4x4 matrices, row-major,
+ * form one 64-value token.  Host-side: c2w host [n_frames][4][4] float64,
+ * n_frames a positive multiple of 4; tokens host [n_frames/4][64] float32.
+ */
+int nomas_cam_tokens(const double* c2w, int n_frames, double translation_scale,
+                     double rotation_scale, float* tokens);
+
+/*
+ * Camera cross-attention (comfyui-wiki news, 相机控制作为一等输入 and 模型内部:
+ * extrinsic embedding injected by cross-attention).  Kc = bf16(cam . w_k),
+ * Vc = bf16(cam . w_v) per head; every query attends to all Nc camera tokens:
+ *   out_i = softmax_n(sm_scale <q_i, Kc_n>) . Vc_n    (no RoPE)
+ * q: device [Lq][H][128] bf16 (video-token queries).  cam: device [Nc][64]
+ * float32.  w_k, w_v: device [64][H*128] bf16.  out: device [Lq][H][128]
+ * bf16.  1 <= Nc <= NOMAS_MAX_CAM.
+ */
+int nomas_cam_xattn(const nomas_bf16* q, int64_t Lq, int H, const float* cam, int Nc,
+                    const nomas_bf16* w_k, const nomas_bf16* w_v, float sm_scale,
+                    nomas_bf16* out, void* stream);
+
+/*
+ * Host copy of the library's float32 RoPE table for one axis (0 = t, 1 = h,
+ * 2 = w): cos_out/sin_out host [npos][d/2] with entry (p, i) =
+ * fl32(cos(p * 256^(-2i/d))).  Needs no GPU.
+ */
+int nomas_rope_table(int axis, int npos, float* cos_out, float* sin_out);
+
+/* Static description of an error code; never NULL. */
+const char* nomas_strerror(int code);
+
+/* Library version string. */
+const char* nomas_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NOMAS_H */

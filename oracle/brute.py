@@ -151,6 +151,7 @@ def cam_xattn(q, cam, w_k, w_v, H, sm_scale, bf16_operands=True):
     w_k/w_v [64][H*128] (floats).  Returns out [Lq][H][128]."""
     rnd = round_bf16 if bf16_operands else (lambda v: v)
     Nc = len(cam)
+    cam = [[rnd(v) for v in row] for row in cam]
     Kc = [[rnd(math.fsum(cam[n][i] * w_k[i][c] for i in range(64))) for c in range(H * D)] for n in range(Nc)]
     Vc = [[rnd(math.fsum(cam[n][i] * w_v[i][c] for i in range(64))) for c in range(H * D)] for n in range(Nc)]
     out = []

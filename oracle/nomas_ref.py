@@ -32,8 +32,9 @@ Readings where the pages are silent (each is listed in the design notes):
   * Camera tokens: poses made relative to the first frame of the turn,
     translation x translation_scale, rotation angle x rotation_scale
     (axis-angle), 4 consecutive 4x4 matrices flattened row-major into 64
-    values.  Kc = bf16(cam @ Wk), Vc = bf16(cam @ Wv); every video query
-    attends to every camera token of its turn.
+    values.  The embedding is a BF16 linear layer: Kc = bf16(bf16(cam) @ Wk),
+    Vc = bf16(bf16(cam) @ Wv); every video query attends to every camera
+    token of its turn.
 """
 from __future__ import annotations
 
@@ -341,9 +342,13 @@ def cam_tokens(c2w, translation_scale=1.0, rotation_scale=2.5) -> np.ndarray:
 
 
 def cam_kv(cam, w_k_bits, w_v_bits, H, bf16_operands=True):
-    """Camera keys and values [Nc][H][128]: cam [Nc][64] times the bf16
-    projection weights [64][H*128]; rounded to BF16 as attention operands."""
+    """Camera keys and values [Nc][H][128]: the camera embedding is a linear
+    layer, and linear layers run in BF16 ([CW] 单张 4090 配置), so the tokens
+    cam [Nc][64] are rounded to bf16, multiplied exactly by the bf16 weights
+    [64][H*128], and the products rounded to bf16 as attention operands."""
     cam = np.asarray(cam, dtype=np.float64)
+    if bf16_operands:
+        cam = bf16_round(cam)
     Kc = cam @ bf16_bits_to_f64(w_k_bits)
     Vc = cam @ bf16_bits_to_f64(w_v_bits)
     if bf16_operands:

@@ -1,0 +1,12 @@
+"""segment_causal_attention_amd: Python binding of libnomas, segment-causal
+attention over a lifelong INT8 KV cache for AMD MI355X (gfx950).
+
+The compute path is the HIP library libnomas.so (C ABI: include/nomas.h);
+this package only marshals arguments.  Build it with
+``python -m segment_causal_attention_amd.build`` (or __graft_entry__.build()).
+"""
+from ._lib import (  # noqa: F401
+    EHIP, ECAPACITY, EINVAL, EUNSUPPORTED, HEAD_DIM, MAX_CAM, MAX_SEGS, OK, SM_SCALE, SYMBOLS,
+    NomasError, Seg, cam_tokens, cam_xattn, kv_quant_append, lib, rope3d, rope_table, seg_array,
+    seg_attn, seg_tokens, strerror, version,
+)

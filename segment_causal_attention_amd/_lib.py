@@ -1,0 +1,226 @@
+"""ctypes binding of libnomas (C ABI in include/nomas.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libnomas.so.  Device tensors are torch tensors (bf16 tensors may be
+torch.bfloat16 or int16 holding the raw bits); torch supplies the memory and
+the current stream.  There is no fallback: if the library is missing, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnomas.so")
+
+OK, EINVAL, ECAPACITY, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4
+HEAD_DIM = 128
+MAX_SEGS = 64
+MAX_CAM = 128
+SM_SCALE = 1.0 / math.sqrt(HEAD_DIM)
+
+SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_cam_tokens",
+           "nomas_cam_xattn", "nomas_rope_table", "nomas_strerror", "nomas_version")
+
+
+class NomasError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (where, strerror(code), code))
+
+
+class Seg(ctypes.Structure):
+    _fields_ = [("n_text", ctypes.c_int32), ("t0", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("Hg", ctypes.c_int32), ("Wg", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_D = ctypes.c_double
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnomas.so (built in-tree by segment_causal_attention_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libnomas.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.nomas_rope3d.argtypes = [_P, _P, ctypes.POINTER(Seg), _I, _I, _P]
+        L.nomas_kv_quant_append.argtypes = [_P, _P, _I64, _I, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64), _P]
+        L.nomas_seg_attn.argtypes = [_P, _P, _P, ctypes.POINTER(Seg), _I, _P, _P, _P, _P, _I64, _I64, _I, _F,
+                                     _P, _P, _P]
+        L.nomas_cam_tokens.argtypes = [_P, _I, _D, _D, _P]
+        L.nomas_cam_xattn.argtypes = [_P, _I64, _I, _P, _I, _P, _P, _F, _P, _P]
+        L.nomas_rope_table.argtypes = [_I, _I, _P, _P]
+        L.nomas_strerror.argtypes = [_I]
+        L.nomas_strerror.restype = ctypes.c_char_p
+        L.nomas_version.argtypes = []
+        L.nomas_version.restype = ctypes.c_char_p
+        for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_cam_tokens",
+                     "nomas_cam_xattn", "nomas_rope_table"):
+            getattr(L, name).restype = _I
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().nomas_strerror(int(code)).decode()
+
+
+def version() -> str:
+    return lib().nomas_version().decode()
+
+
+def _check(rc: int, where: str):
+    if rc != OK:
+        raise NomasError(rc, where)
+
+
+def seg_array(segs):
+    """A ctypes array of nomas_seg from (n_text, t0, T, Hg, Wg) tuples or objects with astuple()."""
+    tup = [tuple(s.astuple()) if hasattr(s, "astuple") else tuple(s) for s in segs]
+    arr = (Seg * max(1, len(tup)))()
+    for i, t in enumerate(tup):
+        arr[i] = Seg(*[int(v) for v in t])
+    return arr, len(tup)
+
+
+def seg_tokens(segs) -> int:
+    n = 0
+    for s in segs:
+        t = tuple(s.astuple()) if hasattr(s, "astuple") else tuple(s)
+        n += t[0] + t[2] * t[3] * t[4]
+    return n
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, shape=None, elem=2):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.element_size() != elem:
+        raise ValueError("%s must have %d-byte elements" % (name, elem))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+# ----------------------------------------------------------------------------
+# entry points (same names as the C ABI, without the prefix)
+
+
+def rope3d(x, segs, out=None, stream=None):
+    """3D RoPE of x [L][H][128] (bf16) -> out (new tensor unless given; may be x)."""
+    import torch
+    L, H = x.shape[0], x.shape[1]
+    _dev(x, "x", (seg_tokens(segs), H, HEAD_DIM))
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.shape)
+    arr, n = seg_array(segs)
+    _check(lib().nomas_rope3d(_ptr(x), _ptr(out), arr, n, H, _stream(stream)), "nomas_rope3d")
+    return out
+
+
+def kv_quant_append(k_rot, v, k_codes, v_codes, k_scale, v_scale, length: int, stream=None) -> int:
+    """Quantise k_rot, v [L][H][128] into the cache at `length`; returns the new length."""
+    L, H = k_rot.shape[0], k_rot.shape[1]
+    _dev(k_rot, "k_rot", (L, H, HEAD_DIM))
+    _dev(v, "v", (L, H, HEAD_DIM))
+    cap = k_codes.shape[1]
+    _dev(k_codes, "k_codes", (H, cap, HEAD_DIM), 1)
+    _dev(v_codes, "v_codes", (H, cap, HEAD_DIM), 1)
+    _dev(k_scale, "k_scale", (H, cap), 4)
+    _dev(v_scale, "v_scale", (H, cap), 4)
+    ln = _I64(int(length))
+    _check(lib().nomas_kv_quant_append(_ptr(k_rot), _ptr(v), L, H, _ptr(k_codes), _ptr(v_codes),
+                                       _ptr(k_scale), _ptr(v_scale), cap, ctypes.byref(ln), _stream(stream)),
+           "nomas_kv_quant_append")
+    return int(ln.value)
+
+
+def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None, v_scale=None,
+             cache_len: int = 0, sm_scale: float = SM_SCALE, out=None, lse=None, stream=None):
+    """Segment-causal attention; returns out [Ln][H][128] bf16 (lse filled if given)."""
+    import torch
+    Ln, H = q.shape[0], q.shape[1]
+    shp = (seg_tokens(new_segs), H, HEAD_DIM)
+    _dev(q, "q", shp)
+    _dev(k_new, "k_new", shp)
+    _dev(v_new, "v_new", shp)
+    cap = 0
+    if cache_len > 0:
+        cap = k_codes.shape[1]
+        _dev(k_codes, "k_codes", (H, cap, HEAD_DIM), 1)
+        _dev(v_codes, "v_codes", (H, cap, HEAD_DIM), 1)
+        _dev(k_scale, "k_scale", (H, cap), 4)
+        _dev(v_scale, "v_scale", (H, cap), 4)
+    elif k_codes is not None:
+        cap = k_codes.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", shp)
+    if lse is not None:
+        _dev(lse, "lse", (H, Ln), 4)
+    arr, n = seg_array(new_segs)
+    _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_new), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
+                                _ptr(k_scale), _ptr(v_scale), cap, int(cache_len), H, float(sm_scale),
+                                _ptr(out), _ptr(lse), _stream(stream)), "nomas_seg_attn")
+    return out
+
+
+def cam_tokens(c2w, translation_scale: float = 1.0, rotation_scale: float = 2.5) -> np.ndarray:
+    """Host: c2w [N][4][4] float64 -> camera tokens [N/4][64] float32."""
+    c = np.ascontiguousarray(c2w, dtype=np.float64)
+    N = c.shape[0]
+    out = np.zeros((N // 4, 64), np.float32)
+    _check(lib().nomas_cam_tokens(c.ctypes.data, N, float(translation_scale), float(rotation_scale),
+                                  out.ctypes.data), "nomas_cam_tokens")
+    return out
+
+
+def cam_xattn(q, cam, w_k, w_v, sm_scale: float = SM_SCALE, out=None, stream=None):
+    """Camera cross-attention of q [Lq][H][128] over cam [Nc][64] (float32, device)."""
+    import torch
+    Lq, H = q.shape[0], q.shape[1]
+    _dev(q, "q", (Lq, H, HEAD_DIM))
+    Nc = cam.shape[0]
+    _dev(cam, "cam", (Nc, 64), 4)
+    _dev(w_k, "w_k", (64, H * HEAD_DIM))
+    _dev(w_v, "w_v", (64, H * HEAD_DIM))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.shape)
+    _check(lib().nomas_cam_xattn(_ptr(q), Lq, H, _ptr(cam), Nc, _ptr(w_k), _ptr(w_v), float(sm_scale),
+                                 _ptr(out), _stream(stream)), "nomas_cam_xattn")
+    return out
+
+
+def rope_table(axis: int, npos: int):
+    """Host copy of the library's float32 RoPE table: (cos, sin) [npos][d/2]."""
+    d = 16 if axis == 0 else 56
+    c = np.zeros((npos, d // 2), np.float32)
+    s = np.zeros((npos, d // 2), np.float32)
+    _check(lib().nomas_rope_table(axis, npos, c.ctypes.data, s.ctypes.data), "nomas_rope_table")
+    return c, s

@@ -1,0 +1,102 @@
+// Internal definitions shared by the libnomas kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nomas.h"
+
+namespace nomas {
+
+constexpr int D = NOMAS_HEAD_DIM;       // channels per head
+constexpr int NPAIR_T = 8;              // RoPE pairs on the t axis (16 channels)
+constexpr int NPAIR_HW = 28;            // RoPE pairs on the h and w axes (56 channels)
+
+// A segment as the kernels see it: its first token index in the concatenated
+// token array plus the descriptor fields.
+struct SegDev {
+    int32_t start, n_text, t0, T, Hg, Wg;
+};
+
+struct SegTable {
+    int32_t n;
+    SegDev s[NOMAS_MAX_SEGS];
+};
+
+// Device addresses of the per-device RoPE tables.  Entry (p, i) of an axis
+// table holds (cos, sin) of p * 256^(-2i/d).
+struct RopeTables {
+    const float2* t32;    // [NOMAS_MAX_T][8]
+    const float2* h32;    // [NOMAS_MAX_HW][28]
+    const float2* w32;    // [NOMAS_MAX_HW][28]
+    const double2* t64;
+    const double2* h64;
+    const double2* w64;
+};
+
+// Builds the tables on the current device on first use; returns NOMAS_OK or
+// NOMAS_EHIP.  Thread-safe.
+int rope_tables(RopeTables* out);
+
+// Host-side float64 angle of pair i on an axis of width d at position p.
+double rope_angle(int p, int i, int d);
+
+// ----------------------------------------------------------------------------
+// device helpers
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef float nm_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 nm_bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16x2 (a in the low half), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    nm_f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, nm_bf16x2));
+}
+
+// Position of token `idx` of the concatenated segments in `st`:
+// video flag and (t, h, w).
+__device__ __forceinline__ bool token_pos(const SegTable& st, int idx, int& t, int& h, int& w) {
+    int a = 0;
+    while (a + 1 < st.n && st.s[a + 1].start <= idx) ++a;
+    const SegDev& s = st.s[a];
+    int loc = idx - s.start - s.n_text;
+    if (loc < 0) { t = h = w = 0; return false; }
+    int hw = s.Hg * s.Wg;
+    int tt = loc / hw;
+    int rem = loc - tt * hw;
+    int hh = rem / s.Wg;
+    t = s.t0 + tt;
+    h = hh;
+    w = rem - hh * s.Wg;
+    return true;
+}
+
+// Rotate the 4 channel pairs held in a 16-byte group of 8 bf16 values at
+// channels [8*grp, 8*grp+8) of a token at (t, h, w); float32 arithmetic with
+// the float32 table, result rounded to bf16.  grp 0..1 -> t, 2..8 -> h,
+// 9..15 -> w (the axis chunks are multiples of 8 channels).
+__device__ __forceinline__ uint4 rope_group_f32(uint4 x, int grp, int t, int h, int w,
+                                                const RopeTables& rt) {
+    const float2* tab;
+    int base;
+    if (grp < 2) { tab = rt.t32 + t * NPAIR_T; base = 4 * grp; }
+    else if (grp < 9) { tab = rt.h32 + h * NPAIR_HW; base = 4 * (grp - 2); }
+    else { tab = rt.w32 + w * NPAIR_HW; base = 4 * (grp - 9); }
+    uint32_t in[4] = {x.x, x.y, x.z, x.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float2 cs = tab[base + i];
+        float x0 = bf16lo(in[i]), x1 = bf16hi(in[i]);
+        float y0 = x0 * cs.x - x1 * cs.y;
+        float y1 = x0 * cs.y + x1 * cs.x;
+        o[i] = pack_bf16(y0, y1);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+}  // namespace nomas

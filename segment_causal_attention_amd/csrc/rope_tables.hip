@@ -1,0 +1,89 @@
+// Per-device RoPE cos/sin tables (3D RoPE, axes [16, 56, 56], theta 256:
+// comfyui-wiki news page on Hy-Nomas, section 模型内部).
+//
+// The tables live in static device arrays of this code object, so building
+// them allocates nothing: the first call on a device computes them on the host
+// in float64 (libm cos/sin of p * 256^(-2i/d)) and copies them in; float32
+// entries are the float64 values rounded once.
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "common.hpp"
+
+namespace nomas {
+
+__device__ float2 g_rope_t32[NOMAS_MAX_T * NPAIR_T];
+__device__ float2 g_rope_h32[NOMAS_MAX_HW * NPAIR_HW];
+__device__ float2 g_rope_w32[NOMAS_MAX_HW * NPAIR_HW];
+__device__ double2 g_rope_t64[NOMAS_MAX_T * NPAIR_T];
+__device__ double2 g_rope_h64[NOMAS_MAX_HW * NPAIR_HW];
+__device__ double2 g_rope_w64[NOMAS_MAX_HW * NPAIR_HW];
+
+double rope_angle(int p, int i, int d) {
+    double omega = std::pow(256.0, -2.0 * (double)i / (double)d);
+    return (double)p * omega;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+bool g_ready[kMaxDevices];
+RopeTables g_tabs[kMaxDevices];
+
+template <typename V2, typename S>
+std::vector<V2> host_table(int npos, int npair, int d) {
+    std::vector<V2> v((size_t)npos * npair);
+    for (int p = 0; p < npos; ++p)
+        for (int i = 0; i < npair; ++i) {
+            double a = rope_angle(p, i, d);
+            v[(size_t)p * npair + i].x = (S)std::cos(a);
+            v[(size_t)p * npair + i].y = (S)std::sin(a);
+        }
+    return v;
+}
+
+template <typename T>
+bool upload(const T& sym, const void* src, size_t bytes, const void** addr) {
+    if (hipMemcpyToSymbol(HIP_SYMBOL(sym), src, bytes, 0, hipMemcpyHostToDevice) != hipSuccess) return false;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(sym)) != hipSuccess) return false;
+    *addr = p;
+    return true;
+}
+
+}  // namespace
+
+int rope_tables(RopeTables* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NOMAS_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_ready[dev]) {
+        auto t32 = host_table<float2, float>(NOMAS_MAX_T, NPAIR_T, 16);
+        auto h32 = host_table<float2, float>(NOMAS_MAX_HW, NPAIR_HW, 56);
+        auto t64 = host_table<double2, double>(NOMAS_MAX_T, NPAIR_T, 16);
+        auto h64 = host_table<double2, double>(NOMAS_MAX_HW, NPAIR_HW, 56);
+        RopeTables r{};
+        const void* a[6];
+        bool ok = upload(g_rope_t32, t32.data(), t32.size() * sizeof(float2), &a[0]) &&
+                  upload(g_rope_h32, h32.data(), h32.size() * sizeof(float2), &a[1]) &&
+                  upload(g_rope_w32, h32.data(), h32.size() * sizeof(float2), &a[2]) &&
+                  upload(g_rope_t64, t64.data(), t64.size() * sizeof(double2), &a[3]) &&
+                  upload(g_rope_h64, h64.data(), h64.size() * sizeof(double2), &a[4]) &&
+                  upload(g_rope_w64, h64.data(), h64.size() * sizeof(double2), &a[5]);
+        if (!ok) return NOMAS_EHIP;
+        r.t32 = (const float2*)a[0];
+        r.h32 = (const float2*)a[1];
+        r.w32 = (const float2*)a[2];
+        r.t64 = (const double2*)a[3];
+        r.h64 = (const double2*)a[4];
+        r.w64 = (const double2*)a[5];
+        g_tabs[dev] = r;
+        g_ready[dev] = true;
+    }
+    *out = g_tabs[dev];
+    return NOMAS_OK;
+}
+
+}  // namespace nomas

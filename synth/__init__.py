@@ -268,3 +268,14 @@ def turn_inputs(k: int, with_cam: bool = True):
         out["w_k"] = bf16_tensor(5, 0, "w_k", (64, cfg.H * D), scale=1.0 / 8.0)
         out["w_v"] = bf16_tensor(5, 0, "w_v", (64, cfg.H * D), scale=1.0 / 8.0)
     return out
+
+
+def random_bf16(seed: int, shape, scale: float = 1.0) -> np.ndarray:
+    """Ad-hoc seeded N(0, scale^2) bf16 tensor (uint16 bits) for edge-case
+    shapes that are not one of the named workloads."""
+    n = int(np.prod(shape))
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    x = g.standard_normal(n, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return to_bf16_bits(x).reshape(shape)

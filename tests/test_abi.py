@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/nomas.h declares, rejects bad arguments on the host before touching
+the device, and its host-side pieces (RoPE table, camera tokens) agree with
+the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import segment_causal_attention_amd as nomas
+import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nomas.h")
+FAKE = 0x10000          # an aligned, never-dereferenced address for host-side checks
+
+
+def declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(nomas_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = nomas.lib()
+    names = declared()
+    assert set(names) >= {"nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_cam_xattn"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(nomas.SYMBOLS)
+    assert "gfx950" in nomas.version()
+
+
+def test_strerror_covers_codes():
+    for c in (nomas.OK, nomas.EINVAL, nomas.ECAPACITY, nomas.EHIP, nomas.EUNSUPPORTED):
+        assert nomas.strerror(c) and nomas.strerror(c) != "unknown error code"
+    assert nomas.strerror(12345) == "unknown error code"
+
+
+def segs(*t):
+    return nomas.seg_array(t)
+
+
+def test_seg_attn_host_checks():
+    L = nomas.lib()
+    sa, n = segs((16, 0, 2, 4, 6))
+    P = ctypes.c_void_p
+    good = dict(q=FAKE, k=FAKE, v=FAKE, segs=sa, n=n, kc=None, vc=None, ks=None, vs=None, cap=0, clen=0,
+                H=2, sm=0.088, out=FAKE, lse=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.nomas_seg_attn(P(a["q"]), P(a["k"]), P(a["v"]), a["segs"], a["n"], P(a["kc"]), P(a["vc"]),
+                                P(a["ks"]), P(a["vs"]), a["cap"], a["clen"], a["H"], a["sm"], P(a["out"]),
+                                P(a["lse"]), None)
+
+    assert call(q=None) == nomas.EINVAL
+    assert call(out=None) == nomas.EINVAL
+    assert call(q=FAKE + 2) == nomas.EINVAL            # misaligned
+    assert call(H=0) == nomas.EINVAL
+    assert call(sm=0.0) == nomas.EINVAL
+    assert call(sm=float("nan")) == nomas.EINVAL
+    assert call(n=0) == nomas.EINVAL
+    assert call(clen=5, cap=4) == nomas.EINVAL        # cache_len > cap
+    assert call(clen=4, cap=4) == nomas.EINVAL        # cache pointers missing
+    bad, nb = segs((16, 0, 2, 0, 6))                  # video frames with a zero-height grid
+    assert call(segs=bad, n=nb) == nomas.EINVAL
+    neg, nn = segs((-1, 0, 2, 4, 6))
+    assert call(segs=neg, n=nn) == nomas.EINVAL
+    far, nf = segs((0, 16380, 8, 4, 6))               # t beyond the RoPE table
+    assert call(segs=far, n=nf) == nomas.EUNSUPPORTED
+    many, nm = nomas.seg_array([(1, 0, 0, 0, 0)] * (nomas.MAX_SEGS + 1))
+    assert call(segs=many, n=nm) == nomas.EUNSUPPORTED
+    empty, ne = segs((0, 0, 0, 0, 0))                 # no tokens: nothing to do
+    assert call(segs=empty, n=ne) == nomas.OK
+
+
+def test_kv_quant_append_host_checks():
+    L = nomas.lib()
+    P = ctypes.c_void_p
+    ln = ctypes.c_int64(10)
+
+    def call(L_=4, H=2, cap=16, k=FAKE, sc=FAKE, length=ln):
+        return L.nomas_kv_quant_append(P(k), P(FAKE), L_, H, P(FAKE), P(FAKE), P(sc), P(FAKE), cap,
+                                       ctypes.byref(length) if length is not None else None, None)
+
+    assert call(L_=7) == nomas.ECAPACITY and ln.value == 10      # 10 + 7 > 16: nothing written
+    assert call(L_=-1) == nomas.EINVAL
+    assert call(H=0) == nomas.EINVAL
+    assert call(k=None) == nomas.EINVAL
+    assert call(k=FAKE + 8) == nomas.EINVAL
+    assert call(sc=FAKE + 2) == nomas.EINVAL
+    assert call(length=None) == nomas.EINVAL
+    assert call(L_=0) == nomas.OK and ln.value == 10               # empty append is a no-op
+    big = ctypes.c_int64(17)
+    assert call(length=big) == nomas.EINVAL                         # len > cap
+
+
+def test_rope3d_and_cam_xattn_host_checks():
+    L = nomas.lib()
+    P = ctypes.c_void_p
+    sa, n = segs((16, 0, 2, 4, 6))
+    assert L.nomas_rope3d(P(None), P(FAKE), sa, n, 2, None) == nomas.EINVAL
+    assert L.nomas_rope3d(P(FAKE), P(FAKE), sa, n, 0, None) == nomas.EINVAL
+    assert L.nomas_cam_xattn(P(FAKE), 10, 2, P(FAKE), 0, P(FAKE), P(FAKE), 0.1, P(FAKE), None) == nomas.EINVAL
+    assert L.nomas_cam_xattn(P(FAKE), 10, 2, P(FAKE), nomas.MAX_CAM + 1, P(FAKE), P(FAKE), 0.1, P(FAKE),
+                             None) == nomas.EUNSUPPORTED
+    assert L.nomas_cam_xattn(P(FAKE), 10, 2, P(None), 5, P(FAKE), P(FAKE), 0.1, P(FAKE), None) == nomas.EINVAL
+    assert L.nomas_cam_xattn(P(FAKE), 0, 2, P(FAKE), 5, P(FAKE), P(FAKE), 0.1, P(FAKE), None) == nomas.OK
+
+
+@pytest.mark.parametrize("axis,npos", [(0, 400), (1, 22), (2, 40), (1, 1024)])
+def test_rope_table_bit_identical_to_oracle(axis, npos):
+    c, s = nomas.rope_table(axis, npos)
+    co, so = oracle.rope_table_f32(axis, npos)
+    assert np.array_equal(c.view(np.uint32), co.view(np.uint32))
+    assert np.array_equal(s.view(np.uint32), so.view(np.uint32))
+
+
+def test_cam_tokens_match_oracle():
+    c2w = synth.camera_path(5, 0, 288)
+    got = nomas.cam_tokens(c2w)
+    ref = oracle.cam_tokens(c2w)
+    assert got.shape == (72, 64)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=2e-6)
+    # same float32 values as rounding the oracle's float64 tokens, but for rare last-bit cases
+    assert np.mean(got == ref.astype(np.float32)) > 0.99
+    got2 = nomas.cam_tokens(c2w, translation_scale=2.0, rotation_scale=1.0)
+    np.testing.assert_allclose(got2, oracle.cam_tokens(c2w, 2.0, 1.0), rtol=0, atol=2e-6)
+    with pytest.raises(nomas.NomasError):
+        nomas.cam_tokens(c2w[:6])

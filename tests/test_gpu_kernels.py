@@ -1,0 +1,212 @@
+"""GPU parity of each libnomas entry point against the CPU oracle, on small and
+edge-case shapes (ragged tails, several query tiles, packed segments, short
+caches).  Calls go through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import segment_causal_attention_amd as nomas
+import synth
+from gpu_util import SM, assert_close, bits, cache_tensors, dev, dev16, f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------------------
+# rope3d: float64 rotation rounded once, so it should equal the oracle's bits
+
+
+ROPE_CASES = [
+    ("tiny", [s.astuple() for s in synth.TINY_SEGS], 2),
+    ("text+video", [(256, 18, 2, 22, 40)], 16),
+    ("late-t", [(3, 16000, 2, 7, 5), (0, 9, 1, 30, 33)], 3),
+]
+
+
+@pytest.mark.parametrize("name,segs,H", ROPE_CASES, ids=[c[0] for c in ROPE_CASES])
+def test_rope3d_matches_oracle(name, segs, H):
+    L = sum(s[0] + s[2] * s[3] * s[4] for s in segs)
+    x = synth.random_bf16(101, (L, H, 128), 3.0)
+    say("rope3d", name, L, H)
+    xd = dev16(x)
+    y = nomas.rope3d(xd, segs)
+    torch.cuda.synchronize()
+    ref = oracle.f64_to_bf16_bits(oracle.bf16_round(oracle.rope3d(oracle.bf16_bits_to_f64(x), segs)))
+    got = bits(y)
+    diff = got != ref
+    say("  mismatching bf16 values: %d of %d" % (diff.sum(), diff.size))
+    if diff.any():   # at most one unit in the last place
+        assert np.abs(got[diff].astype(np.int32) - ref[diff].astype(np.int32)).max() <= 1
+    assert diff.mean() < 1e-5
+    # in place gives the same bits
+    nomas.rope3d(xd, segs, out=xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(xd), got)
+
+
+# ----------------------------------------------------------------------------
+# kv_quant_append: bit-exact codes and scales
+
+
+def _quant_inputs():
+    rng_rows = []
+    a = synth.random_bf16(7, (300, 3, 128), 1.0)
+    b = synth.random_bf16(8, (300, 3, 128), 1.0)
+    # outlier channels x20, tiny magnitudes, an all-zero row and exact ties
+    b32 = oracle.bf16_bits_to_f64(b)
+    b32[:, :, 5] *= 20.0
+    b32[10:20] *= 1e-4
+    b32[20] = 0.0
+    b32[21, 0, :] = 0.0
+    b32[21, 0, 0] = 127.0
+    b32[21, 0, 1:9] = [2.5, 3.5, 0.5, 1.5, -2.5, -3.5, -0.5, 126.5]
+    b = oracle.f64_to_bf16_bits(oracle.bf16_round(b32))
+    return a, b
+
+
+def test_kv_quant_append_bit_exact_and_offsets():
+    k, v = _quant_inputs()
+    L, H = k.shape[0], k.shape[1]
+    cap = 2 * L + 37
+    kc, vc, ks, vs = cache_tensors(H, cap)
+    kc.fill_(77)
+    ks.fill_(-1.0)
+    n = nomas.kv_quant_append(dev16(k[:123]), dev16(v[:123]), kc, vc, ks, vs, 0)
+    assert n == 123
+    n = nomas.kv_quant_append(dev16(k), dev16(v), kc, vc, ks, vs, n)
+    assert n == 123 + L
+    torch.cuda.synchronize()
+    for src, codes, scales, start in ((k[:123], kc, ks, 0), (k, kc, ks, 123), (v[:123], vc, vs, 0), (v, vc, vs, 123)):
+        qo, so = oracle.quantise(oracle.bf16_bits_to_f64(src))          # [L][H][128], [L][H]
+        qg = codes.cpu().numpy()[:, start:start + len(src)].transpose(1, 0, 2)
+        sg = scales.cpu().numpy()[:, start:start + len(src)].T
+        assert np.array_equal(qg, qo)
+        assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    # entries past the appended range are untouched
+    assert torch.all(kc[:, 123 + L:] == 77) and torch.all(ks[:, 123 + L:] == -1.0)
+    # a full cache refuses and leaves everything as it was
+    with pytest.raises(nomas.NomasError) as ei:
+        nomas.kv_quant_append(dev16(k), dev16(v), kc, vc, ks, vs, n)
+    assert ei.value.code == nomas.ECAPACITY
+
+
+# ----------------------------------------------------------------------------
+# seg_attn
+
+
+def _run_gpu(q, k, v, segs, cache, Lc, H, with_lse=True):
+    Ln = q.shape[0]
+    lse = torch.empty((H, Ln), dtype=torch.float32, device="cuda:0") if with_lse else None
+    if Lc > 0:
+        kc, vc, ks, vs = (dev(a) for a in cache)
+    else:
+        kc = vc = ks = vs = None
+    out = nomas.seg_attn(dev16(q), dev16(k), dev16(v), segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse)
+    torch.cuda.synchronize()
+    return f64(out), (lse.cpu().numpy() if with_lse else None), out
+
+
+def _check_case(name, q, k, v, segs, cache, Lc, H):
+    say("seg_attn", name, "Ln", q.shape[0], "Lc", Lc, "H", H)
+    got, lse, _ = _run_gpu(q, k, v, segs, cache, Lc, H)
+    kc, vc, ks, vs = cache if Lc > 0 else (np.zeros((H, 0, 128), np.int8),) * 2 + (np.zeros((H, 0), np.float32),) * 2
+    ref, lref = oracle.seg_attn(q, k, v, segs, kc, vc, ks, vs, Lc, SM)
+    assert_close(got, ref, name)
+    np.testing.assert_allclose(lse, lref, rtol=0, atol=2e-3)
+
+
+@pytest.mark.parametrize("mode", ["cache", "packed", "three"])
+def test_seg_attn_tiny(mode):
+    inp = synth.tiny_inputs()
+    segs = [s.astuple() for s in inp["segs"]]
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    n = 64
+    if mode == "packed":
+        _check_case("tiny-packed", q[:2 * n], k[:2 * n], v[:2 * n], segs[:2], None, 0, 2)
+        return
+    cache = oracle.build_cache(k[:n], v[:n], segs[:1])
+    hi = 2 * n if mode == "cache" else 3 * n
+    _check_case("tiny-" + mode, q[n:hi], k[n:hi], v[n:hi], segs[1:hi // n], cache, n, 2)
+
+
+EDGE = [
+    ("one-token", [(1, 0, 0, 0, 0)], 0, 2),
+    ("one-token-cache1", [(1, 0, 0, 0, 0)], 1, 2),
+    ("text-only-300", [(300, 0, 0, 0, 0)], 5, 1),
+    ("ragged-97-cache130", [(7, 3, 2, 5, 9)], 130, 2),
+    ("packed-5", [(3, 0, 1, 2, 3), (0, 1, 2, 3, 5), (10, 3, 1, 1, 1), (1, 4, 3, 2, 2), (0, 7, 1, 8, 8)], 77, 2),
+    ("two-seg-multi-tile", [(5, 0, 1, 3, 4), (40, 1, 3, 10, 9)], 0, 3),
+    ("turn-shape-small", [(256, 18, 2, 22, 40)], 1760, 2),
+    ("empty-segment-between", [(4, 0, 1, 2, 2), (0, 0, 0, 0, 0), (2, 1, 2, 3, 3)], 64, 2),
+]
+
+
+@pytest.mark.parametrize("name,segs,Lc,H", EDGE, ids=[c[0] for c in EDGE])
+def test_seg_attn_edge_shapes(name, segs, Lc, H):
+    Ln = sum(s[0] + s[2] * s[3] * s[4] for s in segs)
+    q = synth.random_bf16(201, (Ln, H, 128))
+    k = synth.random_bf16(202, (Ln, H, 128))
+    v = synth.random_bf16(203, (Ln, H, 128))
+    cache = None
+    if Lc > 0:
+        hist = [(0, 0, 1, 1, Lc)]                 # a one-row "frame" of Lc history tokens
+        kh = synth.random_bf16(204, (Lc, H, 128))
+        vh = synth.random_bf16(205, (Lc, H, 128))
+        cache = oracle.build_cache(kh, vh, hist, cap=Lc + 11)
+    _check_case(name, q, k, v, segs, cache, Lc, H)
+
+
+def test_seg_attn_future_segments_never_leak():
+    """Rows of earlier packed segments give bit-identical outputs when every
+    later-segment key and value is NaN, and stay finite."""
+    inp = synth.tiny_inputs()
+    segs = [s.astuple() for s in inp["segs"]]
+    q, k, v = (inp[x].copy() for x in ("q", "k", "v"))
+    got0, lse0, _ = _run_gpu(q, k, v, segs, None, 0, 2)
+    k[64:] = 0x7FC0
+    v[64:] = 0x7FC0
+    got1, lse1, _ = _run_gpu(q, k, v, segs, None, 0, 2)
+    assert np.all(np.isfinite(got1[:64])) and np.all(np.isfinite(lse1[:, :64]))
+    assert np.array_equal(got0[:64], got1[:64]) and np.array_equal(lse0[:, :64], lse1[:, :64])
+    assert np.all(np.isnan(got1[128:]))
+
+
+def test_seg_attn_deterministic_and_cache_copy():
+    inp = synth.tiny_inputs()
+    segs = [s.astuple() for s in inp["segs"]]
+    n = 64
+    cache = oracle.build_cache(inp["k"][:n], inp["v"][:n], segs[:1])
+    args = (inp["q"][n:], inp["k"][n:], inp["v"][n:], segs[1:], cache, n, 2)
+    _, _, o1 = _run_gpu(*args)
+    _, _, o2 = _run_gpu(*args)
+    assert torch.equal(o1, o2)
+    # a resumed cache (codes, scales and length copied elsewhere) gives the same bits
+    kc, vc, ks, vs = (dev(a) for a in cache)
+    kc2, vc2, ks2, vs2 = (t.clone() for t in (kc, vc, ks, vs))
+    o3 = nomas.seg_attn(dev16(args[0]), dev16(args[1]), dev16(args[2]), segs[1:], kc2, vc2, ks2, vs2,
+                        cache_len=n, sm_scale=SM)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3)
+
+
+# ----------------------------------------------------------------------------
+# cam_xattn
+
+
+@pytest.mark.parametrize("Lq,H,Nc", [(100, 2, 1), (3000, 2, 72), (64, 3, 5), (2100, 1, 32), (700, 2, 33), (257, 2, 128)])
+def test_cam_xattn_matches_oracle(Lq, H, Nc):
+    say("cam_xattn", Lq, H, Nc)
+    q = synth.random_bf16(301, (Lq, H, 128))
+    wk = synth.random_bf16(302, (64, H * 128), 1 / 8)
+    wv = synth.random_bf16(303, (64, H * 128), 1 / 8)
+    c2w = synth.camera_path(5, 7, 4 * Nc)
+    cam = oracle.cam_tokens(c2w).astype(np.float32)
+    out = nomas.cam_xattn(dev16(q), dev(cam), dev16(wk), dev16(wv), sm_scale=SM)
+    torch.cuda.synchronize()
+    got = f64(out)
+    ref = oracle.cam_xattn(q, cam, wk, wv, SM)
+    assert_close(got, ref, "cam_xattn Lq=%d H=%d Nc=%d" % (Lq, H, Nc))
+    if Nc == 1:   # one camera token: every query returns its value vector
+        _, Vc = oracle.cam_kv(cam, wk, wv, H)
+        np.testing.assert_allclose(got, np.broadcast_to(Vc[0][None], got.shape), rtol=0, atol=1e-2)
