@@ -1,0 +1,250 @@
+"""Throughput of the segment-causal attention path on one MI355X.
+
+One step = one turn of the whole hot path at the full-lifelong-cache shape
+(a 12 s segment: 72 latent frames x 880 = 63,360 new tokens, 16 heads x 128,
+over 288 cached latent frames = 253,440 INT8 tokens):
+    nomas_seg_attn   (63,360 queries x 316,800 keys, RoPE fused, INT8 cache)
+    nomas_cam_xattn  (63,360 video queries x 72 camera tokens)
+    nomas_rope3d     (the segment's keys, before caching)
+    nomas_kv_quant_append (the segment's K/V into the cache at 253,440)
+The append writes the same cache slots every step, so every step sees the
+same 253,440-token history.  Inputs are seeded synthetic tensors resident in
+HBM before timing starts.
+
+value = algorithmic attention FLOPs per step / wall time per step (TFLOP/s),
+with algorithmic FLOPs = 4 * 128 * H * (allowed query-key pairs).
+The roofline block times nomas_seg_attn alone with HIP events on its stream.
+The CPU baseline times the oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (plain copy kernel for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense BF16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "seg_attn_fullcache_traffic.json")
+KERNEL_SOURCES = ["segment_causal_attention_amd/csrc/seg_attn.hip", "segment_causal_attention_amd/csrc/common.hpp"]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per seg_attn launch from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_digest") != kernel_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def copy_calibration():
+    """A plain device copy of a known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import segment_causal_attention_amd as nomas
+    import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[4]
+    H, Lq, Lc = cfg.H, cfg.Lq, cfg.Lc
+    (seg,) = cfg.new_segs
+    (hseg,) = cfg.hist_segs
+    cap = Lc + Lq
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+    Nc = 72
+
+    t0 = time.time()
+    inp = synth.layer_inputs(4)
+    cam_in = synth.turn_inputs(0, with_cam=True)
+    log("inputs generated in %.1f s" % (time.time() - t0))
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    q, k_new, v_new = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])
+    q_cam = d16(cam_in["q_cam"])
+    w_k, w_v = d16(cam_in["w_k"]), d16(cam_in["w_v"])
+    cam = torch.from_numpy(nomas.cam_tokens(cam_in["c2w"])).to(dev)
+    kc = torch.empty((H, cap, 128), dtype=torch.int8, device=dev)
+    vc = torch.empty((H, cap, 128), dtype=torch.int8, device=dev)
+    ks = torch.empty((H, cap), dtype=torch.float32, device=dev)
+    vs = torch.empty((H, cap), dtype=torch.float32, device=dev)
+    # build the 288-frame history the way the path does: rotate, then quantise
+    kh = d16(inp["k_hist"])
+    vh = d16(inp["v_hist"])
+    nomas.rope3d(kh, [hseg], out=kh)
+    n = nomas.kv_quant_append(kh, vh, kc, vc, ks, vs, 0)
+    assert n == Lc
+    del kh, vh
+    out = torch.empty_like(q)
+    out_cam = torch.empty_like(q_cam)
+    k_rot = torch.empty_like(k_new)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record(stream)
+        nomas.seg_attn(q, k_new, v_new, [seg], kc, vc, ks, vs, cache_len=Lc, sm_scale=sm, out=out, stream=stream)
+        if i is not None:
+            ev[i][1].record(stream)
+        nomas.cam_xattn(q_cam, cam, w_k, w_v, sm_scale=sm, out=out_cam, stream=stream)
+        nomas.rope3d(k_new, [seg], out=k_rot, stream=stream)
+        nomas.kv_quant_append(k_rot, v_new, kc, vc, ks, vs, Lc, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    pairs = Lq * (Lc + Lq)
+    flops = 4.0 * 128 * H * pairs
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    log("step %.3f ms, seg_attn %.3f ms (%.1f TFLOP/s, %.1f%% of peak)"
+        % (ms_step, attn_ms, achieved, 100 * achieved / PEAK_BF16_TFLOPS))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, cfg, sm)
+
+    line = {
+        "metric": "seg-causal attention TFLOP/s (BF16 MFMA) + % of peak, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, INT8 cache quantised on the GPU)",
+        "config": {
+            "workload": "fullcache: 12 s segment (72 latent frames x 880 = 63,360 queries) over 288 cached "
+                        "latent frames (253,440 INT8 keys) + own segment = 316,800 keys, 16 heads x 128; "
+                        "step = seg_attn + cam_xattn (72 camera tokens) + rope3d + kv_quant_append",
+            "heads": H, "head_dim": 128, "queries": Lq, "cache_tokens": Lc, "keys_per_query": Lc + Lq,
+            "algorithmic_flop_per_step": flops,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "seg_attn_kernel",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": round(attn_ms, 3),
+            "traffic": traffic_for_current_kernel(),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def cpu_baseline(inp, cfg, sm):
+    """The oracle (numpy float64) on a bounded sample: head 0, the first 2048
+    of the 63,360 query rows, all 316,800 allowed keys."""
+    import numpy as np
+
+    import oracle
+
+    H, Lq, Lc = cfg.H, cfg.Lq, cfg.Lc
+    rows = np.arange(2048)
+    kc, vc, ks, vs = oracle.build_cache(inp["k_hist"][:, :1], inp["v_hist"][:, :1], cfg.hist_segs)
+    q1 = np.ascontiguousarray(inp["q"][:, :1])
+    k1 = np.ascontiguousarray(inp["k_new"][:, :1])
+    v1 = np.ascontiguousarray(inp["v_new"][:, :1])
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    t0 = time.perf_counter()
+    oracle.seg_attn(q1, k1, v1, cfg.new_segs, kc, vc, ks, vs, Lc, sm, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * 128 * len(rows) * (Lc + Lq)
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((i.get("num_threads") or 1) for i in info) if info else int(threads)
+    except Exception:
+        cores = int(threads)
+    log("cpu baseline: %.2f s for %.3e FLOP" % (dt, flops))
+    return {
+        "value": round(flops / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "seconds": round(dt, 2),
+        "sample": "numpy float64 oracle, head 0 of 16, query rows 0..2047 of 63,360, each over all 316,800 "
+                  "allowed keys (%.2e algorithmic FLOP), timed including its per-head key dequantisation "
+                  "and rotation" % flops,
+    }
+
+
+if __name__ == "__main__":
+    main()

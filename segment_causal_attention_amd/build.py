@@ -19,6 +19,11 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnomas.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "rope_tables.hip", "kv_quant.hip", "rope3d.hip", "seg_attn.hip", "cam_xattn.hip"]
+# The attention kernels take maxima with v_max/v_max3; without IEEE mode they
+# need no NaN-quieting copies of every operand.  NaN inputs still propagate to
+# every row that can see them through the products.
+PER_FILE = {"seg_attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+            "cam_xattn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
@@ -40,7 +45,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     for s in SOURCES:
         o = os.path.join(BUILD, s.replace(".hip", ".o"))
         objs.append(o)
-        cmds.append([HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, "-c", os.path.join(CSRC, s), "-o", o])
+        cmds.append([HIPCC, *FLAGS, *PER_FILE.get(s, []), *extra_flags, "-I", INCLUDE, "-c",
+                     os.path.join(CSRC, s), "-o", o])
     with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 1)) as ex:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp%d" % os.getpid()

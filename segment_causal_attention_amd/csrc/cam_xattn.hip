@@ -156,7 +156,7 @@ __global__ __launch_bounds__(512) void cam_xattn_kernel(const uint16_t* __restri
                 if (key >= Nc) s[r] = -INFINITY;
                 mx = fmaxf(mx, s[r]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = half_max(mx);
             const float mn = mx * scale_log2;
             if (__any(mn > m + 8.0f)) {
                 const float mnew = fmaxf(m, mn);
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(512) void cam_xattn_kernel(const uint16_t* __restri
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const cbf16x8*>(vrow + 16), p1, o[db], 0, 0, 0);
             }
         }
-        lsum += __shfl_xor(lsum, 32);
+        lsum = half_sum(lsum);
         const float inv = 1.0f / lsum;
         const int64_t row = rbeg + 32 * b + l32;
         if (row < rend) {

@@ -57,6 +57,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, nm_bf16x2));
 }
 
+// Combine a per-lane value with the one in the other half of the wave
+// (lane l and l^32) through v_permlane32_swap: the two returned registers hold
+// the low and the high half broadcast, so a symmetric op of the pair gives the
+// reduction over {l, l^32} in every lane.
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Position of token `idx` of the concatenated segments in `st`:
 // video flag and (t, h, w).
 __device__ __forceinline__ bool token_pos(const SegTable& st, int idx, int& t, int& h, int& w) {

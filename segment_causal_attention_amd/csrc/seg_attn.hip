@@ -41,9 +41,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;              // keys per tile
-constexpr int NW = 4;               // waves per workgroup
-constexpr int QW = 64;              // query rows per wave
+constexpr int NW = 8;               // waves per workgroup (2 per SIMD)
+constexpr int QW = 32;              // query rows per wave
 constexpr int BM = NW * QW;         // query rows per workgroup
+constexpr int NT = NW * 64;         // threads per workgroup
 constexpr int KSTR = D + 8;         // LDS row stride of the K tile (bf16), padded
 constexpr int VSTR = BN + 8;        // LDS row stride of the V^T tile (bf16), padded
 
@@ -65,11 +66,13 @@ struct AttnArgs {
     RopeTables rt;
 };
 
-// Registers that carry the next key tile from HBM to LDS.
+// This thread's share of one key tile on its way from HBM to LDS.
+//   K: thread owns key row tid/8, channels 16*(tid%8) .. +16
+//   V: thread owns keys 4*(tid%16) .. +4, channels 4*(tid/16) .. +4
 struct Prefetch {
-    uint4 a[4];     // K: cache 2 x 16 codes; new 4 x 8 bf16
-    uint4 b[4];     // V: cache 4 keys x 8 codes (in .x/.y of b[0..1] pairs); new 4 keys x 8 bf16
-    float sc[5];    // cache scales: K of this thread's row, V of its 4 keys
+    uint4 a[2];       // K: cache 16 codes in a[0]; new 16 bf16 in a[0..1]
+    uint32_t b[8];    // V: cache 4 keys x 4 codes in b[0..3]; new 4 keys x 4 bf16 in b[0..7]
+    float sc[5];      // cache scales: K of the row, V of the 4 keys
 };
 
 // position (in the permuted V^T row) of key k, k a multiple of 4 inside a tile
@@ -83,128 +86,160 @@ __device__ __forceinline__ float i8(uint32_t word, int byte) {
     return (float)(int8_t)(word >> (8 * byte));
 }
 
-__device__ __forceinline__ void load_cache_tile(const AttnArgs& A, int head, int key0, int tid, Prefetch& p) {
-    const int64_t hb = (int64_t)head * A.cap;
-    {
-        const int krow = tid >> 2, kpart = tid & 3;
+__device__ __forceinline__ void load_tile(const AttnArgs& A, int head, int t, int nc, int kend, int tid,
+                                          Prefetch& p) {
+    const int krow = tid >> 3, kpart = tid & 7;
+    const int kg = tid & 15, dq = tid >> 4;
+    if (t < nc) {
+        const int key0 = t * BN;
+        const int64_t hb = (int64_t)head * A.cap;
         const int key = key0 + krow;
         if (key < A.Lc) {
-            const uint4* src = reinterpret_cast<const uint4*>(A.kc + (hb + key) * D + 32 * kpart);
-            p.a[0] = src[0];
-            p.a[1] = src[1];
+            p.a[0] = *reinterpret_cast<const uint4*>(A.kc + (hb + key) * D + 16 * kpart);
             p.sc[0] = A.ks[hb + key];
         } else {
-            p.a[0] = p.a[1] = make_uint4(0, 0, 0, 0);
+            p.a[0] = make_uint4(0, 0, 0, 0);
             p.sc[0] = 0.0f;
         }
-    }
-    {
-        const int kg = tid & 15, dg = tid >> 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 4 * kg + i;
-            uint2 w = make_uint2(0, 0);
-            float s = 0.0f;
-            if (key < A.Lc) {
-                w = *reinterpret_cast<const uint2*>(A.vc + (hb + key) * D + 8 * dg);
-                s = A.vs[hb + key];
-            }
-            if (i & 1) { p.b[i >> 1].z = w.x; p.b[i >> 1].w = w.y; }
-            else { p.b[i >> 1].x = w.x; p.b[i >> 1].y = w.y; }
-            p.sc[1 + i] = s;
+            const int kv = key0 + 4 * kg + i;
+            const bool ok = kv < A.Lc;
+            p.b[i] = ok ? *reinterpret_cast<const uint32_t*>(A.vc + (hb + kv) * D + 4 * dq) : 0u;
+            p.sc[1 + i] = ok ? A.vs[hb + kv] : 0.0f;
         }
-    }
-}
-
-__device__ __forceinline__ void store_cache_tile(const Prefetch& p, uint16_t* Ks, uint16_t* Vt, int tid) {
-    {
-        const int krow = tid >> 2, kpart = tid & 3;
-        const float s = p.sc[0];
-        uint32_t wv[8] = {p.a[0].x, p.a[0].y, p.a[0].z, p.a[0].w, p.a[1].x, p.a[1].y, p.a[1].z, p.a[1].w};
-        uint32_t o[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            o[2 * i] = pack_bf16(i8(wv[i], 0) * s, i8(wv[i], 1) * s);
-            o[2 * i + 1] = pack_bf16(i8(wv[i], 2) * s, i8(wv[i], 3) * s);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(Ks + krow * KSTR + 32 * kpart);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-    }
-    {
-        const int kg = tid & 15, dg = tid >> 4;
-        // key i's 8 codes: lo word / hi word
-        uint32_t lo[4] = {p.b[0].x, p.b[0].z, p.b[1].x, p.b[1].z};
-        uint32_t hi[4] = {p.b[0].y, p.b[0].w, p.b[1].y, p.b[1].w};
-        const int col = vperm(4 * kg);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            float x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = i8(d < 4 ? lo[i] : hi[i], d & 3) * p.sc[1 + i];
-            *reinterpret_cast<uint2*>(Vt + (8 * dg + d) * VSTR + col) =
-                make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
-        }
-    }
-}
-
-__device__ __forceinline__ void load_new_tile(const AttnArgs& A, int head, int key0, int kend, int tid, Prefetch& p) {
-    {
-        const int krow = tid >> 2, kpart = tid & 3;
+    } else {
+        const int key0 = (t - nc) * BN;
         const int key = key0 + krow;
         if (key < kend) {
-            const uint4* src = reinterpret_cast<const uint4*>(A.k + ((int64_t)key * A.H + head) * D + 32 * kpart);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p.a[i] = src[i];
+            const uint4* src = reinterpret_cast<const uint4*>(A.k + ((int64_t)key * A.H + head) * D + 16 * kpart);
+            p.a[0] = src[0];
+            p.a[1] = src[1];
         } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p.a[i] = make_uint4(0, 0, 0, 0);
+            p.a[0] = p.a[1] = make_uint4(0, 0, 0, 0);
         }
-    }
-    {
-        const int kg = tid & 15, dg = tid >> 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 4 * kg + i;
-            p.b[i] = (key < kend)
-                         ? *reinterpret_cast<const uint4*>(A.v + ((int64_t)key * A.H + head) * D + 8 * dg)
-                         : make_uint4(0, 0, 0, 0);
+            const int kv = key0 + 4 * kg + i;
+            uint2 w = make_uint2(0, 0);
+            if (kv < kend) w = *reinterpret_cast<const uint2*>(A.v + ((int64_t)kv * A.H + head) * D + 4 * dq);
+            p.b[2 * i] = w.x;
+            p.b[2 * i + 1] = w.y;
         }
     }
 }
 
-__device__ __forceinline__ void store_new_tile(const AttnArgs& A, Prefetch& p, int key0, int kend,
-                                               uint16_t* Ks, uint16_t* Vt, int tid) {
-    {
-        const int krow = tid >> 2, kpart = tid & 3;
-        const int key = key0 + krow;
-        int t, h, w;
-        if (key < kend && token_pos(A.segs, key, t, h, w)) {
+__device__ __forceinline__ void store_tile(const AttnArgs& A, int t, int nc, int kend, int tid, Prefetch& p,
+                                           uint16_t* Ks, uint16_t* Vt) {
+    const int krow = tid >> 3, kpart = tid & 7;
+    const int kg = tid & 15, dq = tid >> 4;
+    uint4* kdst = reinterpret_cast<uint4*>(Ks + krow * KSTR + 16 * kpart);
+    const int col = vperm(4 * kg);
+    if (t < nc) {
+        // K: 16 codes * scale -> bf16
+        const float s = p.sc[0];
+        const uint32_t w[4] = {p.a[0].x, p.a[0].y, p.a[0].z, p.a[0].w};
+        uint32_t o[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.a[i] = rope_group_f32(p.a[i], 4 * kpart + i, t, h, w, A.rt);
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = pack_bf16(i8(w[i], 0) * s, i8(w[i], 1) * s);
+            o[2 * i + 1] = pack_bf16(i8(w[i], 2) * s, i8(w[i], 3) * s);
         }
-        uint4* dst = reinterpret_cast<uint4*>(Ks + krow * KSTR + 32 * kpart);
+        kdst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        kdst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        // V: 4 keys x 4 channels, transposed: one 4-key run per channel
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = p.a[i];
-    }
-    {
-        const int kg = tid & 15, dg = tid >> 4;
-        const int col = vperm(4 * kg);
-        uint32_t wv[4][4];
+        for (int d = 0; d < 4; ++d) {
+            const float x0 = i8(p.b[0], d) * p.sc[1], x1 = i8(p.b[1], d) * p.sc[2];
+            const float x2 = i8(p.b[2], d) * p.sc[3], x3 = i8(p.b[3], d) * p.sc[4];
+            *reinterpret_cast<uint2*>(Vt + (4 * dq + d) * VSTR + col) = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
+        }
+    } else {
+        const int key = (t - nc) * BN + krow;
+        int tt, h, w;
+        if (key < kend && token_pos(A.segs, key, tt, h, w)) {
+            p.a[0] = rope_group_f32(p.a[0], 2 * kpart, tt, h, w, A.rt);
+            p.a[1] = rope_group_f32(p.a[1], 2 * kpart + 1, tt, h, w, A.rt);
+        }
+        kdst[0] = p.a[0];
+        kdst[1] = p.a[1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { wv[i][0] = p.b[i].x; wv[i][1] = p.b[i].y; wv[i][2] = p.b[i].z; wv[i][3] = p.b[i].w; }
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const int c = d >> 1;
+        for (int d = 0; d < 4; ++d) {
+            const int wi = d >> 1;
             const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-            uint32_t p01 = __builtin_amdgcn_perm(wv[1][c], wv[0][c], sel);
-            uint32_t p23 = __builtin_amdgcn_perm(wv[3][c], wv[2][c], sel);
-            *reinterpret_cast<uint2*>(Vt + (8 * dg + d) * VSTR + col) = make_uint2(p01, p23);
+            const uint32_t p01 = __builtin_amdgcn_perm(p.b[2 + wi], p.b[wi], sel);
+            const uint32_t p23 = __builtin_amdgcn_perm(p.b[6 + wi], p.b[4 + wi], sel);
+            *reinterpret_cast<uint2*>(Vt + (4 * dq + d) * VSTR + col) = make_uint2(p01, p23);
         }
     }
 }
 
-__global__ __launch_bounds__(256, 1) void seg_attn_kernel(const AttnArgs A) {
+// One 64-key tile for the 32 query rows of this wave: S^T = K.Q^T, online
+// softmax, O^T += V^T.P^T.  MASK: keys at or beyond `lim` are excluded.
+template <bool MASK>
+__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                          const bf16x8 (&qf)[8], f32x16 (&o)[4], float& m, float& lsum,
+                                          float c, int lim, int g, int l32) {
+    f32x16 s[2];
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const uint16_t* kr = K + (32 * kb + l32) * KSTR + 8 * g;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr), qf[0], zero, 0, 0, 0);
+#pragma unroll
+        for (int kk = 1; kk < 8; ++kk)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk), qf[kk],
+                                                            s[kb], 0, 0, 0);
+    }
+    if (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) >= lim) s[kb][r] = -INFINITY;
+    }
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    mx = half_max(mx);
+    const float mn = mx * c;
+    if (__any(mn > m + 8.0f)) {
+        const float mnew = fmaxf(m, mn);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m = mnew;
+    }
+    const float nm = -m;
+    bf16x8 pb[4];
+    const nm_bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        uint32_t pk[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, nm));
+            pk[r >> 1] = pack_bf16(p0, p1);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(nm_bf16x2, pk[r >> 1]), ones, lsum, false);
+        }
+        pb[2 * kb] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        pb[2 * kb + 1] = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+    }
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(V + (32 * db + l32) * VSTR + 16 * ch + 8 * g);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ch], o[db], 0, 0, 0);
+        }
+    }
+}
+
+__global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
 
@@ -223,11 +258,11 @@ __global__ __launch_bounds__(256, 1) void seg_attn_kernel(const AttnArgs A) {
     const int kend = seg_end;                 // new keys [0, kend) are allowed
     const float c = A.scale_log2;
 
-    // ---- Q fragments with RoPE: lane holds query (l32) and channels 16kk+8g..+8
-    bf16x8 qf[2][8];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int row = r0 + wave * QW + qb * 32 + l32;
+    // ---- Q fragments with RoPE: lane holds query row l32 of this wave,
+    //      channels 16kk + 8g .. +8 (the B operand of S^T = K.Q^T)
+    bf16x8 qf[8];
+    {
+        const int row = r0 + wave * QW + l32;
         int t = 0, h = 0, w = 0;
         const bool valid = row < r1;
         const bool vid = valid && token_pos(A.segs, row, t, h, w);
@@ -236,145 +271,60 @@ __global__ __launch_bounds__(256, 1) void seg_attn_kernel(const AttnArgs A) {
         for (int kk = 0; kk < 8; ++kk) {
             uint4 x = valid ? src[2 * kk + g] : make_uint4(0, 0, 0, 0);
             if (vid) x = rope_group_f32(x, 2 * kk + g, t, h, w, A.rt);
-            qf[qb][kk] = __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, x.z, x.w});
+            qf[kk] = __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, x.z, x.w});
         }
     }
 
-    f32x16 o[2][4];
+    f32x16 o[4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
-    float m[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.0f, 0.0f};
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    float m = -INFINITY, lsum = 0.0f;
 
     const int nc = (A.Lc + BN - 1) / BN;
     const int nt = nc + (kend + BN - 1) / BN;
+    const bool odd = wave & 1;
 
     Prefetch pf;
-    if (nc > 0) { load_cache_tile(A, head, 0, tid, pf); store_cache_tile(pf, Ks[0], Vt[0], tid); }
-    else { load_new_tile(A, head, 0, kend, tid, pf); store_new_tile(A, pf, 0, kend, Ks[0], Vt[0], tid); }
+    load_tile(A, head, 0, nc, kend, tid, pf);
+    store_tile(A, 0, nc, kend, tid, pf, Ks[0], Vt[0]);
+    if (nt > 1) load_tile(A, head, 1, nc, kend, tid, pf);
     __syncthreads();
 
+    // Odd waves refill the other buffer before their tile math, even waves
+    // after it, so the two waves sharing a SIMD alternate between MFMA and
+    // VALU work.  Each refill immediately requests the tile after it.
     for (int j = 0; j < nt; ++j) {
         const int buf = j & 1;
-        const int jn = j + 1;
-        if (jn < nt) {
-            if (jn < nc) load_cache_tile(A, head, jn * BN, tid, pf);
-            else load_new_tile(A, head, (jn - nc) * BN, kend, tid, pf);
+        if (odd && j + 1 < nt) {
+            store_tile(A, j + 1, nc, kend, tid, pf, Ks[buf ^ 1], Vt[buf ^ 1]);
+            if (j + 2 < nt) load_tile(A, head, j + 2, nc, kend, tid, pf);
         }
         const int lim = (j < nc) ? min(BN, A.Lc - j * BN) : min(BN, kend - (j - nc) * BN);
-
-        // ---- S^T = K . Q^T
-        const uint16_t* K = Ks[buf];
-        f32x16 s[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.0f;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(K + (32 * kb + l32) * KSTR + 16 * kk + 8 * g);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], s[kb][qb], 0, 0, 0);
-            }
-        }
-        if (lim < BN) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= lim) { s[kb][0][r] = -INFINITY; s[kb][1][r] = -INFINITY; }
-                }
-        }
-
-        // ---- online softmax (base 2), P packed to bf16 in the B-operand layout
-        bf16x8 pb[2][4];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = mx * c;
-            if (__any(mn > m[qb] + 8.0f)) {
-                const float mnew = fmaxf(m[qb], mn);
-                const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-                lsum[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-                m[qb] = mnew;
-            }
-            const float nm = -m[qb];
-            float acc = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                uint32_t pk[8];
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c, nm));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r + 1], c, nm));
-                    acc += p0 + p1;
-                    pk[r >> 1] = pack_bf16(p0, p1);
-                }
-                pb[qb][2 * kb] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-                pb[qb][2 * kb + 1] = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
-            }
-            lsum[qb] += acc;
-        }
-
-        // ---- O^T += V^T . P^T
-        const uint16_t* V = Vt[buf];
-#pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const bf16x8 va = *reinterpret_cast<const bf16x8*>(V + (32 * db + l32) * VSTR + 16 * ch + 8 * g);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][ch], o[qb][db], 0, 0, 0);
-            }
-        }
-
-        if (jn < nt) {
-            if (jn < nc) store_cache_tile(pf, Ks[buf ^ 1], Vt[buf ^ 1], tid);
-            else store_new_tile(A, pf, (jn - nc) * BN, kend, Ks[buf ^ 1], Vt[buf ^ 1], tid);
+        if (lim == BN) tile_step<false>(Ks[buf], Vt[buf], qf, o, m, lsum, c, lim, g, l32);
+        else tile_step<true>(Ks[buf], Vt[buf], qf, o, m, lsum, c, lim, g, l32);
+        if (!odd && j + 1 < nt) {
+            store_tile(A, j + 1, nc, kend, tid, pf, Ks[buf ^ 1], Vt[buf ^ 1]);
+            if (j + 2 < nt) load_tile(A, head, j + 2, nc, kend, tid, pf);
         }
         __syncthreads();
     }
 
     // ---- epilogue: O / l -> bf16; lse = (m + log2 l) ln 2
+    const float lt = half_sum(lsum);
+    const float inv = 1.0f / lt;
+    const int row = r0 + wave * QW + l32;
+    if (row < r1) {
+        uint16_t* dst = A.out + ((int64_t)row * A.H + head) * D;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float lt = lsum[qb] + __shfl_xor(lsum[qb], 32);
-        const float inv = 1.0f / lt;
-        const int row = r0 + wave * QW + qb * 32 + l32;
-        if (row < r1) {
-            uint16_t* dst = A.out + ((int64_t)row * A.H + head) * D;
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int d0 = 32 * db + 8 * i + 4 * g;
-                    const f32x16& ov = o[qb][db];
-                    *reinterpret_cast<uint2*>(dst + d0) =
-                        make_uint2(pack_bf16(ov[4 * i] * inv, ov[4 * i + 1] * inv),
-                                   pack_bf16(ov[4 * i + 2] * inv, ov[4 * i + 3] * inv));
-                }
-            if (A.lse && g == 0) A.lse[(int64_t)head * A.Ln + row] = (m[qb] + __log2f(lt)) * 0.69314718055994531f;
-        }
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint2*>(dst + 32 * db + 8 * i + 4 * g) =
+                    make_uint2(pack_bf16(o[db][4 * i] * inv, o[db][4 * i + 1] * inv),
+                               pack_bf16(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv));
+        if (A.lse && g == 0) A.lse[(int64_t)head * A.Ln + row] = (m + __log2f(lt)) * 0.69314718055994531f;
     }
 }
 
@@ -401,7 +351,7 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.rt = rt;
     if (nt == 0) return NOMAS_OK;
     const int64_t blocks = (int64_t)nt * H;
-    hipLaunchKernelGGL(seg_attn_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, A);
+    hipLaunchKernelGGL(seg_attn_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, A);
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
 }
 

@@ -113,7 +113,9 @@ def _check_case(name, q, k, v, segs, cache, Lc, H):
     kc, vc, ks, vs = cache if Lc > 0 else (np.zeros((H, 0, 128), np.int8),) * 2 + (np.zeros((H, 0), np.float32),) * 2
     ref, lref = oracle.seg_attn(q, k, v, segs, kc, vc, ks, vs, Lc, SM)
     assert_close(got, ref, name)
-    np.testing.assert_allclose(lse, lref, rtol=0, atol=2e-3)
+    # the row sum is taken over the bf16-rounded probabilities that also feed
+    # P.V (relative error <= 2^-9 per term), so |lse error| <= ~2^-9 + fp32 terms
+    np.testing.assert_allclose(lse, lref, rtol=0, atol=2.0 ** -8)
 
 
 @pytest.mark.parametrize("mode", ["cache", "packed", "three"])
