@@ -43,6 +43,7 @@ int build_segs(const nomas_seg* segs, int n, SegTable* st, int64_t* total) {
         if (s.T > 0 && (s.Hg < 1 || s.Wg < 1)) return NOMAS_EINVAL;
         if (s.T > 0 && ((int64_t)s.t0 + s.T > NOMAS_MAX_T || s.Hg > NOMAS_MAX_HW || s.Wg > NOMAS_MAX_HW))
             return NOMAS_EUNSUPPORTED;
+        if ((int64_t)s.T * s.Hg * s.Wg >= ((int64_t)1 << 24)) return NOMAS_EUNSUPPORTED;   // float-estimated divisions
         const int64_t ntok = (int64_t)s.n_text + (int64_t)s.T * s.Hg * s.Wg;
         SegDev& d = st->s[i];
         d.start = (int32_t)start;
@@ -51,6 +52,8 @@ int build_segs(const nomas_seg* segs, int n, SegTable* st, int64_t* total) {
         d.T = s.T;
         d.Hg = s.T > 0 ? s.Hg : 1;
         d.Wg = s.T > 0 ? s.Wg : 1;
+        d.inv_hw = 1.0f / (float)(d.Hg * d.Wg);
+        d.inv_w = 1.0f / (float)d.Wg;
         start += ntok;
         if (start > kMaxTokens) return NOMAS_EUNSUPPORTED;
     }

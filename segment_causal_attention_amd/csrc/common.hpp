@@ -16,6 +16,7 @@ constexpr int NPAIR_HW = 28;            // RoPE pairs on the h and w axes (56 ch
 // token array plus the descriptor fields.
 struct SegDev {
     int32_t start, n_text, t0, T, Hg, Wg;
+    float inv_hw, inv_w;      // 1/(Hg*Wg) and 1/Wg, for the float-estimated divisions below
 };
 
 struct SegTable {
@@ -70,21 +71,46 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() is a full
+// workgroup fence, which also waits for every outstanding global load; the
+// key-tile prefetches must stay in flight across the per-tile barrier, and
+// only the LDS tile writes need to be visible to the other waves.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// n / d for 0 <= n < 2^24, d >= 1, from a float estimate with inv = 1/d:
+// the estimate is off by at most one, which one compare-and-step fixes.
+__device__ __forceinline__ int fdiv(int n, int d, float inv) {
+    int q = (int)((float)n * inv);
+    int r = n - q * d;
+    q += (r >= d) ? 1 : 0;
+    q -= (r < 0) ? 1 : 0;
+    return q;
+}
+
+// (t, h, w) of video token `loc` (counted from the first video token) of segment s.
+__device__ __forceinline__ void video_pos(const SegDev& s, int loc, int& t, int& h, int& w) {
+    const int hw = s.Hg * s.Wg;
+    const int tt = fdiv(loc, hw, s.inv_hw);
+    const int rem = loc - tt * hw;
+    const int hh = fdiv(rem, s.Wg, s.inv_w);
+    t = s.t0 + tt;
+    h = hh;
+    w = rem - hh * s.Wg;
+}
+
 // Position of token `idx` of the concatenated segments in `st`:
 // video flag and (t, h, w).
 __device__ __forceinline__ bool token_pos(const SegTable& st, int idx, int& t, int& h, int& w) {
     int a = 0;
     while (a + 1 < st.n && st.s[a + 1].start <= idx) ++a;
     const SegDev& s = st.s[a];
-    int loc = idx - s.start - s.n_text;
+    const int loc = idx - s.start - s.n_text;
     if (loc < 0) { t = h = w = 0; return false; }
-    int hw = s.Hg * s.Wg;
-    int tt = loc / hw;
-    int rem = loc - tt * hw;
-    int hh = rem / s.Wg;
-    t = s.t0 + tt;
-    h = hh;
-    w = rem - hh * s.Wg;
+    video_pos(s, loc, t, h, w);
     return true;
 }
 

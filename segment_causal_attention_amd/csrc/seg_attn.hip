@@ -86,43 +86,43 @@ __device__ __forceinline__ float i8(uint32_t word, int byte) {
     return (float)(int8_t)(word >> (8 * byte));
 }
 
+// Loads are never guarded: key indices are clamped into the allowed range
+// ([0, Lc) for the cache, [0, kend) for new keys), so every address is valid
+// and the clamped rows are keys this workgroup may see anyway.  Keys past the
+// range only occur in a tail tile, where their scores are masked to -inf and
+// their probabilities are exactly 0.
 __device__ __forceinline__ void load_tile(const AttnArgs& A, int head, int t, int nc, int kend, int tid,
                                           Prefetch& p) {
     const int krow = tid >> 3, kpart = tid & 7;
     const int kg = tid & 15, dq = tid >> 4;
     if (t < nc) {
-        const int key0 = t * BN;
-        const int64_t hb = (int64_t)head * A.cap;
-        const int key = key0 + krow;
-        if (key < A.Lc) {
-            p.a[0] = *reinterpret_cast<const uint4*>(A.kc + (hb + key) * D + 16 * kpart);
-            p.sc[0] = A.ks[hb + key];
-        } else {
-            p.a[0] = make_uint4(0, 0, 0, 0);
-            p.sc[0] = 0.0f;
-        }
+        const int key0 = t * BN, last = A.Lc - 1;
+        const int8_t* kc = A.kc + (int64_t)head * A.cap * D;
+        const int8_t* vc = A.vc + (int64_t)head * A.cap * D;
+        const float* ks = A.ks + (int64_t)head * A.cap;
+        const float* vs = A.vs + (int64_t)head * A.cap;
+        const int key = min(key0 + krow, last);
+        p.a[0] = *reinterpret_cast<const uint4*>(kc + (int64_t)key * D + 16 * kpart);
+        p.sc[0] = ks[key];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int kv = key0 + 4 * kg + i;
-            const bool ok = kv < A.Lc;
-            p.b[i] = ok ? *reinterpret_cast<const uint32_t*>(A.vc + (hb + kv) * D + 4 * dq) : 0u;
-            p.sc[1 + i] = ok ? A.vs[hb + kv] : 0.0f;
+            const int kv = min(key0 + 4 * kg + i, last);
+            p.b[i] = *reinterpret_cast<const uint32_t*>(vc + (int64_t)kv * D + 4 * dq);
+            p.sc[1 + i] = vs[kv];
         }
     } else {
-        const int key0 = (t - nc) * BN;
-        const int key = key0 + krow;
-        if (key < kend) {
-            const uint4* src = reinterpret_cast<const uint4*>(A.k + ((int64_t)key * A.H + head) * D + 16 * kpart);
-            p.a[0] = src[0];
-            p.a[1] = src[1];
-        } else {
-            p.a[0] = p.a[1] = make_uint4(0, 0, 0, 0);
-        }
+        const int key0 = (t - nc) * BN, last = kend - 1;
+        const int64_t rs = (int64_t)A.H * D;
+        const uint16_t* kb = A.k + head * D;
+        const uint16_t* vb = A.v + head * D;
+        const int key = min(key0 + krow, last);
+        const uint4* src = reinterpret_cast<const uint4*>(kb + key * rs + 16 * kpart);
+        p.a[0] = src[0];
+        p.a[1] = src[1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int kv = key0 + 4 * kg + i;
-            uint2 w = make_uint2(0, 0);
-            if (kv < kend) w = *reinterpret_cast<const uint2*>(A.v + ((int64_t)kv * A.H + head) * D + 4 * dq);
+            const int kv = min(key0 + 4 * kg + i, last);
+            const uint2 w = *reinterpret_cast<const uint2*>(vb + kv * rs + 4 * dq);
             p.b[2 * i] = w.x;
             p.b[2 * i + 1] = w.y;
         }
@@ -155,9 +155,17 @@ __device__ __forceinline__ void store_tile(const AttnArgs& A, int t, int nc, int
             *reinterpret_cast<uint2*>(Vt + (4 * dq + d) * VSTR + col) = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
         }
     } else {
-        const int key = (t - nc) * BN + krow;
+        const int key = min((t - nc) * BN + krow, kend - 1);
         int tt, h, w;
-        if (key < kend && token_pos(A.segs, key, tt, h, w)) {
+        bool vid;
+        if (A.segs.n == 1) {
+            const int loc = key - A.segs.s[0].n_text;
+            vid = loc >= 0;
+            if (vid) video_pos(A.segs.s[0], loc, tt, h, w);
+        } else {
+            vid = token_pos(A.segs, key, tt, h, w);
+        }
+        if (vid) {
             p.a[0] = rope_group_f32(p.a[0], 2 * kpart, tt, h, w, A.rt);
             p.a[1] = rope_group_f32(p.a[1], 2 * kpart + 1, tt, h, w, A.rt);
         }
@@ -262,14 +270,14 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     //      channels 16kk + 8g .. +8 (the B operand of S^T = K.Q^T)
     bf16x8 qf[8];
     {
-        const int row = r0 + wave * QW + l32;
+        // rows past the tile's end read the last row (never stored)
+        const int row = min(r0 + wave * QW + l32, r1 - 1);
         int t = 0, h = 0, w = 0;
-        const bool valid = row < r1;
-        const bool vid = valid && token_pos(A.segs, row, t, h, w);
+        const bool vid = token_pos(A.segs, row, t, h, w);
         const uint4* src = reinterpret_cast<const uint4*>(A.q + ((int64_t)row * A.H + head) * D);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            uint4 x = valid ? src[2 * kk + g] : make_uint4(0, 0, 0, 0);
+            uint4 x = src[2 * kk + g];
             if (vid) x = rope_group_f32(x, 2 * kk + g, t, h, w, A.rt);
             qf[kk] = __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, x.z, x.w});
         }
@@ -284,31 +292,44 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
 
     const int nc = (A.Lc + BN - 1) / BN;
     const int nt = nc + (kend + BN - 1) / BN;
-    const bool odd = wave & 1;
 
+    // Prefetch registers always hold the next tile to be written to LDS.  Loads
+    // are unconditional (tile indices clamped to the last tile, a harmless
+    // reload) and sit in straight-line code, so no wait for them is needed
+    // before their consumer one iteration later.
     Prefetch pf;
     load_tile(A, head, 0, nc, kend, tid, pf);
     store_tile(A, 0, nc, kend, tid, pf, Ks[0], Vt[0]);
-    if (nt > 1) load_tile(A, head, 1, nc, kend, tid, pf);
-    __syncthreads();
+    load_tile(A, head, min(1, nt - 1), nc, kend, tid, pf);
+    lds_barrier();
 
-    // Odd waves refill the other buffer before their tile math, even waves
-    // after it, so the two waves sharing a SIMD alternate between MFMA and
-    // VALU work.  Each refill immediately requests the tile after it.
-    for (int j = 0; j < nt; ++j) {
+    auto step = [&](int j) {
         const int buf = j & 1;
-        if (odd && j + 1 < nt) {
-            store_tile(A, j + 1, nc, kend, tid, pf, Ks[buf ^ 1], Vt[buf ^ 1]);
-            if (j + 2 < nt) load_tile(A, head, j + 2, nc, kend, tid, pf);
-        }
         const int lim = (j < nc) ? min(BN, A.Lc - j * BN) : min(BN, kend - (j - nc) * BN);
         if (lim == BN) tile_step<false>(Ks[buf], Vt[buf], qf, o, m, lsum, c, lim, g, l32);
         else tile_step<true>(Ks[buf], Vt[buf], qf, o, m, lsum, c, lim, g, l32);
-        if (!odd && j + 1 < nt) {
-            store_tile(A, j + 1, nc, kend, tid, pf, Ks[buf ^ 1], Vt[buf ^ 1]);
-            if (j + 2 < nt) load_tile(A, head, j + 2, nc, kend, tid, pf);
+    };
+    auto refill = [&](int j) {
+        // tile j+1 into the buffer tile j-1 used (every wave is past it), then
+        // request tile j+2; in the last iteration this rewrites an unused buffer
+        const int buf = j & 1;
+        store_tile(A, min(j + 1, nt - 1), nc, kend, tid, pf, Ks[buf ^ 1], Vt[buf ^ 1]);
+        load_tile(A, head, min(j + 2, nt - 1), nc, kend, tid, pf);
+    };
+    // Odd waves refill before their tile math, even waves after it, so the two
+    // waves sharing a SIMD alternate between MFMA and VALU work.
+    if (wave & 1) {
+        for (int j = 0; j < nt; ++j) {
+            refill(j);
+            step(j);
+            lds_barrier();
         }
-        __syncthreads();
+    } else {
+        for (int j = 0; j < nt; ++j) {
+            step(j);
+            refill(j);
+            lds_barrier();
+        }
     }
 
     // ---- epilogue: O / l -> bf16; lse = (m + log2 l) ln 2
