@@ -74,6 +74,8 @@ enum {
 #define NOMAS_MAX_T 16384          /* latent-frame positions t < NOMAS_MAX_T   */
 #define NOMAS_MAX_HW 1024          /* grid positions h, w < NOMAS_MAX_HW       */
 #define NOMAS_MAX_CAM 128          /* camera tokens per call                   */
+#define NOMAS_MAX_CACHE (1 << 24)  /* nomas_seg_attn: cache capacity (tokens)  */
+#define NOMAS_MAX_TOKEN_HEADS (1 << 23)  /* nomas_seg_attn: new tokens x heads */
 
 /*
  * 3D RoPE (comfyui-wiki news, 模型内部: axes [16, 56, 56], theta 256).
@@ -121,7 +123,8 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
  *   then the cache pointers may be NULL).
  * sm_scale > 0 (1/sqrt(128) for the model).
  * out: device, [Ln][H][128] bf16.  lse: device [H][Ln] float32 or NULL.
- * n_new_segs in [1, NOMAS_MAX_SEGS].
+ * n_new_segs in [1, NOMAS_MAX_SEGS]; cap <= NOMAS_MAX_CACHE and
+ * Ln * H <= NOMAS_MAX_TOKEN_HEADS, else NOMAS_EUNSUPPORTED.
  */
 int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,
                    const nomas_seg* new_segs, int n_new_segs,

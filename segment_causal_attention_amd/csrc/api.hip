@@ -179,6 +179,8 @@ int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf1
     int rc = build_segs(new_segs, n_new_segs, &st, &Ln);
     if (rc != NOMAS_OK) return rc;
     if (Ln == 0) return NOMAS_OK;
+    // the attention kernel addresses a head's cache and the new tokens with 32-bit offsets
+    if (cap > NOMAS_MAX_CACHE || Ln * H > NOMAS_MAX_TOKEN_HEADS) return NOMAS_EUNSUPPORTED;
     RopeTables rt;
     if ((rc = rope_tables(&rt)) != NOMAS_OK) return rc;
     return launch_seg_attn(q, k_new, v_new, st, (int)Ln, k_codes, v_codes, k_scale, v_scale, cap, (int)cache_len, H,

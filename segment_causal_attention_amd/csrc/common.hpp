@@ -24,16 +24,28 @@ struct SegTable {
     SegDev s[NOMAS_MAX_SEGS];
 };
 
-// Device addresses of the per-device RoPE tables.  Entry (p, i) of an axis
-// table holds (cos, sin) of p * 256^(-2i/d).
+// Device addresses of the per-device RoPE tables.  One float32 and one
+// float64 array each hold the three axis tables back to back: t at entry 0
+// ([NOMAS_MAX_T][8]), h at ROPE_H0 and w at ROPE_W0 ([NOMAS_MAX_HW][28]
+// each); entry (p, i) of an axis holds (cos, sin) of p * 256^(-2i/d).
+constexpr int ROPE_H0 = NOMAS_MAX_T * NPAIR_T;
+constexpr int ROPE_W0 = ROPE_H0 + NOMAS_MAX_HW * NPAIR_HW;
+constexpr int ROPE_N = ROPE_W0 + NOMAS_MAX_HW * NPAIR_HW;
 struct RopeTables {
-    const float2* t32;    // [NOMAS_MAX_T][8]
-    const float2* h32;    // [NOMAS_MAX_HW][28]
-    const float2* w32;    // [NOMAS_MAX_HW][28]
-    const double2* t64;
-    const double2* h64;
-    const double2* w64;
+    const float2* f32;
+    const double2* f64;
 };
+
+// First table entry for the 4 channel pairs held by the 8-channel group
+// `grp` (0..15) of a token at (t, h, w): groups 0-1 turn with t, 2-8 with h,
+// 9-15 with w (the axis chunks are multiples of 8 channels).  Integer
+// selects only, so lanes holding different groups do not diverge.
+__device__ __forceinline__ int rope_entry(int grp, int t, int h, int w) {
+    const int tt = t * NPAIR_T + 4 * grp;
+    const int hh = ROPE_H0 + h * NPAIR_HW + 4 * (grp - 2);
+    const int ww = ROPE_W0 + w * NPAIR_HW + 4 * (grp - 9);
+    return grp < 2 ? tt : (grp < 9 ? hh : ww);
+}
 
 // Builds the tables on the current device on first use; returns NOMAS_OK or
 // NOMAS_EHIP.  Thread-safe.
@@ -116,24 +128,19 @@ __device__ __forceinline__ bool token_pos(const SegTable& st, int idx, int& t, i
 
 // Rotate the 4 channel pairs held in a 16-byte group of 8 bf16 values at
 // channels [8*grp, 8*grp+8) of a token at (t, h, w); float32 arithmetic with
-// the float32 table, result rounded to bf16.  grp 0..1 -> t, 2..8 -> h,
-// 9..15 -> w (the axis chunks are multiples of 8 channels).
+// the float32 table, result rounded to bf16.
 __device__ __forceinline__ uint4 rope_group_f32(uint4 x, int grp, int t, int h, int w,
                                                 const RopeTables& rt) {
-    const float2* tab;
-    int base;
-    if (grp < 2) { tab = rt.t32 + t * NPAIR_T; base = 4 * grp; }
-    else if (grp < 9) { tab = rt.h32 + h * NPAIR_HW; base = 4 * (grp - 2); }
-    else { tab = rt.w32 + w * NPAIR_HW; base = 4 * (grp - 9); }
-    uint32_t in[4] = {x.x, x.y, x.z, x.w};
+    const float4* tab = reinterpret_cast<const float4*>(rt.f32 + rope_entry(grp, t, h, w));
+    const float4 c01 = tab[0], c23 = tab[1];      // (cos, sin) of pairs 0, 1 and 2, 3
+    const float cs[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
+    const uint32_t in[4] = {x.x, x.y, x.z, x.w};
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float2 cs = tab[base + i];
-        float x0 = bf16lo(in[i]), x1 = bf16hi(in[i]);
-        float y0 = x0 * cs.x - x1 * cs.y;
-        float y1 = x0 * cs.y + x1 * cs.x;
-        o[i] = pack_bf16(y0, y1);
+        const float c = cs[2 * i], sn = cs[2 * i + 1];
+        const float x0 = bf16lo(in[i]), x1 = bf16hi(in[i]);
+        o[i] = pack_bf16(x0 * c - x1 * sn, x0 * sn + x1 * c);
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
 }

@@ -39,15 +39,11 @@ __global__ __launch_bounds__(256) void rope3d_kernel(const uint4* __restrict__ x
     uint4 w = x[idx];
     int t, h, ww;
     if (token_pos(st, tok, t, h, ww)) {
-        const double2* tab;
-        int base;
-        if (grp < 2) { tab = rt.t64 + t * NPAIR_T; base = 4 * grp; }
-        else if (grp < 9) { tab = rt.h64 + h * NPAIR_HW; base = 4 * (grp - 2); }
-        else { tab = rt.w64 + ww * NPAIR_HW; base = 4 * (grp - 9); }
-        w.x = rot_pair_f64(w.x, tab[base + 0]);
-        w.y = rot_pair_f64(w.y, tab[base + 1]);
-        w.z = rot_pair_f64(w.z, tab[base + 2]);
-        w.w = rot_pair_f64(w.w, tab[base + 3]);
+        const double2* tab = rt.f64 + rope_entry(grp, t, h, ww);
+        w.x = rot_pair_f64(w.x, tab[0]);
+        w.y = rot_pair_f64(w.y, tab[1]);
+        w.z = rot_pair_f64(w.z, tab[2]);
+        w.w = rot_pair_f64(w.w, tab[3]);
     }
     y[idx] = w;
 }

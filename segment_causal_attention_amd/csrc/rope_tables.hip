@@ -13,12 +13,8 @@
 
 namespace nomas {
 
-__device__ float2 g_rope_t32[NOMAS_MAX_T * NPAIR_T];
-__device__ float2 g_rope_h32[NOMAS_MAX_HW * NPAIR_HW];
-__device__ float2 g_rope_w32[NOMAS_MAX_HW * NPAIR_HW];
-__device__ double2 g_rope_t64[NOMAS_MAX_T * NPAIR_T];
-__device__ double2 g_rope_h64[NOMAS_MAX_HW * NPAIR_HW];
-__device__ double2 g_rope_w64[NOMAS_MAX_HW * NPAIR_HW];
+__device__ __attribute__((aligned(16))) float2 g_rope32[ROPE_N];
+__device__ __attribute__((aligned(16))) double2 g_rope64[ROPE_N];
 
 double rope_angle(int p, int i, int d) {
     double omega = std::pow(256.0, -2.0 * (double)i / (double)d);
@@ -64,21 +60,23 @@ int rope_tables(RopeTables* out) {
         auto h32 = host_table<float2, float>(NOMAS_MAX_HW, NPAIR_HW, 56);
         auto t64 = host_table<double2, double>(NOMAS_MAX_T, NPAIR_T, 16);
         auto h64 = host_table<double2, double>(NOMAS_MAX_HW, NPAIR_HW, 56);
+        std::vector<float2> all32;
+        std::vector<double2> all64;
+        all32.reserve(ROPE_N);
+        all64.reserve(ROPE_N);
+        all32.insert(all32.end(), t32.begin(), t32.end());
+        all32.insert(all32.end(), h32.begin(), h32.end());   // h
+        all32.insert(all32.end(), h32.begin(), h32.end());   // w (same widths and frequencies)
+        all64.insert(all64.end(), t64.begin(), t64.end());
+        all64.insert(all64.end(), h64.begin(), h64.end());
+        all64.insert(all64.end(), h64.begin(), h64.end());
+        const void* a[2];
+        if (!upload(g_rope32, all32.data(), all32.size() * sizeof(float2), &a[0]) ||
+            !upload(g_rope64, all64.data(), all64.size() * sizeof(double2), &a[1]))
+            return NOMAS_EHIP;
         RopeTables r{};
-        const void* a[6];
-        bool ok = upload(g_rope_t32, t32.data(), t32.size() * sizeof(float2), &a[0]) &&
-                  upload(g_rope_h32, h32.data(), h32.size() * sizeof(float2), &a[1]) &&
-                  upload(g_rope_w32, h32.data(), h32.size() * sizeof(float2), &a[2]) &&
-                  upload(g_rope_t64, t64.data(), t64.size() * sizeof(double2), &a[3]) &&
-                  upload(g_rope_h64, h64.data(), h64.size() * sizeof(double2), &a[4]) &&
-                  upload(g_rope_w64, h64.data(), h64.size() * sizeof(double2), &a[5]);
-        if (!ok) return NOMAS_EHIP;
-        r.t32 = (const float2*)a[0];
-        r.h32 = (const float2*)a[1];
-        r.w32 = (const float2*)a[2];
-        r.t64 = (const double2*)a[3];
-        r.h64 = (const double2*)a[4];
-        r.w64 = (const double2*)a[5];
+        r.f32 = (const float2*)a[0];
+        r.f64 = (const double2*)a[1];
         g_tabs[dev] = r;
         g_ready[dev] = true;
     }

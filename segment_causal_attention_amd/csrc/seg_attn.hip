@@ -66,14 +66,29 @@ struct AttnArgs {
     RopeTables rt;
 };
 
-// This thread's share of one key tile on its way from HBM to LDS.
-//   K: thread owns key row tid/8, channels 16*(tid%8) .. +16
-//   V: thread owns keys 4*(tid%16) .. +4, channels 4*(tid/16) .. +4
+// This thread's share of one key tile on its way from HBM to LDS.  Both
+// kinds of tile fill all four registers, so the two load paths join without
+// copies:
+//   K: key row tid/8, channels 16*(tid%8) .. +16
+//   V: keys 4*(tid%16) .. +4, channels 4*(tid/16) .. +4
+//   cache tile: a0 = 16 K codes, a1.x = K scale, b0 = 4 keys x 4 V codes,
+//               b1 = the 4 V scales
+//   new tile:   a0, a1 = 16 K values (bf16), b0, b1 = 4 keys x 4 V values
 struct Prefetch {
-    uint4 a[2];       // K: cache 16 codes in a[0]; new 16 bf16 in a[0..1]
-    uint32_t b[8];    // V: cache 4 keys x 4 codes in b[0..3]; new 4 keys x 4 bf16 in b[0..7]
-    float sc[5];      // cache scales: K of the row, V of the 4 keys
+    uint4 a0, a1, b0, b1;
 };
+
+// Buffer descriptors of the key/value ranges one workgroup may read.  Each
+// covers exactly the allowed keys, so a read past them returns zeros: tail
+// keys of the last tile come back as zero vectors (their scores are masked)
+// and tokens of later segments are never read.
+struct Bufs {
+    __amdgpu_buffer_rsrc_t kc, vc, ks, vs, k, v;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
 
 // position (in the permuted V^T row) of key k, k a multiple of 4 inside a tile
 __device__ __forceinline__ int vperm(int k) {
@@ -86,59 +101,64 @@ __device__ __forceinline__ float i8(uint32_t word, int byte) {
     return (float)(int8_t)(word >> (8 * byte));
 }
 
-// Loads are never guarded: key indices are clamped into the allowed range
-// ([0, Lc) for the cache, [0, kend) for new keys), so every address is valid
-// and the clamped rows are keys this workgroup may see anyway.  Keys past the
-// range only occur in a tail tile, where their scores are masked to -inf and
-// their probabilities are exactly 0.
-__device__ __forceinline__ void load_tile(const AttnArgs& A, int head, int t, int nc, int kend, int tid,
-                                          Prefetch& p) {
-    const int krow = tid >> 3, kpart = tid & 7;
-    const int kg = tid & 15, dq = tid >> 4;
-    if (t < nc) {
-        const int key0 = t * BN, last = A.Lc - 1;
-        const int8_t* kc = A.kc + (int64_t)head * A.cap * D;
-        const int8_t* vc = A.vc + (int64_t)head * A.cap * D;
-        const float* ks = A.ks + (int64_t)head * A.cap;
-        const float* vs = A.vs + (int64_t)head * A.cap;
-        const int key = min(key0 + krow, last);
-        p.a[0] = *reinterpret_cast<const uint4*>(kc + (int64_t)key * D + 16 * kpart);
-        p.sc[0] = ks[key];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kv = min(key0 + 4 * kg + i, last);
-            p.b[i] = *reinterpret_cast<const uint32_t*>(vc + (int64_t)kv * D + 4 * dq);
-            p.sc[1 + i] = vs[kv];
-        }
+// Which keys a tile holds.  Full tiles come first (cache, then new keys),
+// the at most two partial tiles (cache tail, new-key tail) last.
+struct TileRef {
+    bool cache;
+    int key0, lim;      // first key, number of valid keys
+};
+
+__device__ __forceinline__ TileRef tile_at(int j, int Lc, int kend) {
+    const int ncf = Lc / BN, nnf = kend / BN;
+    if (j < ncf) return {true, j * BN, BN};
+    if (j < ncf + nnf) return {false, (j - ncf) * BN, BN};
+    if (j == ncf + nnf && Lc % BN) return {true, ncf * BN, Lc - ncf * BN};
+    return {false, nnf * BN, kend - nnf * BN};
+}
+
+__device__ __forceinline__ void load_tile(const Bufs& B, const TileRef& T, uint32_t rs, int tid, Prefetch& p) {
+    const uint32_t krow = tid >> 3, kpart = tid & 7;
+    const uint32_t kg = tid & 15, dq = tid >> 4;
+    if (T.cache) {
+        const uint32_t key = T.key0 + krow;
+        const uint32_t kv = T.key0 + 4 * kg;
+        p.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(B.kc, key * D + 16 * kpart, 0, 0));
+        p.a1 = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(B.ks, 4 * key, 0, 0), 0u, 0u, 0u);
+        const uint32_t vo = kv * D + 4 * dq;
+        p.b0 = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(B.vc, vo, 0, 0),
+                          __builtin_amdgcn_raw_buffer_load_b32(B.vc, vo + D, 0, 0),
+                          __builtin_amdgcn_raw_buffer_load_b32(B.vc, vo + 2 * D, 0, 0),
+                          __builtin_amdgcn_raw_buffer_load_b32(B.vc, vo + 3 * D, 0, 0));
+        p.b1 = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(B.vs, 4 * kv, 0, 0),
+                          __builtin_amdgcn_raw_buffer_load_b32(B.vs, 4 * kv + 4, 0, 0),
+                          __builtin_amdgcn_raw_buffer_load_b32(B.vs, 4 * kv + 8, 0, 0),
+                          __builtin_amdgcn_raw_buffer_load_b32(B.vs, 4 * kv + 12, 0, 0));
     } else {
-        const int key0 = (t - nc) * BN, last = kend - 1;
-        const int64_t rs = (int64_t)A.H * D;
-        const uint16_t* kb = A.k + head * D;
-        const uint16_t* vb = A.v + head * D;
-        const int key = min(key0 + krow, last);
-        const uint4* src = reinterpret_cast<const uint4*>(kb + key * rs + 16 * kpart);
-        p.a[0] = src[0];
-        p.a[1] = src[1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kv = min(key0 + 4 * kg + i, last);
-            const uint2 w = *reinterpret_cast<const uint2*>(vb + kv * rs + 4 * dq);
-            p.b[2 * i] = w.x;
-            p.b[2 * i + 1] = w.y;
-        }
+        const uint32_t key = T.key0 + krow;
+        const uint32_t kv = T.key0 + 4 * kg;
+        const uint32_t ko = key * rs + 32 * kpart;
+        p.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(B.k, ko, 0, 0));
+        p.a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(B.k, ko + 16, 0, 0));
+        const uint32_t vo = kv * rs + 8 * dq;
+        const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(B.v, vo, 0, 0);
+        const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(B.v, vo + rs, 0, 0);
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(B.v, vo + 2 * rs, 0, 0);
+        const auto v3 = __builtin_amdgcn_raw_buffer_load_b64(B.v, vo + 3 * rs, 0, 0);
+        p.b0 = make_uint4(v0[0], v0[1], v1[0], v1[1]);
+        p.b1 = make_uint4(v2[0], v2[1], v3[0], v3[1]);
     }
 }
 
-__device__ __forceinline__ void store_tile(const AttnArgs& A, int t, int nc, int kend, int tid, Prefetch& p,
+__device__ __forceinline__ void store_tile(const AttnArgs& A, const TileRef& T, int kend, int tid, Prefetch& p,
                                            uint16_t* Ks, uint16_t* Vt) {
     const int krow = tid >> 3, kpart = tid & 7;
     const int kg = tid & 15, dq = tid >> 4;
     uint4* kdst = reinterpret_cast<uint4*>(Ks + krow * KSTR + 16 * kpart);
     const int col = vperm(4 * kg);
-    if (t < nc) {
+    if (T.cache) {
         // K: 16 codes * scale -> bf16
-        const float s = p.sc[0];
-        const uint32_t w[4] = {p.a[0].x, p.a[0].y, p.a[0].z, p.a[0].w};
+        const float s = __uint_as_float(p.a1.x);
+        const uint32_t w[4] = {p.a0.x, p.a0.y, p.a0.z, p.a0.w};
         uint32_t o[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -148,35 +168,40 @@ __device__ __forceinline__ void store_tile(const AttnArgs& A, int t, int nc, int
         kdst[0] = make_uint4(o[0], o[1], o[2], o[3]);
         kdst[1] = make_uint4(o[4], o[5], o[6], o[7]);
         // V: 4 keys x 4 channels, transposed: one 4-key run per channel
+        const float s0 = __uint_as_float(p.b1.x), s1 = __uint_as_float(p.b1.y);
+        const float s2 = __uint_as_float(p.b1.z), s3 = __uint_as_float(p.b1.w);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const float x0 = i8(p.b[0], d) * p.sc[1], x1 = i8(p.b[1], d) * p.sc[2];
-            const float x2 = i8(p.b[2], d) * p.sc[3], x3 = i8(p.b[3], d) * p.sc[4];
+            const float x0 = i8(p.b0.x, d) * s0, x1 = i8(p.b0.y, d) * s1;
+            const float x2 = i8(p.b0.z, d) * s2, x3 = i8(p.b0.w, d) * s3;
             *reinterpret_cast<uint2*>(Vt + (4 * dq + d) * VSTR + col) = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
         }
     } else {
-        const int key = min((t - nc) * BN + krow, kend - 1);
+        // K rows past the allowed range read as zeros and stay zero (no rotation)
+        const int key = T.key0 + krow;
         int tt, h, w;
         bool vid;
         if (A.segs.n == 1) {
             const int loc = key - A.segs.s[0].n_text;
-            vid = loc >= 0;
+            vid = loc >= 0 && key < kend;
             if (vid) video_pos(A.segs.s[0], loc, tt, h, w);
         } else {
-            vid = token_pos(A.segs, key, tt, h, w);
+            vid = key < kend && token_pos(A.segs, key, tt, h, w);
         }
         if (vid) {
-            p.a[0] = rope_group_f32(p.a[0], 2 * kpart, tt, h, w, A.rt);
-            p.a[1] = rope_group_f32(p.a[1], 2 * kpart + 1, tt, h, w, A.rt);
+            p.a0 = rope_group_f32(p.a0, 2 * kpart, tt, h, w, A.rt);
+            p.a1 = rope_group_f32(p.a1, 2 * kpart + 1, tt, h, w, A.rt);
         }
-        kdst[0] = p.a[0];
-        kdst[1] = p.a[1];
+        kdst[0] = p.a0;
+        kdst[1] = p.a1;
+        // V: word j of key i holds channels 4dq + 2j, +1
+        const uint32_t wv[4][2] = {{p.b0.x, p.b0.y}, {p.b0.z, p.b0.w}, {p.b1.x, p.b1.y}, {p.b1.z, p.b1.w}};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int wi = d >> 1;
             const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t p01 = __builtin_amdgcn_perm(p.b[2 + wi], p.b[wi], sel);
-            const uint32_t p23 = __builtin_amdgcn_perm(p.b[6 + wi], p.b[4 + wi], sel);
+            const uint32_t p01 = __builtin_amdgcn_perm(wv[1][wi], wv[0][wi], sel);
+            const uint32_t p23 = __builtin_amdgcn_perm(wv[3][wi], wv[2][wi], sel);
             *reinterpret_cast<uint2*>(Vt + (4 * dq + d) * VSTR + col) = make_uint2(p01, p23);
         }
     }
@@ -199,6 +224,14 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ K, const 
             s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk), qf[kk],
                                                             s[kb], 0, 0, 0);
     }
+    // keep several K fragments in flight ahead of the MFMAs that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);       // 6 LDS reads
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -254,14 +287,16 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
-    const int head = blockIdx.x / A.ntq;
-    const int qt = blockIdx.x - head * A.ntq;
+    const int head = __builtin_amdgcn_readfirstlane(blockIdx.x / A.ntq);
+    const int qt = __builtin_amdgcn_readfirstlane(blockIdx.x - head * A.ntq);
 
     int a = 0;
     while (a + 1 < A.segs.n && A.tile0[a + 1] <= qt) ++a;
     const SegDev& sg = A.segs.s[a];
-    const int seg_end = sg.start + sg.n_text + sg.T * sg.Hg * sg.Wg;
-    const int r0 = sg.start + (qt - A.tile0[a]) * BM;
+    // workgroup-uniform values, kept in scalar registers so that tile choices
+    // are scalar branches and tile bases are scalar addresses
+    const int seg_end = __builtin_amdgcn_readfirstlane(sg.start + sg.n_text + sg.T * sg.Hg * sg.Wg);
+    const int r0 = __builtin_amdgcn_readfirstlane(sg.start + (qt - A.tile0[a]) * BM);
     const int r1 = min(r0 + BM, seg_end);
     const int kend = seg_end;                 // new keys [0, kend) are allowed
     const float c = A.scale_log2;
@@ -290,46 +325,63 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
 
-    const int nc = (A.Lc + BN - 1) / BN;
-    const int nt = nc + (kend + BN - 1) / BN;
+    const int nc = __builtin_amdgcn_readfirstlane((A.Lc + BN - 1) / BN);
+    const int nt = __builtin_amdgcn_readfirstlane(nc + (kend + BN - 1) / BN);
+
+    Bufs B;
+    {
+        const size_t hb = (size_t)head * A.cap;
+        B.kc = make_rsrc(A.kc + hb * D, (uint32_t)A.Lc * D);
+        B.vc = make_rsrc(A.vc + hb * D, (uint32_t)A.Lc * D);
+        B.ks = make_rsrc(A.ks + hb, (uint32_t)A.Lc * 4);
+        B.vs = make_rsrc(A.vs + hb, (uint32_t)A.Lc * 4);
+        // new tokens [0, kend) of this head: rows of H*128 bf16, this head's 128 at the front
+        const uint32_t bytes = (uint32_t)(kend - 1) * (uint32_t)A.H * D * 2 + D * 2;
+        B.k = make_rsrc(A.k + head * D, bytes);
+        B.v = make_rsrc(A.v + head * D, bytes);
+    }
+    const uint32_t rs = (uint32_t)A.H * D * 2;      // bytes per new-token row
 
     // Prefetch registers always hold the next tile to be written to LDS.  Loads
     // are unconditional (tile indices clamped to the last tile, a harmless
     // reload) and sit in straight-line code, so no wait for them is needed
     // before their consumer one iteration later.
+    const int nfull = __builtin_amdgcn_readfirstlane(A.Lc / BN + kend / BN);
     Prefetch pf;
-    load_tile(A, head, 0, nc, kend, tid, pf);
-    store_tile(A, 0, nc, kend, tid, pf, Ks[0], Vt[0]);
-    load_tile(A, head, min(1, nt - 1), nc, kend, tid, pf);
+    load_tile(B, tile_at(0, A.Lc, kend), rs, tid, pf);
+    store_tile(A, tile_at(0, A.Lc, kend), kend, tid, pf, Ks[0], Vt[0]);
+    load_tile(B, tile_at(min(1, nt - 1), A.Lc, kend), rs, tid, pf);
     lds_barrier();
 
-    auto step = [&](int j) {
-        const int buf = j & 1;
-        const int lim = (j < nc) ? min(BN, A.Lc - j * BN) : min(BN, kend - (j - nc) * BN);
-        if (lim == BN) tile_step<false>(Ks[buf], Vt[buf], qf, o, m, lsum, c, lim, g, l32);
-        else tile_step<true>(Ks[buf], Vt[buf], qf, o, m, lsum, c, lim, g, l32);
-    };
     auto refill = [&](int j) {
         // tile j+1 into the buffer tile j-1 used (every wave is past it), then
         // request tile j+2; in the last iteration this rewrites an unused buffer
         const int buf = j & 1;
-        store_tile(A, min(j + 1, nt - 1), nc, kend, tid, pf, Ks[buf ^ 1], Vt[buf ^ 1]);
-        load_tile(A, head, min(j + 2, nt - 1), nc, kend, tid, pf);
+        store_tile(A, tile_at(min(j + 1, nt - 1), A.Lc, kend), kend, tid, pf, Ks[buf ^ 1], Vt[buf ^ 1]);
+        load_tile(B, tile_at(min(j + 2, nt - 1), A.Lc, kend), rs, tid, pf);
     };
     // Odd waves refill before their tile math, even waves after it, so the two
-    // waves sharing a SIMD alternate between MFMA and VALU work.
+    // waves sharing a SIMD alternate between MFMA and VALU work.  Full tiles
+    // run without any masking; the partial tiles come last, in a loop of
+    // their own.
     if (wave & 1) {
-        for (int j = 0; j < nt; ++j) {
+        for (int j = 0; j < nfull; ++j) {
             refill(j);
-            step(j);
+            tile_step<false>(Ks[j & 1], Vt[j & 1], qf, o, m, lsum, c, BN, g, l32);
             lds_barrier();
         }
     } else {
-        for (int j = 0; j < nt; ++j) {
-            step(j);
+        for (int j = 0; j < nfull; ++j) {
+            tile_step<false>(Ks[j & 1], Vt[j & 1], qf, o, m, lsum, c, BN, g, l32);
             refill(j);
             lds_barrier();
         }
+    }
+    for (int j = nfull; j < nt; ++j) {
+        const int lim = tile_at(j, A.Lc, kend).lim;
+        tile_step<true>(Ks[j & 1], Vt[j & 1], qf, o, m, lsum, c, lim, g, l32);
+        refill(j);
+        lds_barrier();
     }
 
     // ---- epilogue: O / l -> bf16; lse = (m + log2 l) ln 2
