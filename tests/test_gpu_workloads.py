@@ -1,0 +1,174 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark uses.  Every output tensor is computed in full on the GPU; the
+oracle recomputes a seeded sample of rows (and of heads where a head's whole
+cache must be rebuilt on the CPU), which it can do row by row because rows
+are independent.
+
+  3 s turn     16,096 queries x 31,936 keys, every 16th row + the last 64, all heads
+  4 s segment  21,376 x 37,216, outlier channels x20, layers 0 and 53
+  full cache   63,360 x 316,800, cache built on the GPU (rope3d + quantise)
+  five turns   cache grown turn by turn to 253,440 tokens, camera cross-attention
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import segment_causal_attention_amd as nomas
+import synth
+from gpu_util import SM, assert_close, bits, cache_tensors, dev, dev16, f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(Lq, stride, tail=64, extra=()):
+    rows = set(range(0, Lq, stride)) | set(range(max(0, Lq - tail), Lq)) | set(extra)
+    return np.array(sorted(r for r in rows if 0 <= r < Lq))
+
+
+def run_attn(q, k, v, segs, cache, Lc, H):
+    kc, vc, ks, vs = cache
+    lse = torch.empty((H, q.shape[0]), dtype=torch.float32, device="cuda:0")
+    out = nomas.seg_attn(q, k, v, segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_rows(name, out, lse, inp_q, inp_k, inp_v, segs, ocache, Lc, rows, heads=None, gpu_heads=None):
+    """Oracle rows vs GPU rows; `heads` index the oracle's inputs, `gpu_heads`
+    the GPU output (the same heads unless the oracle got a head subset)."""
+    kc, vc, ks, vs = ocache
+    gpu_heads = heads if gpu_heads is None else gpu_heads
+    say("%s: oracle on %d rows x %s heads" % (name, len(rows), "all" if heads is None else len(heads)))
+    ref, lref = oracle.seg_attn(inp_q, inp_k, inp_v, segs, kc, vc, ks, vs, Lc, SM, rows=rows, heads=heads)
+    got = f64(out)[rows]
+    gl = lse.cpu().numpy()[:, rows]
+    if gpu_heads is not None:
+        got = got[:, gpu_heads]
+        gl = gl[gpu_heads]
+    assert_close(got, ref, name)
+    np.testing.assert_allclose(gl, lref, rtol=0, atol=2.0 ** -8)
+
+
+@pytest.mark.parametrize("cid,layer", [(2, 0), (3, 0), (3, 53)], ids=["turn3s", "seg4s-layer0", "seg4s-layer53"])
+def test_attention_with_oracle_cache(cid, layer):
+    """3 s turn and 4 s segment (with outliers): the INT8 history comes from
+    the oracle's quantiser, byte for byte."""
+    inp = synth.layer_inputs(cid, layer)
+    cfg = inp["cfg"]
+    if cfg.outliers:
+        assert len(inp["outlier_cols"]) == 20
+    say("config", cfg.name, "layer", layer, "Lq", cfg.Lq, "Lc", cfg.Lc)
+    ocache = oracle.build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs)
+    gcache = tuple(dev(a) for a in ocache)
+    out, lse = run_attn(dev16(inp["q"]), dev16(inp["k_new"]), dev16(inp["v_new"]), cfg.new_segs, gcache, cfg.Lc, cfg.H)
+    rows = sample_rows(cfg.Lq, 16 if cid == 2 else 64, extra=range(250, 262))
+    check_rows("%s layer %d" % (cfg.name, layer), out, lse, inp["q"], inp["k_new"], inp["v_new"], cfg.new_segs,
+               ocache, cfg.Lc, rows)
+
+
+def gpu_append(k_new_d, v_new_d, segs, cache, length):
+    """The path's per-segment cache update: rotate the keys, quantise, append."""
+    k_rot = nomas.rope3d(k_new_d, segs)
+    n = nomas.kv_quant_append(k_rot, v_new_d, *cache, length)
+    torch.cuda.synchronize()
+    return k_rot, n
+
+
+def oracle_head_rows(k_bits, v_bits, segs, h):
+    """The oracle's rotated bf16 keys and INT8 rows of one head."""
+    kr = oracle.bf16_round(oracle.rope3d(oracle.bf16_bits_to_f64(k_bits[:, h:h + 1]), segs))[:, 0]
+    kq, kscale = oracle.quantise(kr)
+    vq, vscale = oracle.quantise(oracle.bf16_bits_to_f64(v_bits[:, h]))
+    return kr, kq, kscale, vq, vscale
+
+
+def check_cache_rows(name, cache, start, k_rot_d, k_bits, v_bits, segs, heads):
+    """GPU-rotated keys equal the oracle's bf16 bits; GPU codes and scales
+    equal the oracle's quantisation bit for bit."""
+    kc, vc, ks, vs = cache
+    L = k_bits.shape[0]
+    for h in heads:
+        kr, kq, kscale, vq, vscale = oracle_head_rows(k_bits, v_bits, segs, h)
+        got_rot = bits(k_rot_d[:, h].contiguous())
+        mism = int(np.sum(got_rot != oracle.f64_to_bf16_bits(kr)))
+        say("%s head %d: rotated-key mismatches %d of %d" % (name, h, mism, got_rot.size))
+        assert mism == 0
+        assert np.array_equal(kc[h, start:start + L].cpu().numpy(), kq)
+        assert np.array_equal(vc[h, start:start + L].cpu().numpy(), vq)
+        assert np.array_equal(ks[h, start:start + L].cpu().numpy().view(np.uint32), kscale.view(np.uint32))
+        assert np.array_equal(vs[h, start:start + L].cpu().numpy().view(np.uint32), vscale.view(np.uint32))
+
+
+def test_full_cache_workload():
+    """12 s segment over 288 cached latent frames (~317K keys), cache built on
+    the GPU exactly as the benchmark builds it."""
+    inp = synth.layer_inputs(4)
+    cfg = inp["cfg"]
+    H, Lq, Lc = cfg.H, cfg.Lq, cfg.Lc
+    heads = [0, 9]
+    say("config", cfg.name, "Lq", Lq, "Lc", Lc)
+    cache = cache_tensors(H, Lc + Lq)
+    k_rot, n = gpu_append(dev16(inp["k_hist"]), dev16(inp["v_hist"]), cfg.hist_segs, cache, 0)
+    assert n == Lc
+    check_cache_rows("full-cache history", cache, 0, k_rot, inp["k_hist"], inp["v_hist"], cfg.hist_segs, heads)
+    del k_rot
+    out, lse = run_attn(dev16(inp["q"]), dev16(inp["k_new"]), dev16(inp["v_new"]), cfg.new_segs, cache, Lc, H)
+    # the oracle's own cache for the sampled heads (bit-identical to the GPU's, checked above)
+    sub = lambda a: np.ascontiguousarray(a[:, heads])
+    ocache = oracle.build_cache(sub(inp["k_hist"]), sub(inp["v_hist"]), cfg.hist_segs)
+    rows = sample_rows(Lq, 1024, tail=16, extra=range(880, 890))
+    check_rows("full cache", out, lse, sub(inp["q"]), sub(inp["k_new"]), sub(inp["v_new"]),
+               cfg.new_segs, ocache, Lc, rows, heads=list(range(len(heads))), gpu_heads=heads)
+
+
+def test_five_turns_growing_cache():
+    """Five 12 s turns: each turn attends over the cache of all earlier turns,
+    runs camera cross-attention, then rotates and appends its keys/values.
+    Quantisation is checked every turn, attention and camera on turns 0 and 4."""
+    cfg = synth.CONFIGS[5]
+    H = cfg.H
+    cap = 5 * synth.turn_seg(0).ntok
+    cache = cache_tensors(H, cap)
+    heads = [3, 12]
+    length = 0
+    okc = {h: [] for h in heads}
+    for k in range(5):
+        check = k in (0, 4)
+        inp = synth.turn_inputs(k, with_cam=check)
+        seg = inp["seg"]
+        say("turn", k, "cache", length)
+        kd, vd = dev16(inp["k_new"]), dev16(inp["v_new"])
+        if check:
+            out, lse = run_attn(dev16(inp["q"]), kd, vd, [seg], cache, length, H)
+            # oracle cache of earlier turns for the sampled heads, from its own quantiser
+            kcs = np.zeros((H, max(1, length), 128), np.int8)
+            vcs = np.zeros_like(kcs)
+            kss = np.zeros((H, max(1, length)), np.float32)
+            vss = np.zeros_like(kss)
+            for h in heads:
+                if length:
+                    kcs[h, :length] = np.concatenate([r[0] for r in okc[h]])
+                    vcs[h, :length] = np.concatenate([r[2] for r in okc[h]])
+                    kss[h, :length] = np.concatenate([r[1] for r in okc[h]])
+                    vss[h, :length] = np.concatenate([r[3] for r in okc[h]])
+            rows = sample_rows(seg.ntok, 2048, tail=16)
+            check_rows("turn %d" % k, out, lse, inp["q"], inp["k_new"], inp["v_new"], [seg],
+                       (kcs, vcs, kss, vss), length, rows, heads=heads)
+            # camera cross-attention of the turn's video queries
+            cam = nomas.cam_tokens(inp["c2w"])
+            cam_o = oracle.cam_tokens(inp["c2w"]).astype(np.float32)
+            np.testing.assert_allclose(cam, cam_o, rtol=0, atol=2e-6)
+            oc = nomas.cam_xattn(dev16(inp["q_cam"]), dev(cam_o), dev16(inp["w_k"]), dev16(inp["w_v"]), sm_scale=SM)
+            torch.cuda.synchronize()
+            crow = sample_rows(seg.ntok, 997, tail=8)
+            cref = oracle.cam_xattn(inp["q_cam"], cam_o, inp["w_k"], inp["w_v"], SM, rows=crow)
+            assert_close(f64(oc)[crow], cref, "turn %d camera" % k)
+        k_rot, n = gpu_append(kd, vd, [seg], cache, length)
+        check_cache_rows("turn %d append" % k, cache, length, k_rot, inp["k_new"], inp["v_new"], [seg], heads)
+        for h in heads:
+            _, kq, kscale, vq, vscale = oracle_head_rows(inp["k_new"], inp["v_new"], [seg], h)
+            okc[h].append((kq, kscale, vq, vscale))
+        length = n
+        del k_rot, kd, vd
+    assert length == cap
