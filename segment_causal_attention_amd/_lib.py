@@ -160,14 +160,15 @@ def kv_quant_append(k_rot, v, k_codes, v_codes, k_scale, v_scale, length: int, s
     return int(ln.value)
 
 
-def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None, v_scale=None,
+def seg_attn(q, k_rot, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None, v_scale=None,
              cache_len: int = 0, sm_scale: float = SM_SCALE, out=None, lse=None, stream=None):
-    """Segment-causal attention; returns out [Ln][H][128] bf16 (lse filled if given)."""
+    """Segment-causal attention; returns out [Ln][H][128] bf16 (lse filled if given).
+    q is taken before RoPE, k_rot after it (as rope3d returns it)."""
     import torch
     Ln, H = q.shape[0], q.shape[1]
     shp = (seg_tokens(new_segs), H, HEAD_DIM)
     _dev(q, "q", shp)
-    _dev(k_new, "k_new", shp)
+    _dev(k_rot, "k_rot", shp)
     _dev(v_new, "v_new", shp)
     cap = 0
     if cache_len > 0:
@@ -184,7 +185,7 @@ def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
     if lse is not None:
         _dev(lse, "lse", (H, Ln), 4)
     arr, n = seg_array(new_segs)
-    _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_new), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
+    _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_rot), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
                                 _ptr(k_scale), _ptr(v_scale), cap, int(cache_len), H, float(sm_scale),
                                 _ptr(out), _ptr(lse), _stream(stream)), "nomas_seg_attn")
     return out

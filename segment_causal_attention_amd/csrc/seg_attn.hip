@@ -6,18 +6,23 @@
 // cached token and to the new tokens of segments 0..a, never to a later
 // segment.  Cached K/V are INT8 with one fp32 scale per (token, head); the
 // attention itself runs in BF16 (comfyui-wiki, 单张 4090 配置): cached entries
-// enter the products as bf16(fl32(code*scale)), new Q/K are rotated by 3D RoPE
-// (comfyui-wiki, 模型内部: [16, 56, 56], theta 256) on load and rounded to bf16.
+// enter the products as bf16(fl32(code*scale)); queries are rotated by 3D
+// RoPE (comfyui-wiki, 模型内部: [16, 56, 56], theta 256) on load and rounded
+// to bf16; new keys arrive already rotated (the rows the cache append stores).
 //
-// Kernel shape.  One workgroup = 4 waves x 64 query rows = 256 rows of one
+// Kernel shape.  One workgroup = 8 waves x 32 query rows = 256 rows of one
 // head, all inside one new segment, so every row allows the same keys:
 // the cache [0, Lc) and the new tokens [0, end of its segment).  Later
-// segments are never loaded.  Keys stream through LDS in tiles of 64,
-// double-buffered: while the waves run the MFMAs of tile j from one buffer,
-// the registers already hold tile j+1 from HBM, which is then dequantised
-// (cache: int8 * scale -> bf16) or rotated (new keys: RoPE -> bf16) once per
-// workgroup and written to the other buffer.  V is written transposed
-// ([channel][key]) so that both products read 16 contiguous bytes per lane.
+// segments are never loaded.  Keys stream through three LDS buffers in tiles
+// of 64.  Tile j+2 is converted (cache: int8 * scale -> bf16; new keys: bf16
+// copy, V transposed) once per workgroup while the waves work on tiles j and
+// j+1, and each wave runs a software pipeline across tiles: the S^T products
+// of tile j+1 issue between the softmax instructions of tile j, and the O^T
+// products of tile j between the conversion instructions of tile j+2, so
+// every wave always has independent vector work between its matrix
+// instructions.  One LDS barrier per tile; HBM loads for tile j+3 are in
+// flight across it.  V^T is stored [channel][key] so that both products
+// read 16 contiguous bytes per lane.
 //
 // Both products put the query on the MFMA's N side (v_mfma_f32_32x32x16_bf16):
 //   S^T (keys x queries) = K (keys x d) . Q^T       A = K from LDS, B = Q in regs
@@ -32,6 +37,8 @@
 // Softmax is online in base 2 (scale folded into one fma) with a lazy
 // rescale: O and the sum are rescaled only when a row's max grows by more
 // than 8 (a factor 256), which keeps every exponent bounded.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace nomas {
@@ -47,6 +54,10 @@ constexpr int BM = NW * QW;         // query rows per workgroup
 constexpr int NT = NW * 64;         // threads per workgroup
 constexpr int KSTR = D + 8;         // LDS row stride of the K tile (bf16), padded
 constexpr int VSTR = BN + 8;        // LDS row stride of the V^T tile (bf16), padded
+#ifndef PF_DIST
+#define PF_DIST 4
+#endif
+constexpr int FD = PF_DIST;         // LDS fragment reads issued this many products ahead
 
 struct AttnArgs {
     const uint16_t* q;
@@ -101,25 +112,29 @@ __device__ __forceinline__ float i8(uint32_t word, int byte) {
     return (float)(int8_t)(word >> (8 * byte));
 }
 
-// Which keys a tile holds.  Full tiles come first (cache, then new keys),
-// the at most two partial tiles (cache tail, new-key tail) last.
+// Which keys a tile holds.  Cache tiles come first, [0, nc), then the new
+// keys' tiles; the last tile of each run may be partial.
 struct TileRef {
     bool cache;
     int key0, lim;      // first key, number of valid keys
 };
 
-__device__ __forceinline__ TileRef tile_at(int j, int Lc, int kend) {
-    const int ncf = Lc / BN, nnf = kend / BN;
-    if (j < ncf) return {true, j * BN, BN};
-    if (j < ncf + nnf) return {false, (j - ncf) * BN, BN};
-    if (j == ncf + nnf && Lc % BN) return {true, ncf * BN, Lc - ncf * BN};
-    return {false, nnf * BN, kend - nnf * BN};
+__device__ __forceinline__ TileRef tile_at(int j, int Lc, int nc, int kend) {
+    if (j < nc) return {true, j * BN, min(BN, Lc - j * BN)};
+    return {false, (j - nc) * BN, min(BN, kend - (j - nc) * BN)};
 }
 
+// What a stretch of steps knows about its tiles at compile time: all cache,
+// all new keys, or either (a scalar branch per tile).  Each kind issues one
+// fixed sequence of loads, so the wait before a conversion counts exactly
+// the loads issued after it.
+enum TileKind { KIND_CACHE = 0, KIND_NEW = 1, KIND_ANY = 2 };
+
+template <int KIND>
 __device__ __forceinline__ void load_tile(const Bufs& B, const TileRef& T, uint32_t rs, int tid, Prefetch& p) {
     const uint32_t krow = tid >> 3, kpart = tid & 7;
     const uint32_t kg = tid & 15, dq = tid >> 4;
-    if (T.cache) {
+    if (KIND == KIND_CACHE || (KIND == KIND_ANY && T.cache)) {
         const uint32_t key = T.key0 + krow;
         const uint32_t kv = T.key0 + 4 * kg;
         p.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(B.kc, key * D + 16 * kpart, 0, 0));
@@ -149,140 +164,208 @@ __device__ __forceinline__ void load_tile(const Bufs& B, const TileRef& T, uint3
     }
 }
 
-__device__ __forceinline__ void store_tile(const AttnArgs& A, const TileRef& T, int kend, int tid, Prefetch& p,
-                                           uint16_t* Ks, uint16_t* Vt) {
-    const int krow = tid >> 3, kpart = tid & 7;
-    const int kg = tid & 15, dq = tid >> 4;
-    uint4* kdst = reinterpret_cast<uint4*>(Ks + krow * KSTR + 16 * kpart);
-    const int col = vperm(4 * kg);
-    if (T.cache) {
-        // K: 16 codes * scale -> bf16
-        const float s = __uint_as_float(p.a1.x);
-        const uint32_t w[4] = {p.a0.x, p.a0.y, p.a0.z, p.a0.w};
-        uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            o[2 * i] = pack_bf16(i8(w[i], 0) * s, i8(w[i], 1) * s);
-            o[2 * i + 1] = pack_bf16(i8(w[i], 2) * s, i8(w[i], 3) * s);
-        }
-        kdst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        kdst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        // V: 4 keys x 4 channels, transposed: one 4-key run per channel
-        const float s0 = __uint_as_float(p.b1.x), s1 = __uint_as_float(p.b1.y);
-        const float s2 = __uint_as_float(p.b1.z), s3 = __uint_as_float(p.b1.w);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const float x0 = i8(p.b0.x, d) * s0, x1 = i8(p.b0.y, d) * s1;
-            const float x2 = i8(p.b0.z, d) * s2, x3 = i8(p.b0.w, d) * s3;
-            *reinterpret_cast<uint2*>(Vt + (4 * dq + d) * VSTR + col) = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
-        }
-    } else {
-        // K rows past the allowed range read as zeros and stay zero (no rotation)
-        const int key = T.key0 + krow;
-        int tt, h, w;
-        bool vid;
-        if (A.segs.n == 1) {
-            const int loc = key - A.segs.s[0].n_text;
-            vid = loc >= 0 && key < kend;
-            if (vid) video_pos(A.segs.s[0], loc, tt, h, w);
-        } else {
-            vid = key < kend && token_pos(A.segs, key, tt, h, w);
-        }
-        if (vid) {
-            p.a0 = rope_group_f32(p.a0, 2 * kpart, tt, h, w, A.rt);
-            p.a1 = rope_group_f32(p.a1, 2 * kpart + 1, tt, h, w, A.rt);
-        }
-        kdst[0] = p.a0;
-        kdst[1] = p.a1;
-        // V: word j of key i holds channels 4dq + 2j, +1
-        const uint32_t wv[4][2] = {{p.b0.x, p.b0.y}, {p.b0.z, p.b0.w}, {p.b1.x, p.b1.y}, {p.b1.z, p.b1.w}};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int wi = d >> 1;
-            const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t p01 = __builtin_amdgcn_perm(wv[1][wi], wv[0][wi], sel);
-            const uint32_t p23 = __builtin_amdgcn_perm(wv[3][wi], wv[2][wi], sel);
-            *reinterpret_cast<uint2*>(Vt + (4 * dq + d) * VSTR + col) = make_uint2(p01, p23);
-        }
-    }
+// Per-wave state carried across key tiles.
+struct WaveState {
+    bf16x8 qf[8];        // Q^T fragments (B operand): query l32, channels 16kk + 8g .. +8
+    f32x16 o[4];         // O^T accumulators: channels 32db + 8i + 4g + j, query l32
+    float m, lsum;       // running max (base 2, scaled) and partial row sum of this lane half
+};
+
+// Nothing is scheduled across this point: it pins the order of the slots of
+// the pipelined loop body.
+#define SLOT_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// A operand of the i-th S^T product of a tile: key block i%2, channels 16(i/2)
+__device__ __forceinline__ bf16x8 kfrag(const uint16_t* K, int krd, int i) {
+    return *reinterpret_cast<const bf16x8*>(K + krd + 32 * (i & 1) * KSTR + 16 * (i >> 1));
+}
+// A operand of the i-th O^T product of a tile: channel block i%4, key chunk i/4
+__device__ __forceinline__ bf16x8 vfrag(const uint16_t* V, int vrd, int i) {
+    return *reinterpret_cast<const bf16x8*>(V + vrd + 32 * (i & 3) * VSTR + 16 * (i >> 2));
 }
 
-// One 64-key tile for the 32 query rows of this wave: S^T = K.Q^T, online
-// softmax, O^T += V^T.P^T.  MASK: keys at or beyond `lim` are excluded.
-template <bool MASK>
-__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                          const bf16x8 (&qf)[8], f32x16 (&o)[4], float& m, float& lsum,
-                                          float c, int lim, int g, int l32) {
-    f32x16 s[2];
-    const f32x16 zero = {};
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Scores of keys at or past lim (partial tiles) -> -inf.  Register r of block
+// kb holds key 32kb + 8(r/4) + 4g + r%4.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lim, int g) {
+    const int limg = lim - 4 * g;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const uint16_t* kr = K + (32 * kb + l32) * KSTR + 8 * g;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr), qf[0], zero, 0, 0, 0);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kk = 1; kk < 8; ++kk)
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk), qf[kk],
-                                                            s[kb], 0, 0, 0);
-    }
-    // keep several K fragments in flight ahead of the MFMAs that use them
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);       // 6 LDS reads
+        for (int r = 0; r < 16; ++r) {
+            if (32 * kb + 8 * (r >> 2) + (r & 3) >= limg) s[kb][r] = -INFINITY;
+            if ((r & 3) == 3) SLOT_FENCE();
+        }
+}
+
+__device__ __forceinline__ float max_part(const f32x16 (&s)[2], int r0, int r1, float mx) {
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-    if (MASK) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) >= lim) s[kb][r] = -INFINITY;
-    }
-    float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    for (int r = r0; r < r1; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    return mx;
+}
+
+// Row max of the tile (both lane halves) against the running max; O and the
+// sum are rescaled only when the max grows by more than 8 (a factor 256).
+__device__ __forceinline__ void update_max(float mx, WaveState& w, float c) {
     mx = half_max(mx);
     const float mn = mx * c;
-    if (__any(mn > m + 8.0f)) {
-        const float mnew = fmaxf(m, mn);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        lsum *= alpha;
+    if (__any(mn > w.m + 8.0f)) {
+        const float mnew = fmaxf(w.m, mn);
+        const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
+        w.lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        m = mnew;
+            for (int r = 0; r < 16; ++r) w.o[db][r] *= alpha;
+        w.m = mnew;
     }
-    const float nm = -m;
-    bf16x8 pb[4];
+}
+
+// Probability pair q (0..15) of the tile: keys of registers 2(q%8), +1 of
+// block q/8, exp2(s c - m) rounded to bf16 and packed; the row sum is taken
+// over the same bf16 values.  Words 4ch .. 4ch+3 form the B operand of key
+// chunk ch of the O^T product.
+__device__ __forceinline__ void prob_pair(const f32x16 (&s)[2], int q, WaveState& w, float c, uint32_t (&pk)[16]) {
     const nm_bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const int kb = q >> 3, r = 2 * (q & 7);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -w.m));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -w.m));
+    pk[q] = pack_bf16(p0, p1);
+    w.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(nm_bf16x2, pk[q]), ones, w.lsum, false);
+}
+
+__device__ __forceinline__ bf16x8 pchunk(const uint32_t (&pk)[16], int ch) {
+    return __builtin_bit_cast(bf16x8, u32x4{pk[4 * ch], pk[4 * ch + 1], pk[4 * ch + 2], pk[4 * ch + 3]});
+}
+
+// ---------------------------------------------------------------------------
+// HBM tile -> LDS tile, in units small enough to sit between two matrix
+// instructions.  Thread tid writes K row tid/8, channels 16(tid%8) .. +16 and
+// V^T channels 4(tid/16) .. +4 at keys 4(tid%16) .. +4.
+
+struct StoreDst {
+    uint4* k;            // K row tid/8, channels 16(tid%8)
+    uint16_t* v;         // V^T row 4(tid/16), permuted column of key 4(tid%16)
+};
+
+__device__ __forceinline__ StoreDst store_dst(uint16_t* Ks, uint16_t* Vt, int tid) {
+    return {reinterpret_cast<uint4*>(Ks + (tid >> 3) * KSTR + 16 * (tid & 7)), Vt + 4 * (tid >> 4) * VSTR + vperm(4 * (tid & 15))};
+}
+
+// cache tile, K: word u (4 codes) of the 16, times the key's scale; the two
+// 16-byte halves are written after words 1 and 3
+__device__ __forceinline__ void cache_k_unit(int u, const Prefetch& p, uint32_t (&o)[4], const StoreDst& d) {
+    const float s = __uint_as_float(p.a1.x);
+    const uint32_t w = u == 0 ? p.a0.x : u == 1 ? p.a0.y : u == 2 ? p.a0.z : p.a0.w;
+    o[2 * (u & 1)] = pack_bf16(i8(w, 0) * s, i8(w, 1) * s);
+    o[2 * (u & 1) + 1] = pack_bf16(i8(w, 2) * s, i8(w, 3) * s);
+    if (u & 1) d.k[u >> 1] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// cache tile, V: channel dq of the thread's 4, over its 4 keys
+__device__ __forceinline__ void cache_v_unit(int dq, const Prefetch& p, const StoreDst& d) {
+    const float x0 = i8(p.b0.x, dq) * __uint_as_float(p.b1.x), x1 = i8(p.b0.y, dq) * __uint_as_float(p.b1.y);
+    const float x2 = i8(p.b0.z, dq) * __uint_as_float(p.b1.z), x3 = i8(p.b0.w, dq) * __uint_as_float(p.b1.w);
+    *reinterpret_cast<uint2*>(d.v + dq * VSTR) = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
+}
+
+// new-key tile, V: word pairs of the 4 keys regrouped per channel
+__device__ __forceinline__ void new_v_unit(int dq, const Prefetch& p, const StoreDst& d) {
+    const uint32_t sel = (dq & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t w0 = (dq >> 1) ? p.b0.y : p.b0.x, w1 = (dq >> 1) ? p.b0.w : p.b0.z;
+    const uint32_t w2 = (dq >> 1) ? p.b1.y : p.b1.x, w3 = (dq >> 1) ? p.b1.w : p.b1.z;
+    *reinterpret_cast<uint2*>(d.v + dq * VSTR) =
+        make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
+}
+
+// new-key tile, K: the 16 rotated bf16 values copied as they are
+__device__ __forceinline__ void new_k_unit(int half, const Prefetch& p, const StoreDst& d) {
+    d.k[half] = half ? p.a1 : p.a0;
+}
+
+// Whole-tile store, unscheduled (prologue).
+__device__ __forceinline__ void store_tile(const TileRef& T, int tid, const Prefetch& p, uint16_t* Ks, uint16_t* Vt) {
+    const StoreDst d = store_dst(Ks, Vt, tid);
+    if (T.cache) {
+        uint32_t o[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        uint32_t pk[8];
+        for (int u = 0; u < 4; ++u) cache_k_unit(u, p, o, d);
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, nm));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, nm));
-            pk[r >> 1] = pack_bf16(p0, p1);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(nm_bf16x2, pk[r >> 1]), ones, lsum, false);
-        }
-        pb[2 * kb] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-        pb[2 * kb + 1] = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+        for (int dq = 0; dq < 4; ++dq) cache_v_unit(dq, p, d);
+    } else {
+        new_k_unit(0, p, d);
+        new_k_unit(1, p, d);
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq) new_v_unit(dq, p, d);
     }
+}
+
+// ---------------------------------------------------------------------------
+// The pipelined step j.  The S^T products of tile j+1 (K from LDS) run
+// interleaved with the row max and probabilities of tile j; then the O^T
+// products of tile j run interleaved with the conversion of tile j+2 (HBM
+// data already in registers) into the third LDS buffer.  Every slot holds
+// one matrix instruction, the LDS read of the operand two slots ahead and a
+// short run of independent vector work, so each wave keeps issuing while its
+// matrix instructions execute.
+
+template <int KIND>
+__device__ __forceinline__ void pipelined_step(const uint16_t* Kn, const uint16_t* V, uint16_t* K2, uint16_t* V2,
+                                               bool cache2, int lim, int tid, int krd, int vrd, const Prefetch& pf,
+                                               WaveState& w, f32x16 (&s)[2], f32x16 (&sn)[2], float c, int g) {
+    if (KIND != KIND_ANY) cache2 = KIND == KIND_CACHE;
+    if (lim < BN) mask_tile(s, lim, g);
+    uint32_t pk[16];
+    {
+        const f32x16 zero = {};
+        bf16x8 kf[16];
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+        for (int i = 0; i < FD; ++i) kf[i] = kfrag(Kn, krd, i);
+        SLOT_FENCE();
+        float mx = 0.0f;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(V + (32 * db + l32) * VSTR + 16 * ch + 8 * g);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ch], o[db], 0, 0, 0);
+        for (int i = 0; i < 16; ++i) {
+            if (i + FD < 16) kf[i + FD] = kfrag(Kn, krd, i + FD);
+            sn[i & 1] = mfma(kf[i], w.qf[i >> 1], i < 2 ? zero : sn[i & 1]);
+            if (i == 0) mx = max_part(s, 0, 8, fmaxf(s[0][0], s[1][0]));
+            else if (i == 1) mx = max_part(s, 8, 16, mx);
+            else if (i == 2) update_max(mx, w, c);
+            else prob_pair(s, i - 3, w, c, pk);
+            SLOT_FENCE();
         }
+    }
+    // O^T products of tile j with the conversion of tile j+2; the tile kind
+    // is a scalar branch inside each slot, so the accumulators never pass
+    // through a join
+    const StoreDst d = store_dst(K2, V2, tid);
+    bf16x8 vf[16];
+#pragma unroll
+    for (int i = 0; i < FD; ++i) vf[i] = vfrag(V, vrd, i);
+    SLOT_FENCE();
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i + FD < 16) vf[i + FD] = vfrag(V, vrd, i + FD);
+        w.o[i & 3] = mfma(vf[i], pchunk(pk, i >> 2), w.o[i & 3]);
+        if (i < 3) {
+            prob_pair(s, 13 + i, w, c, pk);
+        } else if (i < 7) {
+            if (cache2) cache_k_unit(i - 3, pf, o, d);
+            else new_v_unit(i - 3, pf, d);
+        } else if (i < 11) {
+            if (cache2) cache_v_unit(i - 7, pf, d);
+            else if (i < 9) new_k_unit(i - 7, pf, d);
+        }
+        SLOT_FENCE();
     }
 }
 
 __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[3][BN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[3][D * VSTR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -303,29 +386,27 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
 
     // ---- Q fragments with RoPE: lane holds query row l32 of this wave,
     //      channels 16kk + 8g .. +8 (the B operand of S^T = K.Q^T)
-    bf16x8 qf[8];
+    WaveState ws;
     {
         // rows past the tile's end read the last row (never stored)
         const int row = min(r0 + wave * QW + l32, r1 - 1);
         int t = 0, h = 0, w = 0;
-        const bool vid = token_pos(A.segs, row, t, h, w);
+        if (!token_pos(A.segs, row, t, h, w)) t = h = w = 0;   // text: identity rotation
         const uint4* src = reinterpret_cast<const uint4*>(A.q + ((int64_t)row * A.H + head) * D);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            uint4 x = src[2 * kk + g];
-            if (vid) x = rope_group_f32(x, 2 * kk + g, t, h, w, A.rt);
-            qf[kk] = __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, x.z, x.w});
+            const uint4 x = rope_group_f32(src[2 * kk + g], 2 * kk + g, t, h, w, A.rt);
+            ws.qf[kk] = __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, x.z, x.w});
         }
     }
-
-    f32x16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    float m = -INFINITY, lsum = 0.0f;
+        for (int r = 0; r < 16; ++r) ws.o[db][r] = 0.0f;
+    ws.m = -INFINITY;
+    ws.lsum = 0.0f;
 
-    const int nc = __builtin_amdgcn_readfirstlane((A.Lc + BN - 1) / BN);
+    const int nc = __builtin_amdgcn_readfirstlane((A.Lc + BN - 1) / BN);   // cache tiles
     const int nt = __builtin_amdgcn_readfirstlane(nc + (kend + BN - 1) / BN);
 
     Bufs B;
@@ -341,51 +422,76 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
         B.v = make_rsrc(A.v + head * D, bytes);
     }
     const uint32_t rs = (uint32_t)A.H * D * 2;      // bytes per new-token row
+    const int krd = l32 * KSTR + 8 * g;             // this lane's K / V^T fragment offsets
+    const int vrd = l32 * VSTR + 8 * g;
 
-    // Prefetch registers always hold the next tile to be written to LDS.  Loads
-    // are unconditional (tile indices clamped to the last tile, a harmless
-    // reload) and sit in straight-line code, so no wait for them is needed
-    // before their consumer one iteration later.
-    const int nfull = __builtin_amdgcn_readfirstlane(A.Lc / BN + kend / BN);
-    Prefetch pf;
-    load_tile(B, tile_at(0, A.Lc, kend), rs, tid, pf);
-    store_tile(A, tile_at(0, A.Lc, kend), kend, tid, pf, Ks[0], Vt[0]);
-    load_tile(B, tile_at(min(1, nt - 1), A.Lc, kend), rs, tid, pf);
+    // Three LDS buffers: step j reads K of tile j+1 and V of tile j and
+    // writes tile j+2.  Two prefetch register sets alternate between steps:
+    // the set converted in step j was loaded in step j-2, two steps ahead of
+    // its use.  Loads are unconditional (tile indices clamped to the last
+    // tile, a harmless reload) and straight-line.
+    auto tile = [&](int j) { return tile_at(min(j, nt - 1), A.Lc, nc, kend); };
+    Prefetch pa, pb;
+    load_tile<KIND_ANY>(B, tile(0), rs, tid, pa);
+    load_tile<KIND_ANY>(B, tile(1), rs, tid, pb);
+    store_tile(tile(0), tid, pa, Ks[0], Vt[0]);
+    load_tile<KIND_ANY>(B, tile(2), rs, tid, pa);
+    store_tile(tile(1), tid, pb, Ks[1], Vt[1]);
+    load_tile<KIND_ANY>(B, tile(3), rs, tid, pb);
     lds_barrier();
 
-    auto refill = [&](int j) {
-        // tile j+1 into the buffer tile j-1 used (every wave is past it), then
-        // request tile j+2; in the last iteration this rewrites an unused buffer
-        const int buf = j & 1;
-        store_tile(A, tile_at(min(j + 1, nt - 1), A.Lc, kend), kend, tid, pf, Ks[buf ^ 1], Vt[buf ^ 1]);
-        load_tile(B, tile_at(min(j + 2, nt - 1), A.Lc, kend), rs, tid, pf);
+    f32x16 sa[2], sb[2];
+    {
+        const f32x16 zero = {};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sa[i & 1] = mfma(kfrag(Ks[0], krd, i), ws.qf[i >> 1], i < 2 ? zero : sa[i & 1]);
+    }
+    // Step j: scores of tile j in x, next tile's scores into y; LDS buffer b0
+    // holds tile j; pf holds tile j+2 and is refilled with tile j+4.  Steps
+    // past the last tile see a fully masked tile and change nothing.  Steps
+    // go in pairs, so the score and prefetch sets swap roles without copies.
+    auto step = [&](auto kind, int j, int b0, f32x16 (&x)[2], f32x16 (&y)[2], Prefetch& pf) {
+        constexpr int K = decltype(kind)::value;
+        const int b1 = b0 == 2 ? 0 : b0 + 1;
+        const int b2 = b1 == 2 ? 0 : b1 + 1;
+        const int lim = j < nt ? tile(j).lim : 0;
+        pipelined_step<K>(Ks[b1], Vt[b0], Ks[b2], Vt[b2], tile(j + 2).cache, lim, tid, krd, vrd, pf, ws, x, y, c, g);
+        load_tile<K>(B, tile(j + 4), rs, tid, pf);
+        lds_barrier();
+        return b1;
     };
-    // Odd waves refill before their tile math, even waves after it, so the two
-    // waves sharing a SIMD alternate between MFMA and VALU work.  Full tiles
-    // run without any masking; the partial tiles come last, in a loop of
-    // their own.
-    if (wave & 1) {
-        for (int j = 0; j < nfull; ++j) {
-            refill(j);
-            tile_step<false>(Ks[j & 1], Vt[j & 1], qf, o, m, lsum, c, BN, g, l32);
-            lds_barrier();
-        }
-    } else {
-        for (int j = 0; j < nfull; ++j) {
-            tile_step<false>(Ks[j & 1], Vt[j & 1], qf, o, m, lsum, c, BN, g, l32);
-            refill(j);
-            lds_barrier();
+    const std::integral_constant<int, KIND_CACHE> cache_kind;
+    const std::integral_constant<int, KIND_NEW> new_kind;
+    const std::integral_constant<int, KIND_ANY> any_kind;
+    // all outstanding loads complete before a specialised stretch, so its
+    // waits are counted from its own loads only
+    const auto drain = [] { __builtin_amdgcn_s_waitcnt(0x0f70); };   // vmcnt(0)
+    int j = 0, b = 0;
+    if (j + 5 < nc) {
+        drain();
+        for (; j + 5 < nc; j += 2) {          // tiles j .. j+5 all from the cache
+            b = step(cache_kind, j, b, sa, sb, pa);
+            b = step(cache_kind, j + 1, b, sb, sa, pb);
         }
     }
-    for (int j = nfull; j < nt; ++j) {
-        const int lim = tile_at(j, A.Lc, kend).lim;
-        tile_step<true>(Ks[j & 1], Vt[j & 1], qf, o, m, lsum, c, lim, g, l32);
-        refill(j);
-        lds_barrier();
+    for (; j < nt && !(j + 2 >= nc && j + 5 < nt); j += 2) {
+        b = step(any_kind, j, b, sa, sb, pa);
+        b = step(any_kind, j + 1, b, sb, sa, pb);
+    }
+    if (j + 5 < nt) {
+        drain();
+        for (; j + 5 < nt; j += 2) {          // tiles j+2 .. j+5 all new keys
+            b = step(new_kind, j, b, sa, sb, pa);
+            b = step(new_kind, j + 1, b, sb, sa, pb);
+        }
+    }
+    for (; j < nt; j += 2) {
+        b = step(any_kind, j, b, sa, sb, pa);
+        b = step(any_kind, j + 1, b, sb, sa, pb);
     }
 
     // ---- epilogue: O / l -> bf16; lse = (m + log2 l) ln 2
-    const float lt = half_sum(lsum);
+    const float lt = half_sum(ws.lsum);
     const float inv = 1.0f / lt;
     const int row = r0 + wave * QW + l32;
     if (row < r1) {
@@ -395,9 +501,9 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<uint2*>(dst + 32 * db + 8 * i + 4 * g) =
-                    make_uint2(pack_bf16(o[db][4 * i] * inv, o[db][4 * i + 1] * inv),
-                               pack_bf16(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv));
-        if (A.lse && g == 0) A.lse[(int64_t)head * A.Ln + row] = (m + __log2f(lt)) * 0.69314718055994531f;
+                    make_uint2(pack_bf16(ws.o[db][4 * i] * inv, ws.o[db][4 * i + 1] * inv),
+                               pack_bf16(ws.o[db][4 * i + 2] * inv, ws.o[db][4 * i + 3] * inv));
+        if (A.lse && g == 0) A.lse[(int64_t)head * A.Ln + row] = (ws.m + __log2f(lt)) * 0.69314718055994531f;
     }
 }
 
