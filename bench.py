@@ -135,6 +135,7 @@ def main():
     out = torch.empty_like(q)
     out_cam = torch.empty_like(q_cam)
     k_rot = torch.empty_like(k_new)
+    ws = torch.empty(nomas.seg_attn_workspace([seg], Lc, H), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -146,7 +147,8 @@ def main():
         nomas.rope3d(k_new, [seg], out=k_rot, stream=stream)
         if i is not None:
             ev[i][0].record(stream)
-        nomas.seg_attn(q, k_rot, v_new, [seg], kc, vc, ks, vs, cache_len=Lc, sm_scale=sm, out=out, stream=stream)
+        nomas.seg_attn(q, k_rot, v_new, [seg], kc, vc, ks, vs, cache_len=Lc, sm_scale=sm, out=out, workspace=ws,
+                       stream=stream)
         if i is not None:
             ev[i][1].record(stream)
         nomas.cam_xattn(q_cam, cam, w_k, w_v, sm_scale=sm, out=out_cam, stream=stream)

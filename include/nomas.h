@@ -125,6 +125,11 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
  *   then the cache pointers may be NULL).
  * sm_scale > 0 (1/sqrt(128) for the model).
  * out: device, [Ln][H][128] bf16.  lse: device [H][Ln] float32 or NULL.
+ * workspace: device scratch of at least nomas_seg_attn_workspace(...)
+ *   bytes, 16-byte aligned, owned by the caller; the call overwrites it
+ *   (the keys laid out as 64-key tiles, about 140 bytes per cached or new
+ *   token and head), so two calls in flight must not share one.  Too small
+ *   or NULL: NOMAS_EINVAL.
  * n_new_segs in [1, NOMAS_MAX_SEGS]; cap <= NOMAS_MAX_CACHE and
  * Ln * H <= NOMAS_MAX_TOKEN_HEADS, else NOMAS_EUNSUPPORTED.
  */
@@ -133,7 +138,16 @@ int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_rot, const nomas_bf1
                    const int8_t* k_codes, const int8_t* v_codes,
                    const float* k_scale, const float* v_scale,
                    int64_t cap, int64_t cache_len, int H, float sm_scale,
-                   nomas_bf16* out, float* lse, void* stream);
+                   nomas_bf16* out, float* lse, void* workspace, int64_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Workspace bytes nomas_seg_attn needs for these new segments, cache length
+ * and head count (H * ceil((cache_len + Ln) / 64) * 35840), or a negative
+ * error code (NOMAS_EINVAL / NOMAS_EUNSUPPORTED as for nomas_seg_attn).
+ * Host only.
+ */
+int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len, int H);
 
 /*
  * Camera tokens of one turn (comfyui-wiki news, 相机控制作为一等输入).

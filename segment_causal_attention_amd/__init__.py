@@ -8,5 +8,5 @@ this package only marshals arguments.  Build it with
 from ._lib import (  # noqa: F401
     EHIP, ECAPACITY, EINVAL, EUNSUPPORTED, HEAD_DIM, MAX_CAM, MAX_SEGS, OK, SM_SCALE, SYMBOLS,
     NomasError, Seg, cam_tokens, cam_xattn, kv_quant_append, lib, rope3d, rope_table, seg_array,
-    seg_attn, seg_tokens, strerror, version,
+    seg_attn, seg_attn_workspace, seg_tokens, strerror, version,
 )

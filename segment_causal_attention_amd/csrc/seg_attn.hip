@@ -10,19 +10,24 @@
 // RoPE (comfyui-wiki, 模型内部: [16, 56, 56], theta 256) on load and rounded
 // to bf16; new keys arrive already rotated (the rows the cache append stores).
 //
-// Kernel shape.  One workgroup = 8 waves x 32 query rows = 256 rows of one
-// head, all inside one new segment, so every row allows the same keys:
-// the cache [0, Lc) and the new tokens [0, end of its segment).  Later
-// segments are never loaded.  Keys stream through three LDS buffers in tiles
-// of 64.  Tile j+2 is converted (cache: int8 * scale -> bf16; new keys: bf16
-// copy, V transposed) once per workgroup while the waves work on tiles j and
-// j+1, and each wave runs a software pipeline across tiles: the S^T products
-// of tile j+1 issue between the softmax instructions of tile j, and the O^T
-// products of tile j between the conversion instructions of tile j+2, so
-// every wave always has independent vector work between its matrix
-// instructions.  One LDS barrier per tile; HBM loads for tile j+3 are in
-// flight across it.  V^T is stored [channel][key] so that both products
-// read 16 contiguous bytes per lane.
+// Two kernels.  The pack kernel lays the keys a call can touch (the cache,
+// then the new tokens) out as 64-key tiles, each a byte image of what the
+// attention kernel wants in LDS: the K tile [key][channel] and the V^T tile
+// [channel][key], bf16, rows padded against bank conflicts, cache entries
+// dequantised, tail keys zero.  It is bound by HBM and runs once per call.
+// The attention kernel then copies tile images into LDS with buffer-to-LDS
+// DMA (no registers, no conversion, no LDS stores), three tiles ahead into
+// four buffers, and spends its vector instructions on the softmax alone:
+// on gfx950 an MFMA hides only a few vector instructions, so every one taken
+// out of the key loop shortens it.
+//
+// Attention kernel shape.  One workgroup = 8 waves x 32 query rows = 256 rows
+// of one head, all inside one new segment, so every row allows the same keys:
+// the cache [0, Lc) and the new tokens [0, end of its segment), i.e. a prefix
+// of the packed key range; later segments are masked in the last tile.  Each
+// wave runs a software pipeline across tiles: the S^T products of tile j+1
+// issue between the softmax instructions of tile j, then the O^T products of
+// tile j.  One LDS barrier per tile.
 //
 // Both products put the query on the MFMA's N side (v_mfma_f32_32x32x16_bf16):
 //   S^T (keys x queries) = K (keys x d) . Q^T       A = K from LDS, B = Q in regs
@@ -37,8 +42,6 @@
 // Softmax is online in base 2 (scale folded into one fma) with a lazy
 // rescale: O and the sum are rescaled only when a row's max grows by more
 // than 8 (a factor 256), which keeps every exponent bounded.
-#include <type_traits>
-
 #include "common.hpp"
 
 namespace nomas {
@@ -52,59 +55,20 @@ constexpr int NW = 8;               // waves per workgroup (2 per SIMD)
 constexpr int QW = 32;              // query rows per wave
 constexpr int BM = NW * QW;         // query rows per workgroup
 constexpr int NT = NW * 64;         // threads per workgroup
-constexpr int KSTR = D + 8;         // LDS row stride of the K tile (bf16), padded
-constexpr int VSTR = BN + 8;        // LDS row stride of the V^T tile (bf16), padded
-#ifndef PF_DIST
-#define PF_DIST 4
-#endif
-constexpr int FD = PF_DIST;         // LDS fragment reads issued this many products ahead
+constexpr int KSTR = D + 8;         // row stride of the K tile image (bf16), padded
+constexpr int VSTR = BN + 8;        // row stride of the V^T tile image (bf16), padded
+constexpr int KIMG = BN * KSTR * 2;           // bytes of the K tile image
+constexpr int VIMG = D * VSTR * 2;            // bytes of the V^T tile image
+constexpr int TILE_BYTES = KIMG + VIMG;       // 35840
+constexpr int TILE_KB = TILE_BYTES / 1024;    // 35 one-kilobyte DMA copies per tile
+constexpr int NBUF = 4;             // LDS tile buffers
+constexpr int FD = 2;               // LDS fragment reads issued this many products ahead
+static_assert(TILE_BYTES % 1024 == 0, "tile images are copied in 1 KB pieces");
 
-struct AttnArgs {
-    const uint16_t* q;
-    const uint16_t* k;
-    const uint16_t* v;
-    const int8_t* kc;
-    const int8_t* vc;
-    const float* ks;
-    const float* vs;
-    uint16_t* out;
-    float* lse;
-    int64_t cap;
-    int32_t Lc, Ln, H, ntq;         // ntq: query tiles per head
-    float scale_log2;               // sm_scale * log2(e)
-    int32_t tile0[NOMAS_MAX_SEGS + 1];   // first query tile of each new segment
-    SegTable segs;
-    RopeTables rt;
-};
-
-// This thread's share of one key tile on its way from HBM to LDS.  Both
-// kinds of tile fill all four registers, so the two load paths join without
-// copies:
-//   K: key row tid/8, channels 16*(tid%8) .. +16
-//   V: keys 4*(tid%16) .. +4, channels 4*(tid/16) .. +4
-//   cache tile: a0 = 16 K codes, a1.x = K scale, b0 = 4 keys x 4 V codes,
-//               b1 = the 4 V scales
-//   new tile:   a0, a1 = 16 K values (bf16), b0, b1 = 4 keys x 4 V values
-struct Prefetch {
-    uint4 a0, a1, b0, b1;
-};
-
-// Buffer descriptors of the key/value ranges one workgroup may read.  Each
-// covers exactly the allowed keys, so a read past them returns zeros: tail
-// keys of the last tile come back as zero vectors (their scores are masked)
-// and tokens of later segments are never read.
-struct Bufs {
-    __amdgpu_buffer_rsrc_t kc, vc, ks, vs, k, v;
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-// position (in the permuted V^T row) of key k, k a multiple of 4 inside a tile
-__device__ __forceinline__ int vperm(int k) {
-    int w = k & 15;
-    int p = (w == 4) ? 8 : (w == 8) ? 4 : w;
+// position (in the permuted V^T row) of key k of a tile
+__device__ __forceinline__ int vperm_key(int k) {
+    const int w = k & 15;
+    const int p = w < 4 ? w : w < 8 ? w + 4 : w < 12 ? w - 4 : w;
     return (k & ~15) + p;
 }
 
@@ -112,56 +76,98 @@ __device__ __forceinline__ float i8(uint32_t word, int byte) {
     return (float)(int8_t)(word >> (8 * byte));
 }
 
-// Which keys a tile holds.  Cache tiles come first, [0, nc), then the new
-// keys' tiles; the last tile of each run may be partial.
-struct TileRef {
-    bool cache;
-    int key0, lim;      // first key, number of valid keys
+// ---------------------------------------------------------------------------
+// Pack kernel: one workgroup of 256 threads builds the image of tile t of
+// head h.  Key x of the packed range is cache token x for x < Lc, new token
+// x - Lc for x < Lc + Ln, and zero beyond.
+
+struct PackArgs {
+    const int8_t* kc;
+    const int8_t* vc;
+    const float* ks;
+    const float* vs;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint8_t* img;
+    int64_t cap;
+    int32_t Lc, Ln, H, ntk;         // ntk: tiles per head
 };
 
-__device__ __forceinline__ TileRef tile_at(int j, int Lc, int nc, int kend) {
-    if (j < nc) return {true, j * BN, min(BN, Lc - j * BN)};
-    return {false, (j - nc) * BN, min(BN, kend - (j - nc) * BN)};
+constexpr int PACK_NT = 256;
+
+// the 8 bf16 values of channels 8j .. 8j+7 of packed key x (as 4 words)
+__device__ __forceinline__ uint4 key_chunk(const PackArgs& P, int h, int x, int j, bool is_v) {
+    if (x < P.Lc) {
+        const size_t row = (size_t)h * P.cap + x;
+        const int8_t* codes = (is_v ? P.vc : P.kc) + row * D + 8 * j;
+        const float s = (is_v ? P.vs : P.ks)[row];
+        const uint2 w = *reinterpret_cast<const uint2*>(codes);
+        return make_uint4(pack_bf16(i8(w.x, 0) * s, i8(w.x, 1) * s), pack_bf16(i8(w.x, 2) * s, i8(w.x, 3) * s),
+                          pack_bf16(i8(w.y, 0) * s, i8(w.y, 1) * s), pack_bf16(i8(w.y, 2) * s, i8(w.y, 3) * s));
+    }
+    if (x < P.Lc + P.Ln) {
+        const uint16_t* src = (is_v ? P.v : P.k) + ((size_t)(x - P.Lc) * P.H + h) * D + 8 * j;
+        return *reinterpret_cast<const uint4*>(src);
+    }
+    return make_uint4(0, 0, 0, 0);
 }
 
-// What a stretch of steps knows about its tiles at compile time: all cache,
-// all new keys, or either (a scalar branch per tile).  Each kind issues one
-// fixed sequence of loads, so the wait before a conversion counts exactly
-// the loads issued after it.
-enum TileKind { KIND_CACHE = 0, KIND_NEW = 1, KIND_ANY = 2 };
-
-template <int KIND>
-__device__ __forceinline__ void load_tile(const Bufs& B, const TileRef& T, uint32_t rs, int tid, Prefetch& p) {
-    const uint32_t krow = tid >> 3, kpart = tid & 7;
-    const uint32_t kg = tid & 15, dq = tid >> 4;
-    if (KIND == KIND_CACHE || (KIND == KIND_ANY && T.cache)) {
-        const uint32_t key = T.key0 + krow;
-        const uint32_t kv = T.key0 + 4 * kg;
-        p.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(B.kc, key * D + 16 * kpart, 0, 0));
-        p.a1 = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(B.ks, 4 * key, 0, 0), 0u, 0u, 0u);
-        const uint32_t vo = kv * D + 4 * dq;
-        p.b0 = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(B.vc, vo, 0, 0),
-                          __builtin_amdgcn_raw_buffer_load_b32(B.vc, vo + D, 0, 0),
-                          __builtin_amdgcn_raw_buffer_load_b32(B.vc, vo + 2 * D, 0, 0),
-                          __builtin_amdgcn_raw_buffer_load_b32(B.vc, vo + 3 * D, 0, 0));
-        p.b1 = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(B.vs, 4 * kv, 0, 0),
-                          __builtin_amdgcn_raw_buffer_load_b32(B.vs, 4 * kv + 4, 0, 0),
-                          __builtin_amdgcn_raw_buffer_load_b32(B.vs, 4 * kv + 8, 0, 0),
-                          __builtin_amdgcn_raw_buffer_load_b32(B.vs, 4 * kv + 12, 0, 0));
-    } else {
-        const uint32_t key = T.key0 + krow;
-        const uint32_t kv = T.key0 + 4 * kg;
-        const uint32_t ko = key * rs + 32 * kpart;
-        p.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(B.k, ko, 0, 0));
-        p.a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(B.k, ko + 16, 0, 0));
-        const uint32_t vo = kv * rs + 8 * dq;
-        const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(B.v, vo, 0, 0);
-        const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(B.v, vo + rs, 0, 0);
-        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(B.v, vo + 2 * rs, 0, 0);
-        const auto v3 = __builtin_amdgcn_raw_buffer_load_b64(B.v, vo + 3 * rs, 0, 0);
-        p.b0 = make_uint4(v0[0], v0[1], v1[0], v1[1]);
-        p.b1 = make_uint4(v2[0], v2[1], v3[0], v3[1]);
+__global__ __launch_bounds__(PACK_NT) void pack_kernel(const PackArgs P) {
+    __shared__ __attribute__((aligned(16))) uint8_t im[TILE_BYTES];
+    const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int x0 = t * BN;
+    // K: 64 keys x 16 chunks of 8 channels, 4 chunks per thread
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + PACK_NT * i, key = c >> 4, j = c & 15;
+        *reinterpret_cast<uint4*>(im + key * KSTR * 2 + 16 * j) = key_chunk(P, h, x0 + key, j, false);
     }
+    // V^T: thread = (key, channel chunk); its 8 channels go to 8 rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + PACK_NT * i, key = c >> 4, j = c & 15;
+        const uint4 w = key_chunk(P, h, x0 + key, j, true);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        uint16_t* col = reinterpret_cast<uint16_t*>(im + KIMG) + vperm_key(key);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) col[(8 * j + e) * VSTR] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+    }
+    // padding of the K rows (64) and V^T rows (128): zero
+    if (tid < BN) *reinterpret_cast<uint4*>(im + tid * KSTR * 2 + 2 * D) = make_uint4(0, 0, 0, 0);
+    if (tid < D) *reinterpret_cast<uint4*>(im + KIMG + tid * VSTR * 2 + 2 * BN) = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(P.img + ((size_t)h * P.ntk + t) * TILE_BYTES);
+    for (int i = tid; i < TILE_BYTES / 16; i += PACK_NT) dst[i] = reinterpret_cast<const uint4*>(im)[i];
+}
+
+// ---------------------------------------------------------------------------
+// Attention kernel
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint8_t* img;             // packed tile images
+    uint16_t* out;
+    float* lse;
+    int32_t Lc, Ln, H, ntq, ntk;    // ntq: query tiles per head, ntk: key tiles per head
+    float scale_log2;               // sm_scale * log2(e)
+    int32_t tile0[NOMAS_MAX_SEGS + 1];   // first query tile of each new segment
+    SegTable segs;
+    RopeTables rt;
+};
+
+// One kilobyte of a tile image into LDS: lane l's 16 bytes, read at byte
+// voff + soff of the resource, land at LDS byte m0 + 16 l.  Written as inline
+// assembly so that the compiler does not tie LDS reads to outstanding DMA
+// (it would wait for every copy in flight); the key loop waits itself.
+__device__ __forceinline__ void dma_1k(uint32_t m0, uint32_t voff, u32x4 rs, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+
+// wait until at most N buffer-to-LDS copies of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_dma() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 // Per-wave state carried across key tiles.
@@ -242,130 +248,75 @@ __device__ __forceinline__ bf16x8 pchunk(const uint32_t (&pk)[16], int ch) {
 }
 
 // ---------------------------------------------------------------------------
-// HBM tile -> LDS tile, in units small enough to sit between two matrix
-// instructions.  Thread tid writes K row tid/8, channels 16(tid%8) .. +16 and
-// V^T channels 4(tid/16) .. +4 at keys 4(tid%16) .. +4.
+// The pipelined step j: 32 slots, each holding one matrix instruction, the
+// LDS read of the operand FD slots ahead and a few vector instructions.
+// Slots 0-15 issue the S^T products of tile j+1, slots 16-31 the O^T
+// products of tile j.  The row max of tile j runs in slots 0-2; each
+// probability pair is formed over three slots (scale and shift, exp2, pack
+// and sum) so that no slot holds a chain of dependent vector instructions.
 
-struct StoreDst {
-    uint4* k;            // K row tid/8, channels 16(tid%8)
-    uint16_t* v;         // V^T row 4(tid/16), permuted column of key 4(tid%16)
-};
-
-__device__ __forceinline__ StoreDst store_dst(uint16_t* Ks, uint16_t* Vt, int tid) {
-    return {reinterpret_cast<uint4*>(Ks + (tid >> 3) * KSTR + 16 * (tid & 7)), Vt + 4 * (tid >> 4) * VSTR + vperm(4 * (tid & 15))};
-}
-
-// cache tile, K: word u (4 codes) of the 16, times the key's scale; the two
-// 16-byte halves are written after words 1 and 3
-__device__ __forceinline__ void cache_k_unit(int u, const Prefetch& p, uint32_t (&o)[4], const StoreDst& d) {
-    const float s = __uint_as_float(p.a1.x);
-    const uint32_t w = u == 0 ? p.a0.x : u == 1 ? p.a0.y : u == 2 ? p.a0.z : p.a0.w;
-    o[2 * (u & 1)] = pack_bf16(i8(w, 0) * s, i8(w, 1) * s);
-    o[2 * (u & 1) + 1] = pack_bf16(i8(w, 2) * s, i8(w, 3) * s);
-    if (u & 1) d.k[u >> 1] = make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-// cache tile, V: channel dq of the thread's 4, over its 4 keys
-__device__ __forceinline__ void cache_v_unit(int dq, const Prefetch& p, const StoreDst& d) {
-    const float x0 = i8(p.b0.x, dq) * __uint_as_float(p.b1.x), x1 = i8(p.b0.y, dq) * __uint_as_float(p.b1.y);
-    const float x2 = i8(p.b0.z, dq) * __uint_as_float(p.b1.z), x3 = i8(p.b0.w, dq) * __uint_as_float(p.b1.w);
-    *reinterpret_cast<uint2*>(d.v + dq * VSTR) = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
-}
-
-// new-key tile, V: word pairs of the 4 keys regrouped per channel
-__device__ __forceinline__ void new_v_unit(int dq, const Prefetch& p, const StoreDst& d) {
-    const uint32_t sel = (dq & 1) ? 0x07060302u : 0x05040100u;
-    const uint32_t w0 = (dq >> 1) ? p.b0.y : p.b0.x, w1 = (dq >> 1) ? p.b0.w : p.b0.z;
-    const uint32_t w2 = (dq >> 1) ? p.b1.y : p.b1.x, w3 = (dq >> 1) ? p.b1.w : p.b1.z;
-    *reinterpret_cast<uint2*>(d.v + dq * VSTR) =
-        make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
-}
-
-// new-key tile, K: the 16 rotated bf16 values copied as they are
-__device__ __forceinline__ void new_k_unit(int half, const Prefetch& p, const StoreDst& d) {
-    d.k[half] = half ? p.a1 : p.a0;
-}
-
-// Whole-tile store, unscheduled (prologue).
-__device__ __forceinline__ void store_tile(const TileRef& T, int tid, const Prefetch& p, uint16_t* Ks, uint16_t* Vt) {
-    const StoreDst d = store_dst(Ks, Vt, tid);
-    if (T.cache) {
-        uint32_t o[4];
+// max of 16 values as a tree of three-input maxima
+__device__ __forceinline__ float max16(const f32x16 (&s)[2], int r0) {
+    float m[6];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) cache_k_unit(u, p, o, d);
-#pragma unroll
-        for (int dq = 0; dq < 4; ++dq) cache_v_unit(dq, p, d);
+    for (int i = 0; i < 5; ++i) {
+        const int k = r0 + (3 * i) / 2;
+        m[i] = (3 * i) % 2 == 0 ? fmaxf(fmaxf(s[0][k], s[1][k]), s[0][k + 1])
+                                : fmaxf(fmaxf(s[1][k], s[0][k + 1]), s[1][k + 1]);
+    }
+    m[5] = s[1][r0 + 7];
+    return fmaxf(fmaxf(fmaxf(m[0], m[1]), m[2]), fmaxf(fmaxf(m[3], m[4]), m[5]));
+}
+
+// probability pair q in three stages; t holds the pairs in flight
+__device__ __forceinline__ void prob_stage(int stage, int q, const f32x16 (&s)[2], WaveState& w, float c,
+                                           float (&t)[4][2], uint32_t (&pk)[16]) {
+    const int kb = q >> 3, r = 2 * (q & 7);
+    float* x = t[q & 3];
+    if (stage == 0) {
+        x[0] = fmaf(s[kb][r], c, -w.m);
+        x[1] = fmaf(s[kb][r + 1], c, -w.m);
+    } else if (stage == 1) {
+        x[0] = __builtin_amdgcn_exp2f(x[0]);
+        x[1] = __builtin_amdgcn_exp2f(x[1]);
     } else {
-        new_k_unit(0, p, d);
-        new_k_unit(1, p, d);
-#pragma unroll
-        for (int dq = 0; dq < 4; ++dq) new_v_unit(dq, p, d);
+        const nm_bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        pk[q] = pack_bf16(x[0], x[1]);
+        w.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(nm_bf16x2, pk[q]), ones, w.lsum, false);
     }
 }
 
-// ---------------------------------------------------------------------------
-// The pipelined step j.  The S^T products of tile j+1 (K from LDS) run
-// interleaved with the row max and probabilities of tile j; then the O^T
-// products of tile j run interleaved with the conversion of tile j+2 (HBM
-// data already in registers) into the third LDS buffer.  Every slot holds
-// one matrix instruction, the LDS read of the operand two slots ahead and a
-// short run of independent vector work, so each wave keeps issuing while its
-// matrix instructions execute.
-
-template <int KIND>
-__device__ __forceinline__ void pipelined_step(const uint16_t* Kn, const uint16_t* V, uint16_t* K2, uint16_t* V2,
-                                               bool cache2, int lim, int tid, int krd, int vrd, const Prefetch& pf,
+__device__ __forceinline__ void pipelined_step(const uint16_t* Kn, const uint16_t* V, int lim, int krd, int vrd,
                                                WaveState& w, f32x16 (&s)[2], f32x16 (&sn)[2], float c, int g) {
-    if (KIND != KIND_ANY) cache2 = KIND == KIND_CACHE;
     if (lim < BN) mask_tile(s, lim, g);
+    const f32x16 zero = {};
     uint32_t pk[16];
-    {
-        const f32x16 zero = {};
-        bf16x8 kf[16];
+    float t[4][2];
+    bf16x8 fr[32];
+    auto frag = [&](int i) { return i < 16 ? kfrag(Kn, krd, i) : vfrag(V, vrd, i - 16); };
 #pragma unroll
-        for (int i = 0; i < FD; ++i) kf[i] = kfrag(Kn, krd, i);
-        SLOT_FENCE();
-        float mx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i + FD < 16) kf[i + FD] = kfrag(Kn, krd, i + FD);
-            sn[i & 1] = mfma(kf[i], w.qf[i >> 1], i < 2 ? zero : sn[i & 1]);
-            if (i == 0) mx = max_part(s, 0, 8, fmaxf(s[0][0], s[1][0]));
-            else if (i == 1) mx = max_part(s, 8, 16, mx);
-            else if (i == 2) update_max(mx, w, c);
-            else prob_pair(s, i - 3, w, c, pk);
-            SLOT_FENCE();
-        }
-    }
-    // O^T products of tile j with the conversion of tile j+2; the tile kind
-    // is a scalar branch inside each slot, so the accumulators never pass
-    // through a join
-    const StoreDst d = store_dst(K2, V2, tid);
-    bf16x8 vf[16];
-#pragma unroll
-    for (int i = 0; i < FD; ++i) vf[i] = vfrag(V, vrd, i);
+    for (int i = 0; i < FD; ++i) fr[i] = frag(i);
     SLOT_FENCE();
-    uint32_t o[4];
+    float mx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        if (i + FD < 16) vf[i + FD] = vfrag(V, vrd, i + FD);
-        w.o[i & 3] = mfma(vf[i], pchunk(pk, i >> 2), w.o[i & 3]);
-        if (i < 3) {
-            prob_pair(s, 13 + i, w, c, pk);
-        } else if (i < 7) {
-            if (cache2) cache_k_unit(i - 3, pf, o, d);
-            else new_v_unit(i - 3, pf, d);
-        } else if (i < 11) {
-            if (cache2) cache_v_unit(i - 7, pf, d);
-            else if (i < 9) new_k_unit(i - 7, pf, d);
-        }
+    for (int i = 0; i < 32; ++i) {
+        if (i + FD < 32) fr[i + FD] = frag(i + FD);
+        if (i < 16) sn[i & 1] = mfma(fr[i], w.qf[i >> 1], i < 2 ? zero : sn[i & 1]);
+        else w.o[i & 3] = mfma(fr[i], pchunk(pk, (i - 16) >> 2), w.o[i & 3]);
+        // row max and rescale of tile j
+        if (i == 0) mx = max16(s, 0);
+        else if (i == 1) mx = fmaxf(mx, max16(s, 8));
+        else if (i == 2) update_max(mx, w, c);
+        // probabilities: pair q in slots 3+q, 4+q, 5+q
+#pragma unroll
+        for (int st = 0; st < 3; ++st)
+            if (i - 3 - st >= 0 && i - 3 - st < 16) prob_stage(st, i - 3 - st, s, w, c, t, pk);
         SLOT_FENCE();
     }
 }
 
 __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[3][BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[3][D * VSTR];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -406,89 +357,66 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     ws.m = -INFINITY;
     ws.lsum = 0.0f;
 
-    const int nc = __builtin_amdgcn_readfirstlane((A.Lc + BN - 1) / BN);   // cache tiles
-    const int nt = __builtin_amdgcn_readfirstlane(nc + (kend + BN - 1) / BN);
-
-    Bufs B;
-    {
-        const size_t hb = (size_t)head * A.cap;
-        B.kc = make_rsrc(A.kc + hb * D, (uint32_t)A.Lc * D);
-        B.vc = make_rsrc(A.vc + hb * D, (uint32_t)A.Lc * D);
-        B.ks = make_rsrc(A.ks + hb, (uint32_t)A.Lc * 4);
-        B.vs = make_rsrc(A.vs + hb, (uint32_t)A.Lc * 4);
-        // new tokens [0, kend) of this head: rows of H*128 bf16, this head's 128 at the front
-        const uint32_t bytes = (uint32_t)(kend - 1) * (uint32_t)A.H * D * 2 + D * 2;
-        B.k = make_rsrc(A.k + head * D, bytes);
-        B.v = make_rsrc(A.v + head * D, bytes);
-    }
-    const uint32_t rs = (uint32_t)A.H * D * 2;      // bytes per new-token row
+    // keys [0, nkeys) of the packed range are allowed: the cache and the new
+    // tokens up to the end of this segment
+    const int nkeys = __builtin_amdgcn_readfirstlane(A.Lc + kend);
+    const int nt = __builtin_amdgcn_readfirstlane((nkeys + BN - 1) / BN);
     const int krd = l32 * KSTR + 8 * g;             // this lane's K / V^T fragment offsets
     const int vrd = l32 * VSTR + 8 * g;
 
-    // Three LDS buffers: step j reads K of tile j+1 and V of tile j and
-    // writes tile j+2.  Two prefetch register sets alternate between steps:
-    // the set converted in step j was loaded in step j-2, two steps ahead of
-    // its use.  Loads are unconditional (tile indices clamped to the last
-    // tile, a harmless reload) and straight-line.
-    auto tile = [&](int j) { return tile_at(min(j, nt - 1), A.Lc, nc, kend); };
-    Prefetch pa, pb;
-    load_tile<KIND_ANY>(B, tile(0), rs, tid, pa);
-    load_tile<KIND_ANY>(B, tile(1), rs, tid, pb);
-    store_tile(tile(0), tid, pa, Ks[0], Vt[0]);
-    load_tile<KIND_ANY>(B, tile(2), rs, tid, pa);
-    store_tile(tile(1), tid, pb, Ks[1], Vt[1]);
-    load_tile<KIND_ANY>(B, tile(3), rs, tid, pb);
+    // ---- tile copies: wave w copies kilobytes w, w+8, ... of each image
+    const int wv = __builtin_amdgcn_readfirstlane(wave) & (NW - 1);
+    const uint64_t hbase = (uint64_t)(uintptr_t)A.img + (uint64_t)head * A.ntk * TILE_BYTES;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+    const uint32_t lane16 = 16u * lane;
+    auto copy_tile = [&](int tile, int b) {
+        const uint64_t base = hbase + (uint64_t)min(tile, nt - 1) * TILE_BYTES;
+        const u32x4 rs = {(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, (uint32_t)TILE_BYTES, 0x00020000u};
+#pragma unroll
+        for (int k = 0; k < (TILE_KB + NW - 1) / NW; ++k) {
+            const int kb = wv + NW * k;
+            if (kb < TILE_KB) dma_1k(lds0 + b * TILE_BYTES + 1024 * kb, lane16, rs, 1024u * kb);
+        }
+    };
+    // wait for this wave's copies of the tile before the last one issued
+    auto wait_prev_tile = [&] {
+        if (wv < TILE_KB % NW) wait_dma<(TILE_KB + NW - 1) / NW>();
+        else wait_dma<TILE_KB / NW>();
+    };
+    auto kbuf = [&](int b) { return reinterpret_cast<const uint16_t*>(lds + b * TILE_BYTES); };
+    auto vbuf = [&](int b) { return reinterpret_cast<const uint16_t*>(lds + b * TILE_BYTES + KIMG); };
+
+    // Tile t lives in buffer t % 4.  Step j copies tile j+3 into the buffer
+    // that tile j-1 left, works on tiles j and j+1, and ends once its copies
+    // of tile j+2 have landed and every wave has reached the barrier.
+    copy_tile(0, 0);
+    copy_tile(1, 1);
+    copy_tile(2, 2);
+    wait_dma<0>();      // tiles 0 and 1 (and 2) of this wave
     lds_barrier();
 
     f32x16 sa[2], sb[2];
     {
         const f32x16 zero = {};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sa[i & 1] = mfma(kfrag(Ks[0], krd, i), ws.qf[i >> 1], i < 2 ? zero : sa[i & 1]);
+        for (int i = 0; i < 16; ++i) sa[i & 1] = mfma(kfrag(kbuf(0), krd, i), ws.qf[i >> 1], i < 2 ? zero : sa[i & 1]);
     }
-    // Step j: scores of tile j in x, next tile's scores into y; LDS buffer b0
-    // holds tile j; pf holds tile j+2 and is refilled with tile j+4.  Steps
-    // past the last tile see a fully masked tile and change nothing.  Steps
-    // go in pairs, so the score and prefetch sets swap roles without copies.
-    auto step = [&](auto kind, int j, int b0, f32x16 (&x)[2], f32x16 (&y)[2], Prefetch& pf) {
-        constexpr int K = decltype(kind)::value;
-        const int b1 = b0 == 2 ? 0 : b0 + 1;
-        const int b2 = b1 == 2 ? 0 : b1 + 1;
-        const int lim = j < nt ? tile(j).lim : 0;
-        pipelined_step<K>(Ks[b1], Vt[b0], Ks[b2], Vt[b2], tile(j + 2).cache, lim, tid, krd, vrd, pf, ws, x, y, c, g);
-        load_tile<K>(B, tile(j + 4), rs, tid, pf);
+    // Step j: scores of tile j in x, next tile's scores into y.  Steps past
+    // the last tile see a fully masked tile and change nothing; steps go in
+    // pairs so the two score sets swap roles without copies.
+    auto step = [&](int j, f32x16 (&x)[2], f32x16 (&y)[2]) {
+        const int b0 = j & 3, b1 = (j + 1) & 3;
+        copy_tile(j + 3, (j + 3) & 3);
+        const int lim = j < nt ? min(BN, nkeys - j * BN) : 0;
+        pipelined_step(kbuf(b1), vbuf(b0), lim, krd, vrd, ws, x, y, c, g);
+        wait_prev_tile();
         lds_barrier();
-        return b1;
     };
-    const std::integral_constant<int, KIND_CACHE> cache_kind;
-    const std::integral_constant<int, KIND_NEW> new_kind;
-    const std::integral_constant<int, KIND_ANY> any_kind;
-    // all outstanding loads complete before a specialised stretch, so its
-    // waits are counted from its own loads only
-    const auto drain = [] { __builtin_amdgcn_s_waitcnt(0x0f70); };   // vmcnt(0)
-    int j = 0, b = 0;
-    if (j + 5 < nc) {
-        drain();
-        for (; j + 5 < nc; j += 2) {          // tiles j .. j+5 all from the cache
-            b = step(cache_kind, j, b, sa, sb, pa);
-            b = step(cache_kind, j + 1, b, sb, sa, pb);
-        }
+    for (int j = 0; j < nt; j += 2) {
+        step(j, sa, sb);
+        step(j + 1, sb, sa);
     }
-    for (; j < nt && !(j + 2 >= nc && j + 5 < nt); j += 2) {
-        b = step(any_kind, j, b, sa, sb, pa);
-        b = step(any_kind, j + 1, b, sb, sa, pb);
-    }
-    if (j + 5 < nt) {
-        drain();
-        for (; j + 5 < nt; j += 2) {          // tiles j+2 .. j+5 all new keys
-            b = step(new_kind, j, b, sa, sb, pa);
-            b = step(new_kind, j + 1, b, sb, sa, pb);
-        }
-    }
-    for (; j < nt; j += 2) {
-        b = step(any_kind, j, b, sa, sb, pa);
-        b = step(any_kind, j + 1, b, sb, sa, pb);
-    }
+    wait_dma<0>();
 
     // ---- epilogue: O / l -> bf16; lse = (m + log2 l) ln 2
     const float lt = half_sum(ws.lsum);
@@ -507,15 +435,26 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     }
 }
 
+int seg_attn_workspace_tiles(int Lc, int Ln) { return (Lc + Ln + BN - 1) / BN; }
+int64_t seg_attn_workspace_bytes(int Lc, int Ln, int H) {
+    return (int64_t)H * seg_attn_workspace_tiles(Lc, Ln) * TILE_BYTES;
+}
+
 int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const SegTable& segs,
                     int Ln, const int8_t* kc, const int8_t* vc, const float* ks, const float* vs,
                     int64_t cap, int Lc, int H, float sm_scale, uint16_t* out, float* lse,
-                    const RopeTables& rt, hipStream_t stream) {
+                    void* workspace, const RopeTables& rt, hipStream_t stream) {
+    const int ntk = seg_attn_workspace_tiles(Lc, Ln);
+    PackArgs P{};
+    P.kc = kc; P.vc = vc; P.ks = ks; P.vs = vs;
+    P.k = k; P.v = v;
+    P.img = static_cast<uint8_t*>(workspace);
+    P.cap = cap; P.Lc = Lc; P.Ln = Ln; P.H = H; P.ntk = ntk;
+
     AttnArgs A{};
-    A.q = q; A.k = k; A.v = v;
-    A.kc = kc; A.vc = vc; A.ks = ks; A.vs = vs;
+    A.q = q; A.img = P.img;
     A.out = out; A.lse = lse;
-    A.cap = cap; A.Lc = Lc; A.Ln = Ln; A.H = H;
+    A.Lc = Lc; A.Ln = Ln; A.H = H; A.ntk = ntk;
     A.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
     int nt = 0;
     for (int i = 0; i < segs.n; ++i) {
@@ -529,6 +468,7 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.segs = segs;
     A.rt = rt;
     if (nt == 0) return NOMAS_OK;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)ntk, (unsigned)H), dim3(PACK_NT), 0, stream, P);
     const int64_t blocks = (int64_t)nt * H;
     hipLaunchKernelGGL(seg_attn_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, A);
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;

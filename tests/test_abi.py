@@ -47,14 +47,16 @@ def test_seg_attn_host_checks():
     L = nomas.lib()
     sa, n = segs((16, 0, 2, 4, 6))
     P = ctypes.c_void_p
+    need = L.nomas_seg_attn_workspace(sa, n, 0, 2)
+    assert need == 2 * 35840                           # 16 + 2*4*6 = 64 new keys: one tile per head
     good = dict(q=FAKE, k=FAKE, v=FAKE, segs=sa, n=n, kc=None, vc=None, ks=None, vs=None, cap=0, clen=0,
-                H=2, sm=0.088, out=FAKE, lse=None)
+                H=2, sm=0.088, out=FAKE, lse=None, ws=FAKE, wsb=need)
 
     def call(**kw):
         a = dict(good, **kw)
         return L.nomas_seg_attn(P(a["q"]), P(a["k"]), P(a["v"]), a["segs"], a["n"], P(a["kc"]), P(a["vc"]),
                                 P(a["ks"]), P(a["vs"]), a["cap"], a["clen"], a["H"], a["sm"], P(a["out"]),
-                                P(a["lse"]), None)
+                                P(a["lse"]), P(a["ws"]), a["wsb"], None)
 
     assert call(q=None) == nomas.EINVAL
     assert call(out=None) == nomas.EINVAL
@@ -75,6 +77,13 @@ def test_seg_attn_host_checks():
     assert call(segs=many, n=nm) == nomas.EUNSUPPORTED
     empty, ne = segs((0, 0, 0, 0, 0))                 # no tokens: nothing to do
     assert call(segs=empty, n=ne) == nomas.OK
+    assert call(ws=None) == nomas.EINVAL               # workspace missing, too small or misaligned
+    assert call(wsb=need - 1) == nomas.EINVAL
+    assert call(ws=FAKE + 8) == nomas.EINVAL
+    # workspace size: H * ceil((cache + new tokens) / 64) tiles of 35840 bytes
+    assert L.nomas_seg_attn_workspace(sa, n, 1000, 3) == 3 * ((1000 + 64 + 63) // 64) * 35840
+    assert L.nomas_seg_attn_workspace(sa, n, -1, 3) == nomas.EINVAL
+    assert L.nomas_seg_attn_workspace(sa, n, 0, 0) == nomas.EINVAL
 
 
 def test_kv_quant_append_host_checks():
