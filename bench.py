@@ -13,7 +13,8 @@ HBM before timing starts.
 
 value = algorithmic attention FLOPs per step / wall time per step (TFLOP/s),
 with algorithmic FLOPs = 4 * 128 * H * (allowed query-key pairs).
-The roofline block times nomas_seg_attn alone with HIP events on its stream.
+The roofline block times nomas_seg_attn alone (its two launches: the pack
+pre-pass and the attention kernel) with HIP events on its stream.
 The CPU baseline times the oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -47,8 +48,9 @@ def kernel_digest() -> str:
 
 
 def traffic_for_current_kernel():
-    """HBM bytes per seg_attn launch from the committed counter summary, or
-    None when the kernel source changed since the counters were taken."""
+    """HBM bytes per nomas_seg_attn call (pack + attention kernels) from the
+    committed counter summary, or None when the kernel source changed since
+    the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -169,7 +171,7 @@ def main():
     attn_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    log("step %.3f ms, seg_attn %.3f ms (%.1f TFLOP/s, %.1f%% of peak)"
+    log("step %.3f ms, nomas_seg_attn %.3f ms (%.1f TFLOP/s, %.1f%% of peak)"
         % (ms_step, attn_ms, achieved, 100 * achieved / PEAK_BF16_TFLOPS))
 
     cpu = None
@@ -199,7 +201,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "seg_attn_kernel",
+            "kernel": "nomas_seg_attn (pack_kernel + seg_attn_kernel)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -213,14 +215,14 @@ def main():
 
 
 def cpu_baseline(inp, cfg, sm):
-    """The oracle (numpy float64) on a bounded sample: head 0, the first 2048
+    """The oracle (numpy float64) on a bounded sample: head 0, the first 8192
     of the 63,360 query rows, all 316,800 allowed keys."""
     import numpy as np
 
     import oracle
 
     H, Lq, Lc = cfg.H, cfg.Lq, cfg.Lc
-    rows = np.arange(2048)
+    rows = np.arange(8192)
     kc, vc, ks, vs = oracle.build_cache(inp["k_hist"][:, :1], inp["v_hist"][:, :1], cfg.hist_segs)
     q1 = np.ascontiguousarray(inp["q"][:, :1])
     k1 = np.ascontiguousarray(inp["k_new"][:, :1])
@@ -243,7 +245,7 @@ def cpu_baseline(inp, cfg, sm):
         "cores": int(cores),
         "kind": "oracle",
         "seconds": round(dt, 2),
-        "sample": "numpy float64 oracle, head 0 of 16, query rows 0..2047 of 63,360, each over all 316,800 "
+        "sample": "numpy float64 oracle, head 0 of 16, query rows 0..8191 of 63,360, each over all 316,800 "
                   "allowed keys (%.2e algorithmic FLOP), timed including its per-head key dequantisation "
                   "and rotation" % flops,
     }
