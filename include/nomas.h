@@ -76,6 +76,7 @@ enum {
 #define NOMAS_MAX_CAM 128          /* camera tokens per call                   */
 #define NOMAS_MAX_CACHE (1 << 24)  /* nomas_seg_attn: cache capacity (tokens)  */
 #define NOMAS_MAX_TOKEN_HEADS (1 << 23)  /* nomas_seg_attn: new tokens x heads */
+#define NOMAS_MAX_SPLIT 4          /* nomas_seg_attn: key-range parts per query tile */
 
 /*
  * 3D RoPE (comfyui-wiki news, 模型内部: axes [16, 56, 56], theta 256).
@@ -125,11 +126,16 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
  *   then the cache pointers may be NULL).
  * sm_scale > 0 (1/sqrt(128) for the model).
  * out: device, [Ln][H][128] bf16.  lse: device [H][Ln] float32 or NULL.
+ * n_split: 0 lets the library split each query tile's keys into 1..4
+ *   contiguous parts so that the grid fills the GPU's last round of
+ *   workgroups (partial results are merged by the log-sum-exp identity);
+ *   1..NOMAS_MAX_SPLIT forces that many parts.  Results agree to rounding.
  * workspace: device scratch of at least nomas_seg_attn_workspace(...)
- *   bytes, 16-byte aligned, owned by the caller; the call overwrites it
- *   (the keys laid out as 64-key tiles, about 140 bytes per cached or new
- *   token and head), so two calls in flight must not share one.  Too small
- *   or NULL: NOMAS_EINVAL.
+ *   bytes (same segments, cache_len, H and n_split, on the current device),
+ *   16-byte aligned, owned by the caller; the call overwrites it (the keys
+ *   laid out as 64-key tiles, about 140 bytes per cached or new token and
+ *   head, plus fp32 partial results when the keys are split), so two calls
+ *   in flight must not share one.  Too small or NULL: NOMAS_EINVAL.
  * n_new_segs in [1, NOMAS_MAX_SEGS]; cap <= NOMAS_MAX_CACHE and
  * Ln * H <= NOMAS_MAX_TOKEN_HEADS, else NOMAS_EUNSUPPORTED.
  */
@@ -138,16 +144,18 @@ int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_rot, const nomas_bf1
                    const int8_t* k_codes, const int8_t* v_codes,
                    const float* k_scale, const float* v_scale,
                    int64_t cap, int64_t cache_len, int H, float sm_scale,
-                   nomas_bf16* out, float* lse, void* workspace, int64_t workspace_bytes,
+                   nomas_bf16* out, float* lse, int n_split, void* workspace, int64_t workspace_bytes,
                    void* stream);
 
 /*
- * Workspace bytes nomas_seg_attn needs for these new segments, cache length
- * and head count (H * ceil((cache_len + Ln) / 64) * 35840), or a negative
- * error code (NOMAS_EINVAL / NOMAS_EUNSUPPORTED as for nomas_seg_attn).
- * Host only.
+ * Workspace bytes nomas_seg_attn needs for these new segments, cache length,
+ * head count and n_split on the current device: H * ceil((cache_len + Ln) /
+ * 64) * 35840, plus parts * Ln * H * 516 when the keys are split into parts
+ * > 1; or a negative error code (NOMAS_EINVAL / NOMAS_EUNSUPPORTED as for
+ * nomas_seg_attn).  Host only.
  */
-int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len, int H);
+int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len, int H,
+                                 int n_split);
 
 /*
  * Camera tokens of one turn (comfyui-wiki news, 相机控制作为一等输入).

@@ -20,6 +20,7 @@ OK, EINVAL, ECAPACITY, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4
 HEAD_DIM = 128
 MAX_SEGS = 64
 MAX_CAM = 128
+MAX_SPLIT = 4
 SM_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
 SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_workspace",
@@ -55,8 +56,8 @@ def lib() -> ctypes.CDLL:
         L.nomas_rope3d.argtypes = [_P, _P, ctypes.POINTER(Seg), _I, _I, _P]
         L.nomas_kv_quant_append.argtypes = [_P, _P, _I64, _I, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64), _P]
         L.nomas_seg_attn.argtypes = [_P, _P, _P, ctypes.POINTER(Seg), _I, _P, _P, _P, _P, _I64, _I64, _I, _F,
-                                     _P, _P, _P, _I64, _P]
-        L.nomas_seg_attn_workspace.argtypes = [ctypes.POINTER(Seg), _I, _I64, _I]
+                                     _P, _P, _I, _P, _I64, _P]
+        L.nomas_seg_attn_workspace.argtypes = [ctypes.POINTER(Seg), _I, _I64, _I, _I]
         L.nomas_seg_attn_workspace.restype = _I64
         L.nomas_cam_tokens.argtypes = [_P, _I, _D, _D, _P]
         L.nomas_cam_xattn.argtypes = [_P, _I64, _I, _P, _I, _P, _P, _F, _P, _P]
@@ -162,21 +163,23 @@ def kv_quant_append(k_rot, v, k_codes, v_codes, k_scale, v_scale, length: int, s
     return int(ln.value)
 
 
-def seg_attn_workspace(new_segs, cache_len: int, H: int) -> int:
-    """Bytes of device workspace seg_attn needs (host only)."""
+def seg_attn_workspace(new_segs, cache_len: int, H: int, n_split: int = 0) -> int:
+    """Bytes of device workspace seg_attn needs on the current device (host only)."""
     arr, n = seg_array(new_segs)
-    nbytes = lib().nomas_seg_attn_workspace(arr, n, int(cache_len), int(H))
+    nbytes = lib().nomas_seg_attn_workspace(arr, n, int(cache_len), int(H), int(n_split))
     if nbytes < 0:
         raise NomasError(int(nbytes), "nomas_seg_attn_workspace")
     return int(nbytes)
 
 
 def seg_attn(q, k_rot, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None, v_scale=None,
-             cache_len: int = 0, sm_scale: float = SM_SCALE, out=None, lse=None, workspace=None, stream=None):
+             cache_len: int = 0, sm_scale: float = SM_SCALE, out=None, lse=None, workspace=None, n_split: int = 0,
+             stream=None):
     """Segment-causal attention; returns out [Ln][H][128] bf16 (lse filled if given).
     q is taken before RoPE, k_rot after it (as rope3d returns it).  workspace:
     a device uint8 tensor of at least seg_attn_workspace(...) bytes, allocated
-    here when not given."""
+    here when not given.  n_split: 0 = the library's choice of key-range parts,
+    1..4 forces that many."""
     import torch
     Ln, H = q.shape[0], q.shape[1]
     shp = (seg_tokens(new_segs), H, HEAD_DIM)
@@ -197,7 +200,7 @@ def seg_attn(q, k_rot, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
     _dev(out, "out", shp)
     if lse is not None:
         _dev(lse, "lse", (H, Ln), 4)
-    need = seg_attn_workspace(new_segs, cache_len, H)
+    need = seg_attn_workspace(new_segs, cache_len, H, n_split)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -205,7 +208,8 @@ def seg_attn(q, k_rot, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
     arr, n = seg_array(new_segs)
     _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_rot), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
                                 _ptr(k_scale), _ptr(v_scale), cap, int(cache_len), H, float(sm_scale),
-                                _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
+                                _ptr(out), _ptr(lse), int(n_split), _ptr(workspace), workspace.numel(),
+                                _stream(stream)),
            "nomas_seg_attn")
     return out
 

@@ -42,6 +42,8 @@
 // Softmax is online in base 2 (scale folded into one fma) with a lazy
 // rescale: O and the sum are rescaled only when a row's max grows by more
 // than 8 (a factor 256), which keeps every exponent bounded.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace nomas {
@@ -148,7 +150,10 @@ struct AttnArgs {
     const uint8_t* img;             // packed tile images
     uint16_t* out;
     float* lse;
+    float* po;                      // split > 1: partial outputs O/l [split][Ln][H][128] fp32
+    float* plse;                    //            partial log2-sum-exp [split][H][Ln]
     int32_t Lc, Ln, H, ntq, ntk;    // ntq: query tiles per head, ntk: key tiles per head
+    int32_t nsplit;                 // key-range parts per query tile
     float scale_log2;               // sm_scale * log2(e)
     int32_t tile0[NOMAS_MAX_SEGS + 1];   // first query tile of each new segment
     SegTable segs;
@@ -321,8 +326,12 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
-    const int head = __builtin_amdgcn_readfirstlane(blockIdx.x / A.ntq);
-    const int qt = __builtin_amdgcn_readfirstlane(blockIdx.x - head * A.ntq);
+    // block = (head * nsplit + split) * ntq + query tile: the workgroups that
+    // share a key range run side by side
+    const int hs = __builtin_amdgcn_readfirstlane(blockIdx.x / A.ntq);
+    const int qt = __builtin_amdgcn_readfirstlane(blockIdx.x - hs * A.ntq);
+    const int head = __builtin_amdgcn_readfirstlane(hs / A.nsplit);
+    const int split = __builtin_amdgcn_readfirstlane(hs - head * A.nsplit);
 
     int a = 0;
     while (a + 1 < A.segs.n && A.tile0[a + 1] <= qt) ++a;
@@ -360,7 +369,10 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     // keys [0, nkeys) of the packed range are allowed: the cache and the new
     // tokens up to the end of this segment
     const int nkeys = __builtin_amdgcn_readfirstlane(A.Lc + kend);
-    const int nt = __builtin_amdgcn_readfirstlane((nkeys + BN - 1) / BN);
+    const int nt_all = (nkeys + BN - 1) / BN;
+    // this workgroup's part of the key tiles: [t0, t0 + nt)
+    const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * nt_all / A.nsplit));
+    const int nt = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * nt_all / A.nsplit) - t0);
     const int krd = l32 * KSTR + 8 * g;             // this lane's K / V^T fragment offsets
     const int vrd = l32 * VSTR + 8 * g;
 
@@ -370,7 +382,7 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     const uint32_t lane16 = 16u * lane;
     auto copy_tile = [&](int tile, int b) {
-        const uint64_t base = hbase + (uint64_t)min(tile, nt - 1) * TILE_BYTES;
+        const uint64_t base = hbase + (uint64_t)(t0 + min(tile, nt - 1)) * TILE_BYTES;
         const u32x4 rs = {(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, (uint32_t)TILE_BYTES, 0x00020000u};
 #pragma unroll
         for (int k = 0; k < (TILE_KB + NW - 1) / NW; ++k) {
@@ -389,6 +401,7 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     // Tile t lives in buffer t % 4.  Step j copies tile j+3 into the buffer
     // that tile j-1 left, works on tiles j and j+1, and ends once its copies
     // of tile j+2 have landed and every wave has reached the barrier.
+    if (nt > 0) {       // a key-range part can be empty when there are fewer tiles than parts
     copy_tile(0, 0);
     copy_tile(1, 1);
     copy_tile(2, 2);
@@ -407,7 +420,7 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     auto step = [&](int j, f32x16 (&x)[2], f32x16 (&y)[2]) {
         const int b0 = j & 3, b1 = (j + 1) & 3;
         copy_tile(j + 3, (j + 3) & 3);
-        const int lim = j < nt ? min(BN, nkeys - j * BN) : 0;
+        const int lim = j < nt ? min(BN, nkeys - (t0 + j) * BN) : 0;
         pipelined_step(kbuf(b1), vbuf(b0), lim, krd, vrd, ws, x, y, c, g);
         wait_prev_tile();
         lds_barrier();
@@ -417,12 +430,24 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
         step(j + 1, sb, sa);
     }
     wait_dma<0>();
+    }
 
     // ---- epilogue: O / l -> bf16; lse = (m + log2 l) ln 2
     const float lt = half_sum(ws.lsum);
-    const float inv = 1.0f / lt;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int row = r0 + wave * QW + l32;
-    if (row < r1) {
+    if (row < r1 && A.nsplit > 1) {
+        // partial result of this key range: O/l in fp32 and log2-sum-exp
+        float* dst = A.po + (((int64_t)split * A.Ln + row) * A.H + head) * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<float4*>(dst + 32 * db + 8 * i + 4 * g) =
+                    make_float4(ws.o[db][4 * i] * inv, ws.o[db][4 * i + 1] * inv, ws.o[db][4 * i + 2] * inv,
+                                ws.o[db][4 * i + 3] * inv);
+        if (g == 0) A.plse[((int64_t)split * A.H + head) * A.Ln + row] = lt > 0.0f ? ws.m + __log2f(lt) : -INFINITY;
+    } else if (row < r1) {
         uint16_t* dst = A.out + ((int64_t)row * A.H + head) * D;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -435,15 +460,94 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     }
 }
 
+// Merge of the key-range parts (log-sum-exp identity): for each (row, head)
+// lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) * (O/l)_s.
+// 32 threads per (row, head), 4 channels each.
+struct MergeArgs {
+    const float* po;
+    const float* plse;
+    uint16_t* out;
+    float* lse;
+    int32_t Ln, H, nsplit;
+};
+
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs M) {
+    const int64_t pair = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);   // row * H + head
+    if (pair >= (int64_t)M.Ln * M.H) return;
+    const int row = (int)(pair / M.H), head = (int)(pair - (int64_t)row * M.H);
+    const int ch = 4 * (threadIdx.x & 31);
+    float mx = -INFINITY;
+    for (int s = 0; s < M.nsplit; ++s) mx = fmaxf(mx, M.plse[((int64_t)s * M.H + head) * M.Ln + row]);
+    float wsum = 0.0f;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s = 0; s < M.nsplit; ++s) {
+        const float ls = M.plse[((int64_t)s * M.H + head) * M.Ln + row];
+        const float w = ls == -INFINITY ? 0.0f : exp2f(ls - mx);
+        const float4 o = *reinterpret_cast<const float4*>(M.po + ((int64_t)s * M.Ln + row) * M.H * D + head * D + ch);
+        wsum += w;
+        acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+    }
+    const float inv = 1.0f / wsum;
+    *reinterpret_cast<uint2*>(M.out + pair * D + ch) =
+        make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
+    if (M.lse && ch == 0) M.lse[(int64_t)head * M.Ln + row] = (mx + __log2f(wsum)) * 0.69314718055994531f;
+}
+
+// ---------------------------------------------------------------------------
+// Launch planning
+
 int seg_attn_workspace_tiles(int Lc, int Ln) { return (Lc + Ln + BN - 1) / BN; }
-int64_t seg_attn_workspace_bytes(int Lc, int Ln, int H) {
-    return (int64_t)H * seg_attn_workspace_tiles(Lc, Ln) * TILE_BYTES;
+
+int device_cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Key-range parts per query tile.  Forced when n_split > 0; otherwise the
+// count (1..4) that fills the last round of workgroups best, keeping every
+// part at 16 tiles or more: one workgroup per CU, so a grid of u units takes
+// ceil(u / CUs) rounds, each 1/parts as long.
+int plan_splits(const SegTable& segs, int Lc, int H, int n_split) {
+    if (n_split > 0) return n_split;
+    int nq = 0, nt_min = 1 << 30;
+    for (int i = 0; i < segs.n; ++i) {
+        const SegDev& s = segs.s[i];
+        const int ntok = s.n_text + s.T * s.Hg * s.Wg;
+        if (ntok == 0) continue;
+        nq += (ntok + BM - 1) / BM;
+        nt_min = std::min(nt_min, (Lc + s.start + ntok + BN - 1) / BN);
+    }
+    const int cus = device_cu_count();
+    if (nq == 0 || cus <= 0) return 1;
+    const int64_t units = (int64_t)nq * H;
+    int best = 1;
+    double best_cost = (double)((units + cus - 1) / cus);
+    for (int p = 2; p <= 4 && nt_min / p >= 16; ++p) {
+        const double cost = (double)((units * p + cus - 1) / cus) / p;
+        if (cost < best_cost - 1e-9) { best = p; best_cost = cost; }
+    }
+    return best;
+}
+
+int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int n_split) {
+    const int p = plan_splits(segs, Lc, H, n_split);
+    int64_t b = (int64_t)H * seg_attn_workspace_tiles(Lc, Ln) * TILE_BYTES;
+    if (p > 1) b += (int64_t)p * Ln * H * (D + 1) * 4;
+    return b;
 }
 
 int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const SegTable& segs,
                     int Ln, const int8_t* kc, const int8_t* vc, const float* ks, const float* vs,
-                    int64_t cap, int Lc, int H, float sm_scale, uint16_t* out, float* lse,
+                    int64_t cap, int Lc, int H, float sm_scale, uint16_t* out, float* lse, int n_split,
                     void* workspace, const RopeTables& rt, hipStream_t stream) {
+    const int nsplit = plan_splits(segs, Lc, H, n_split);
     const int ntk = seg_attn_workspace_tiles(Lc, Ln);
     PackArgs P{};
     P.kc = kc; P.vc = vc; P.ks = ks; P.vs = vs;
@@ -455,6 +559,11 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.q = q; A.img = P.img;
     A.out = out; A.lse = lse;
     A.Lc = Lc; A.Ln = Ln; A.H = H; A.ntk = ntk;
+    A.nsplit = nsplit;
+    if (nsplit > 1) {
+        A.po = reinterpret_cast<float*>(P.img + (int64_t)H * ntk * TILE_BYTES);
+        A.plse = A.po + (int64_t)nsplit * Ln * H * D;
+    }
     A.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
     int nt = 0;
     for (int i = 0; i < segs.n; ++i) {
@@ -469,8 +578,13 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.rt = rt;
     if (nt == 0) return NOMAS_OK;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)ntk, (unsigned)H), dim3(PACK_NT), 0, stream, P);
-    const int64_t blocks = (int64_t)nt * H;
+    const int64_t blocks = (int64_t)nt * H * nsplit;
     hipLaunchKernelGGL(seg_attn_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, A);
+    if (nsplit > 1) {
+        const MergeArgs M{A.po, A.plse, out, lse, Ln, H, nsplit};
+        const int64_t mb = ((int64_t)Ln * H + 7) / 8;
+        hipLaunchKernelGGL(merge_kernel, dim3((unsigned)mb), dim3(256), 0, stream, M);
+    }
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
 }
 

@@ -47,16 +47,16 @@ def test_seg_attn_host_checks():
     L = nomas.lib()
     sa, n = segs((16, 0, 2, 4, 6))
     P = ctypes.c_void_p
-    need = L.nomas_seg_attn_workspace(sa, n, 0, 2)
+    need = L.nomas_seg_attn_workspace(sa, n, 0, 2, 1)
     assert need == 2 * 35840                           # 16 + 2*4*6 = 64 new keys: one tile per head
     good = dict(q=FAKE, k=FAKE, v=FAKE, segs=sa, n=n, kc=None, vc=None, ks=None, vs=None, cap=0, clen=0,
-                H=2, sm=0.088, out=FAKE, lse=None, ws=FAKE, wsb=need)
+                H=2, sm=0.088, out=FAKE, lse=None, split=1, ws=FAKE, wsb=need)
 
     def call(**kw):
         a = dict(good, **kw)
         return L.nomas_seg_attn(P(a["q"]), P(a["k"]), P(a["v"]), a["segs"], a["n"], P(a["kc"]), P(a["vc"]),
                                 P(a["ks"]), P(a["vs"]), a["cap"], a["clen"], a["H"], a["sm"], P(a["out"]),
-                                P(a["lse"]), P(a["ws"]), a["wsb"], None)
+                                P(a["lse"]), a["split"], P(a["ws"]), a["wsb"], None)
 
     assert call(q=None) == nomas.EINVAL
     assert call(out=None) == nomas.EINVAL
@@ -81,9 +81,15 @@ def test_seg_attn_host_checks():
     assert call(wsb=need - 1) == nomas.EINVAL
     assert call(ws=FAKE + 8) == nomas.EINVAL
     # workspace size: H * ceil((cache + new tokens) / 64) tiles of 35840 bytes
-    assert L.nomas_seg_attn_workspace(sa, n, 1000, 3) == 3 * ((1000 + 64 + 63) // 64) * 35840
-    assert L.nomas_seg_attn_workspace(sa, n, -1, 3) == nomas.EINVAL
-    assert L.nomas_seg_attn_workspace(sa, n, 0, 0) == nomas.EINVAL
+    assert L.nomas_seg_attn_workspace(sa, n, 1000, 3, 1) == 3 * ((1000 + 64 + 63) // 64) * 35840
+    # split keys: fp32 partial outputs and log-sum-exps of every part on top
+    assert L.nomas_seg_attn_workspace(sa, n, 1000, 3, 2) == 3 * 17 * 35840 + 2 * 64 * 3 * 129 * 4
+    assert L.nomas_seg_attn_workspace(sa, n, -1, 3, 1) == nomas.EINVAL
+    assert L.nomas_seg_attn_workspace(sa, n, 0, 0, 1) == nomas.EINVAL
+    assert L.nomas_seg_attn_workspace(sa, n, 0, 2, -1) == nomas.EINVAL
+    assert L.nomas_seg_attn_workspace(sa, n, 0, 2, nomas.MAX_SPLIT + 1) == nomas.EUNSUPPORTED
+    assert call(split=-1) == nomas.EINVAL
+    assert call(split=nomas.MAX_SPLIT + 1) == nomas.EUNSUPPORTED
 
 
 def test_kv_quant_append_host_checks():

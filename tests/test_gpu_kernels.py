@@ -95,7 +95,7 @@ def test_kv_quant_append_bit_exact_and_offsets():
 # seg_attn
 
 
-def _run_gpu(q, k, v, segs, cache, Lc, H, with_lse=True):
+def _run_gpu(q, k, v, segs, cache, Lc, H, with_lse=True, n_split=0):
     Ln = q.shape[0]
     lse = torch.empty((H, Ln), dtype=torch.float32, device="cuda:0") if with_lse else None
     if Lc > 0:
@@ -104,14 +104,15 @@ def _run_gpu(q, k, v, segs, cache, Lc, H, with_lse=True):
         kc = vc = ks = vs = None
     # keys enter attention rotated, as the rope3d kernel returns them
     k_rot = nomas.rope3d(dev16(k), segs)
-    out = nomas.seg_attn(dev16(q), k_rot, dev16(v), segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse)
+    out = nomas.seg_attn(dev16(q), k_rot, dev16(v), segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse,
+                         n_split=n_split)
     torch.cuda.synchronize()
     return f64(out), (lse.cpu().numpy() if with_lse else None), out
 
 
-def _check_case(name, q, k, v, segs, cache, Lc, H):
-    say("seg_attn", name, "Ln", q.shape[0], "Lc", Lc, "H", H)
-    got, lse, _ = _run_gpu(q, k, v, segs, cache, Lc, H)
+def _check_case(name, q, k, v, segs, cache, Lc, H, n_split=0):
+    say("seg_attn", name, "Ln", q.shape[0], "Lc", Lc, "H", H, "n_split", n_split)
+    got, lse, _ = _run_gpu(q, k, v, segs, cache, Lc, H, n_split=n_split)
     kc, vc, ks, vs = cache if Lc > 0 else (np.zeros((H, 0, 128), np.int8),) * 2 + (np.zeros((H, 0), np.float32),) * 2
     ref, lref = oracle.seg_attn(q, k, v, segs, kc, vc, ks, vs, Lc, SM)
     assert_close(got, ref, name)
@@ -144,6 +145,40 @@ EDGE = [
     ("turn-shape-small", [(256, 18, 2, 22, 40)], 1760, 2),
     ("empty-segment-between", [(4, 0, 1, 2, 2), (0, 0, 0, 0, 0), (2, 1, 2, 3, 3)], 64, 2),
 ]
+
+
+def _edge_inputs(segs, Lc, H):
+    Ln = sum(s[0] + s[2] * s[3] * s[4] for s in segs)
+    q = synth.random_bf16(201, (Ln, H, 128))
+    k = synth.random_bf16(202, (Ln, H, 128))
+    v = synth.random_bf16(203, (Ln, H, 128))
+    cache = None
+    if Lc > 0:
+        hist = [(0, 0, 1, 1, Lc)]                 # a one-row "frame" of Lc history tokens
+        kh = synth.random_bf16(204, (Lc, H, 128))
+        vh = synth.random_bf16(205, (Lc, H, 128))
+        cache = oracle.build_cache(kh, vh, hist, cap=Lc + 11)
+    return q, k, v, cache
+
+
+SPLIT = [("one-token", 4), ("ragged-97-cache130", 2), ("ragged-97-cache130", 3), ("packed-5", 4),
+         ("turn-shape-small", 2), ("turn-shape-small", 4), ("empty-segment-between", 3)]
+
+
+@pytest.mark.parametrize("name,n_split", SPLIT, ids=["%s-split%d" % c for c in SPLIT])
+def test_seg_attn_split_keys(name, n_split):
+    """Keys split into parts (some empty when a tile range is short) and
+    merged by the log-sum-exp identity: same bar against the oracle, and
+    the unsplit result to rounding."""
+    (segs, Lc, H), = [(c[1], c[2], c[3]) for c in EDGE if c[0] == name]
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    _check_case(name, q, k, v, segs, cache, Lc, H, n_split=n_split)
+    one, lse1, _ = _run_gpu(q, k, v, segs, cache, Lc, H, n_split=1)
+    many, lsen, _ = _run_gpu(q, k, v, segs, cache, Lc, H, n_split=n_split)
+    # each part rounds its probabilities to bf16 against its own running max,
+    # so sums differ at the 2^-9 level, as against the oracle
+    np.testing.assert_allclose(many, one, rtol=0, atol=2.0 ** -7)
+    np.testing.assert_allclose(lsen, lse1, rtol=0, atol=2.0 ** -8)
 
 
 @pytest.mark.parametrize("name,segs,Lc,H", EDGE, ids=[c[0] for c in EDGE])
