@@ -235,19 +235,6 @@ __device__ __forceinline__ void update_max(float mx, WaveState& w, float c) {
     }
 }
 
-// Probability pair q (0..15) of the tile: keys of registers 2(q%8), +1 of
-// block q/8, exp2(s c - m) rounded to bf16 and packed; the row sum is taken
-// over the same bf16 values.  Words 4ch .. 4ch+3 form the B operand of key
-// chunk ch of the O^T product.
-__device__ __forceinline__ void prob_pair(const f32x16 (&s)[2], int q, WaveState& w, float c, uint32_t (&pk)[16]) {
-    const nm_bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const int kb = q >> 3, r = 2 * (q & 7);
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -w.m));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -w.m));
-    pk[q] = pack_bf16(p0, p1);
-    w.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(nm_bf16x2, pk[q]), ones, w.lsum, false);
-}
-
 __device__ __forceinline__ bf16x8 pchunk(const uint32_t (&pk)[16], int ch) {
     return __builtin_bit_cast(bf16x8, u32x4{pk[4 * ch], pk[4 * ch + 1], pk[4 * ch + 2], pk[4 * ch + 3]});
 }
@@ -256,7 +243,8 @@ __device__ __forceinline__ bf16x8 pchunk(const uint32_t (&pk)[16], int ch) {
 // The pipelined step j: 32 slots, each holding one matrix instruction, the
 // LDS read of the operand FD slots ahead and a few vector instructions.
 // Slots 0-15 issue the S^T products of tile j+1, slots 16-31 the O^T
-// products of tile j.  The row max of tile j runs in slots 0-2; each
+// products of tile j.  The row max of tile j+1 is taken after the last
+// product, where the waves wait for one another anyway; each
 // probability pair is formed over three slots (scale and shift, exp2, pack
 // and sum) so that no slot holds a chain of dependent vector instructions.
 
@@ -291,9 +279,15 @@ __device__ __forceinline__ void prob_stage(int stage, int q, const f32x16 (&s)[2
     }
 }
 
-__device__ __forceinline__ void pipelined_step(const uint16_t* Kn, const uint16_t* V, int lim, int krd, int vrd,
-                                               WaveState& w, f32x16 (&s)[2], f32x16 (&sn)[2], float c, int g) {
-    if (lim < BN) mask_tile(s, lim, g);
+// mx: row max of s (this lane half), taken at the end of the previous step;
+// returns the row max of sn, taken after the last product of this step.
+__device__ __forceinline__ float pipelined_step(const uint16_t* Kn, const uint16_t* V, int lim, int krd, int vrd,
+                                                WaveState& w, f32x16 (&s)[2], float mx, f32x16 (&sn)[2], float c,
+                                                int g) {
+    if (lim < BN) {
+        mask_tile(s, lim, g);
+        mx = fmaxf(max16(s, 0), max16(s, 8));
+    }
     const f32x16 zero = {};
     uint32_t pk[16];
     float t[4][2];
@@ -302,22 +296,20 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* Kn, const uint16_
 #pragma unroll
     for (int i = 0; i < FD; ++i) fr[i] = frag(i);
     SLOT_FENCE();
-    float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         if (i + FD < 32) fr[i + FD] = frag(i + FD);
         if (i < 16) sn[i & 1] = mfma(fr[i], w.qf[i >> 1], i < 2 ? zero : sn[i & 1]);
         else w.o[i & 3] = mfma(fr[i], pchunk(pk, (i - 16) >> 2), w.o[i & 3]);
-        // row max and rescale of tile j
-        if (i == 0) mx = max16(s, 0);
-        else if (i == 1) mx = fmaxf(mx, max16(s, 8));
-        else if (i == 2) update_max(mx, w, c);
+        // rescale of tile j
+        if (i == 2) update_max(mx, w, c);
         // probabilities: pair q in slots 3+q, 4+q, 5+q
 #pragma unroll
         for (int st = 0; st < 3; ++st)
             if (i - 3 - st >= 0 && i - 3 - st < 16) prob_stage(st, i - 3 - st, s, w, c, t, pk);
         SLOT_FENCE();
     }
+    return fmaxf(max16(sn, 0), max16(sn, 8));
 }
 
 __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
@@ -414,20 +406,22 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sa[i & 1] = mfma(kfrag(kbuf(0), krd, i), ws.qf[i >> 1], i < 2 ? zero : sa[i & 1]);
     }
+    float ma = fmaxf(max16(sa, 0), max16(sa, 8)), mb = 0.0f;    // row maxima of the two score sets
     // Step j: scores of tile j in x, next tile's scores into y.  Steps past
     // the last tile see a fully masked tile and change nothing; steps go in
     // pairs so the two score sets swap roles without copies.
-    auto step = [&](int j, f32x16 (&x)[2], f32x16 (&y)[2]) {
+    auto step = [&](int j, f32x16 (&x)[2], float mx, f32x16 (&y)[2]) {
         const int b0 = j & 3, b1 = (j + 1) & 3;
         copy_tile(j + 3, (j + 3) & 3);
         const int lim = j < nt ? min(BN, nkeys - (t0 + j) * BN) : 0;
-        pipelined_step(kbuf(b1), vbuf(b0), lim, krd, vrd, ws, x, y, c, g);
+        const float my = pipelined_step(kbuf(b1), vbuf(b0), lim, krd, vrd, ws, x, mx, y, c, g);
         wait_prev_tile();
         lds_barrier();
+        return my;
     };
     for (int j = 0; j < nt; j += 2) {
-        step(j, sa, sb);
-        step(j + 1, sb, sa);
+        mb = step(j, sa, ma, sb);
+        ma = step(j + 1, sb, mb, sa);
     }
     wait_dma<0>();
     }
