@@ -3,9 +3,9 @@
 One step = one turn of the whole hot path at the full-lifelong-cache shape
 (a 12 s segment: 72 latent frames x 880 = 63,360 new tokens, 16 heads x 128,
 over 288 cached latent frames = 253,440 INT8 tokens):
-    nomas_rope3d     (the segment's keys, rotated once for attention and cache)
-    nomas_seg_attn   (63,360 queries x 316,800 keys, query RoPE fused, INT8 cache)
+    nomas_seg_attn   (63,360 queries x 316,800 keys, RoPE fused, INT8 cache)
     nomas_cam_xattn  (63,360 video queries x 72 camera tokens)
+    nomas_rope3d     (the segment's keys, before caching)
     nomas_kv_quant_append (the segment's K/V into the cache at 253,440)
 The append writes the same cache slots every step, so every step sees the
 same 253,440-token history.  Inputs are seeded synthetic tensors resident in
@@ -145,15 +145,14 @@ def main():
           for _ in range(args.steps)]
 
     def step(i=None):
-        # rotate the new keys once: attention and the cache append both use them
-        nomas.rope3d(k_new, [seg], out=k_rot, stream=stream)
         if i is not None:
             ev[i][0].record(stream)
-        nomas.seg_attn(q, k_rot, v_new, [seg], kc, vc, ks, vs, cache_len=Lc, sm_scale=sm, out=out, workspace=ws,
+        nomas.seg_attn(q, k_new, v_new, [seg], kc, vc, ks, vs, cache_len=Lc, sm_scale=sm, out=out, workspace=ws,
                        stream=stream)
         if i is not None:
             ev[i][1].record(stream)
         nomas.cam_xattn(q_cam, cam, w_k, w_v, sm_scale=sm, out=out_cam, stream=stream)
+        nomas.rope3d(k_new, [seg], out=k_rot, stream=stream)
         nomas.kv_quant_append(k_rot, v_new, kc, vc, ks, vs, Lc, stream=stream)
 
     for _ in range(args.warmup):
@@ -195,7 +194,7 @@ def main():
         "config": {
             "workload": "fullcache: 12 s segment (72 latent frames x 880 = 63,360 queries) over 288 cached "
                         "latent frames (253,440 INT8 keys) + own segment = 316,800 keys, 16 heads x 128; "
-                        "step = rope3d + seg_attn + cam_xattn (72 camera tokens) + kv_quant_append",
+                        "step = seg_attn + cam_xattn (72 camera tokens) + rope3d + kv_quant_append",
             "heads": H, "head_dim": 128, "queries": Lq, "cache_tokens": Lc, "keys_per_query": Lc + Lq,
             "algorithmic_flop_per_step": flops,
         },

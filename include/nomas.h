@@ -115,12 +115,11 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
  * segments pack a training sequence (block-causal).
  *   s_ij = sm_scale * <RoPE(q_i), K_j>,  o_i = softmax_j(s_ij) . V_j
  * over the allowed j; lse_i = ln sum_j exp(s_ij).
- * BF16 compute: RoPE(q) is rounded to bf16; cached entries enter as
- * bf16(fl32(code * scale)); products accumulate in fp32.
- * q, k_rot, v_new: device, [Ln][H][128] bf16, Ln = sum of the new segments'
- *   token counts.  q BEFORE RoPE (rotated on load, float32, rounded to
- *   bf16); k_rot AFTER RoPE: the keys as nomas_rope3d returns them for the
- *   same segments, i.e. the rows that nomas_kv_quant_append then stores.
+ * BF16 compute: RoPE(q), RoPE(k_new) are rounded to bf16; cached entries
+ * enter as bf16(fl32(code * scale)); products accumulate in fp32.
+ * q, k_new, v_new: device, [Ln][H][128] bf16, q and k_new BEFORE RoPE
+ *   (rotated inside: q in float32, k_new in float64 exactly as
+ *   nomas_rope3d), Ln = sum of the new segments' token counts.
  * k_codes, v_codes, k_scale, v_scale: device cache as for
  *   nomas_kv_quant_append; its first cache_len entries are used (may be 0,
  *   then the cache pointers may be NULL).
@@ -139,7 +138,7 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
  * n_new_segs in [1, NOMAS_MAX_SEGS]; cap <= NOMAS_MAX_CACHE and
  * Ln * H <= NOMAS_MAX_TOKEN_HEADS, else NOMAS_EUNSUPPORTED.
  */
-int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_rot, const nomas_bf16* v_new,
+int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,
                    const nomas_seg* new_segs, int n_new_segs,
                    const int8_t* k_codes, const int8_t* v_codes,
                    const float* k_scale, const float* v_scale,

@@ -172,11 +172,11 @@ def seg_attn_workspace(new_segs, cache_len: int, H: int, n_split: int = 0) -> in
     return int(nbytes)
 
 
-def seg_attn(q, k_rot, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None, v_scale=None,
+def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None, v_scale=None,
              cache_len: int = 0, sm_scale: float = SM_SCALE, out=None, lse=None, workspace=None, n_split: int = 0,
              stream=None):
     """Segment-causal attention; returns out [Ln][H][128] bf16 (lse filled if given).
-    q is taken before RoPE, k_rot after it (as rope3d returns it).  workspace:
+    q and k_new are taken before RoPE (rotated inside).  workspace:
     a device uint8 tensor of at least seg_attn_workspace(...) bytes, allocated
     here when not given.  n_split: 0 = the library's choice of key-range parts,
     1..4 forces that many."""
@@ -184,7 +184,7 @@ def seg_attn(q, k_rot, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
     Ln, H = q.shape[0], q.shape[1]
     shp = (seg_tokens(new_segs), H, HEAD_DIM)
     _dev(q, "q", shp)
-    _dev(k_rot, "k_rot", shp)
+    _dev(k_new, "k_new", shp)
     _dev(v_new, "v_new", shp)
     cap = 0
     if cache_len > 0:
@@ -206,7 +206,7 @@ def seg_attn(q, k_rot, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
     if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device uint8 tensor")
     arr, n = seg_array(new_segs)
-    _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_rot), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
+    _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_new), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
                                 _ptr(k_scale), _ptr(v_scale), cap, int(cache_len), H, float(sm_scale),
                                 _ptr(out), _ptr(lse), int(n_split), _ptr(workspace), workspace.numel(),
                                 _stream(stream)),

@@ -177,14 +177,14 @@ int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int6
     return seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, n_split);
 }
 
-int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_rot, const nomas_bf16* v_new,
+int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,
                    const nomas_seg* new_segs, int n_new_segs, const int8_t* k_codes, const int8_t* v_codes,
                    const float* k_scale, const float* v_scale, int64_t cap, int64_t cache_len, int H,
                    float sm_scale, nomas_bf16* out, float* lse, int n_split, void* workspace,
                    int64_t workspace_bytes, void* stream) {
-    if (!q || !k_rot || !v_new || !out || H < 1 || !finite_pos(sm_scale) || n_split < 0) return NOMAS_EINVAL;
+    if (!q || !k_new || !v_new || !out || H < 1 || !finite_pos(sm_scale) || n_split < 0) return NOMAS_EINVAL;
     if (n_split > NOMAS_MAX_SPLIT) return NOMAS_EUNSUPPORTED;
-    if (!al16(q) || !al16(k_rot) || !al16(v_new) || !al16(out) || (lse && !al4(lse))) return NOMAS_EINVAL;
+    if (!al16(q) || !al16(k_new) || !al16(v_new) || !al16(out) || (lse && !al4(lse))) return NOMAS_EINVAL;
     if (cap < 0 || cache_len < 0 || cache_len > cap) return NOMAS_EINVAL;
     if (H > kMaxHeads || cap > kMaxTokens) return NOMAS_EUNSUPPORTED;
     if (cache_len > 0) {
@@ -201,7 +201,7 @@ int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_rot, const nomas_bf1
     if (!workspace || !al16(workspace) || workspace_bytes < need) return NOMAS_EINVAL;
     RopeTables rt;
     if ((rc = rope_tables(&rt)) != NOMAS_OK) return rc;
-    return launch_seg_attn(q, k_rot, v_new, st, (int)Ln, k_codes, v_codes, k_scale, v_scale, cap, (int)cache_len, H,
+    return launch_seg_attn(q, k_new, v_new, st, (int)Ln, k_codes, v_codes, k_scale, v_scale, cap, (int)cache_len, H,
                            sm_scale, out, lse, n_split, workspace, rt, (hipStream_t)stream);
 }
 

@@ -145,4 +145,39 @@ __device__ __forceinline__ uint4 rope_group_f32(uint4 x, int grp, int t, int h, 
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// float64 -> bf16, rounded once: truncating to float32 and setting the
+// sticky bit when inexact (round-to-odd) keeps the final round-to-nearest-
+// even to bf16 exact.
+__device__ __forceinline__ uint32_t f64_to_bf16(double d) {
+    float f = __double2float_rz(d);
+    uint32_t b = __float_as_uint(f);
+    if ((double)f != d) b |= 1u;
+    b += 0x7fffu + ((b >> 16) & 1u);
+    return b >> 16;
+}
+
+// one channel pair (x0, x1) rotated in float64 with separately rounded
+// products (no fma contraction), each output rounded once to bf16
+__device__ __forceinline__ uint32_t rot_pair_f64(uint32_t in, double2 cs) {
+#pragma clang fp contract(off)
+    double x0 = (double)bf16lo(in), x1 = (double)bf16hi(in);
+    double y0 = x0 * cs.x - x1 * cs.y;
+    double y1 = x0 * cs.y + x1 * cs.x;
+    return f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+}
+
+// 8 channels [8*grp, 8*grp+8) of token tok of the segments in st, rotated
+// by 3D RoPE in float64 and rounded once to bf16; text tokens unchanged.
+__device__ __forceinline__ uint4 rope_chunk_f64(uint4 w, int grp, int tok, const SegTable& st, const RopeTables& rt) {
+    int t, h, ww;
+    if (token_pos(st, tok, t, h, ww)) {
+        const double2* tab = rt.f64 + rope_entry(grp, t, h, ww);
+        w.x = rot_pair_f64(w.x, tab[0]);
+        w.y = rot_pair_f64(w.y, tab[1]);
+        w.z = rot_pair_f64(w.z, tab[2]);
+        w.w = rot_pair_f64(w.w, tab[3]);
+    }
+    return w;
+}
+
 }  // namespace nomas

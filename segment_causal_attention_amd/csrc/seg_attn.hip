@@ -6,9 +6,10 @@
 // cached token and to the new tokens of segments 0..a, never to a later
 // segment.  Cached K/V are INT8 with one fp32 scale per (token, head); the
 // attention itself runs in BF16 (comfyui-wiki, 单张 4090 配置): cached entries
-// enter the products as bf16(fl32(code*scale)); queries are rotated by 3D
-// RoPE (comfyui-wiki, 模型内部: [16, 56, 56], theta 256) on load and rounded
-// to bf16; new keys arrive already rotated (the rows the cache append stores).
+// enter the products as bf16(fl32(code*scale)); queries and new keys are
+// rotated by 3D RoPE (comfyui-wiki, 模型内部: [16, 56, 56], theta 256) and
+// rounded to bf16: queries on load in float32, keys in the pack kernel in
+// float64 (the same rows nomas_rope3d gives the cache append).
 //
 // Two kernels.  The pack kernel lays the keys a call can touch (the cache,
 // then the new tokens) out as 64-key tiles, each a byte image of what the
@@ -81,18 +82,21 @@ __device__ __forceinline__ float i8(uint32_t word, int byte) {
 // ---------------------------------------------------------------------------
 // Pack kernel: one workgroup of 256 threads builds the image of tile t of
 // head h.  Key x of the packed range is cache token x for x < Lc, new token
-// x - Lc for x < Lc + Ln, and zero beyond.
+// x - Lc for x < Lc + Ln (its key rotated by 3D RoPE in float64 and rounded
+// once to bf16), and zero beyond.
 
 struct PackArgs {
     const int8_t* kc;
     const int8_t* vc;
     const float* ks;
     const float* vs;
-    const uint16_t* k;
+    const uint16_t* k;              // new keys before RoPE
     const uint16_t* v;
     uint8_t* img;
     int64_t cap;
     int32_t Lc, Ln, H, ntk;         // ntk: tiles per head
+    SegTable segs;                  // the new segments (positions of the new keys)
+    RopeTables rt;
 };
 
 constexpr int PACK_NT = 256;
@@ -109,7 +113,9 @@ __device__ __forceinline__ uint4 key_chunk(const PackArgs& P, int h, int x, int 
     }
     if (x < P.Lc + P.Ln) {
         const uint16_t* src = (is_v ? P.v : P.k) + ((size_t)(x - P.Lc) * P.H + h) * D + 8 * j;
-        return *reinterpret_cast<const uint4*>(src);
+        const uint4 w = *reinterpret_cast<const uint4*>(src);
+        // new keys are rotated here exactly as nomas_rope3d rotates them
+        return is_v ? w : rope_chunk_f64(w, j, x - P.Lc, P.segs, P.rt);
     }
     return make_uint4(0, 0, 0, 0);
 }
@@ -548,6 +554,8 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     P.k = k; P.v = v;
     P.img = static_cast<uint8_t*>(workspace);
     P.cap = cap; P.Lc = Lc; P.Ln = Ln; P.H = H; P.ntk = ntk;
+    P.segs = segs;
+    P.rt = rt;
 
     AttnArgs A{};
     A.q = q; A.img = P.img;

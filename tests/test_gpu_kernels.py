@@ -102,9 +102,7 @@ def _run_gpu(q, k, v, segs, cache, Lc, H, with_lse=True, n_split=0):
         kc, vc, ks, vs = (dev(a) for a in cache)
     else:
         kc = vc = ks = vs = None
-    # keys enter attention rotated, as the rope3d kernel returns them
-    k_rot = nomas.rope3d(dev16(k), segs)
-    out = nomas.seg_attn(dev16(q), k_rot, dev16(v), segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse,
+    out = nomas.seg_attn(dev16(q), dev16(k), dev16(v), segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse,
                          n_split=n_split)
     torch.cuda.synchronize()
     return f64(out), (lse.cpu().numpy() if with_lse else None), out
@@ -223,8 +221,8 @@ def test_seg_attn_deterministic_and_cache_copy():
     # a resumed cache (codes, scales and length copied elsewhere) gives the same bits
     kc, vc, ks, vs = (dev(a) for a in cache)
     kc2, vc2, ks2, vs2 = (t.clone() for t in (kc, vc, ks, vs))
-    o3 = nomas.seg_attn(dev16(args[0]), nomas.rope3d(dev16(args[1]), segs[1:]), dev16(args[2]), segs[1:],
-                        kc2, vc2, ks2, vs2, cache_len=n, sm_scale=SM)
+    o3 = nomas.seg_attn(dev16(args[0]), dev16(args[1]), dev16(args[2]), segs[1:], kc2, vc2, ks2, vs2,
+                        cache_len=n, sm_scale=SM)
     torch.cuda.synchronize()
     assert torch.equal(o1, o3)
 

@@ -27,10 +27,9 @@ def sample_rows(Lq, stride, tail=64, extra=()):
 
 
 def run_attn(q, k, v, segs, cache, Lc, H):
-    """Attention as the path runs it: keys rotated by the rope3d kernel first."""
     kc, vc, ks, vs = cache
     lse = torch.empty((H, q.shape[0]), dtype=torch.float32, device="cuda:0")
-    out = nomas.seg_attn(q, nomas.rope3d(k, segs), v, segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse)
+    out = nomas.seg_attn(q, k, v, segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse)
     torch.cuda.synchronize()
     return out, lse
 
