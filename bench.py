@@ -13,8 +13,9 @@ HBM before timing starts.
 
 value = algorithmic attention FLOPs per step / wall time per step (TFLOP/s),
 with algorithmic FLOPs = 4 * 128 * H * (allowed query-key pairs).
-The roofline block times nomas_seg_attn alone (its two launches: the pack
-pre-pass and the attention kernel) with HIP events on its stream.
+The roofline block times nomas_seg_attn alone (its launches: the pack
+pre-pass, the attention kernel and, since this shape splits each query
+tile's key range in two, the merge) with HIP events on its stream.
 The CPU baseline times the oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -48,7 +49,7 @@ def kernel_digest() -> str:
 
 
 def traffic_for_current_kernel():
-    """HBM bytes per nomas_seg_attn call (pack + attention kernels) from the
+    """HBM bytes per nomas_seg_attn call (pack, attention and merge kernels) from the
     committed counter summary, or None when the kernel source changed since
     the counters were taken."""
     try:
@@ -200,7 +201,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "nomas_seg_attn (pack_kernel + seg_attn_kernel)",
+            "kernel": "nomas_seg_attn (pack_kernel + seg_attn_kernel + merge_kernel)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
