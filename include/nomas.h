@@ -133,7 +133,8 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
  *   bytes (same segments, cache_len, H and n_split, on the current device),
  *   16-byte aligned, owned by the caller; the call overwrites it (the keys
  *   laid out as 64-key tiles, about 140 bytes per cached or new token and
- *   head, plus fp32 partial results when the keys are split), so two calls
+ *   head, each tile's largest squared key norm, plus fp32 partial results
+ *   when the keys are split), so two calls
  *   in flight must not share one.  Too small or NULL: NOMAS_EINVAL.
  * n_new_segs in [1, NOMAS_MAX_SEGS]; cap <= NOMAS_MAX_CACHE and
  * Ln * H <= NOMAS_MAX_TOKEN_HEADS, else NOMAS_EUNSUPPORTED.
@@ -148,10 +149,11 @@ int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf1
 
 /*
  * Workspace bytes nomas_seg_attn needs for these new segments, cache length,
- * head count and n_split on the current device: H * ceil((cache_len + Ln) /
- * 64) * 35840, plus parts * Ln * H * 516 when the keys are split into parts
- * > 1; or a negative error code (NOMAS_EINVAL / NOMAS_EUNSUPPORTED as for
- * nomas_seg_attn).  Host only.
+ * head count and n_split on the current device: with T = H * ceil((cache_len
+ * + Ln) / 64) tiles, T * 35840 + (4T rounded up to a multiple of 256), plus
+ * parts * Ln * H * 516 when the keys are split into parts > 1; or a negative
+ * error code (NOMAS_EINVAL / NOMAS_EUNSUPPORTED as for nomas_seg_attn).
+ * Host only.
  */
 int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len, int H,
                                  int n_split);

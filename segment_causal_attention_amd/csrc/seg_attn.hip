@@ -93,6 +93,7 @@ struct PackArgs {
     const uint16_t* k;              // new keys before RoPE
     const uint16_t* v;
     uint8_t* img;
+    float* knorm;                   // [H][ntk]: largest squared key norm of each tile
     int64_t cap;
     int32_t Lc, Ln, H, ntk;         // ntk: tiles per head
     SegTable segs;                  // the new segments (positions of the new keys)
@@ -122,8 +123,10 @@ __device__ __forceinline__ uint4 key_chunk(const PackArgs& P, int h, int x, int 
 
 __global__ __launch_bounds__(PACK_NT) void pack_kernel(const PackArgs P) {
     __shared__ __attribute__((aligned(16))) uint8_t im[TILE_BYTES];
+    __shared__ uint32_t kmax;       // bits of the largest squared key norm (non-negative floats order as integers)
     const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int x0 = t * BN;
+    if (tid == 0) kmax = 0;
     // K: 64 keys x 16 chunks of 8 channels, 4 chunks per thread
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -140,12 +143,32 @@ __global__ __launch_bounds__(PACK_NT) void pack_kernel(const PackArgs P) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) col[(8 * j + e) * VSTR] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
     }
-    // padding of the K rows (64) and V^T rows (128): zero
-    if (tid < BN) *reinterpret_cast<uint4*>(im + tid * KSTR * 2 + 2 * D) = make_uint4(0, 0, 0, 0);
+    // padding of the V^T rows (128): zero
     if (tid < D) *reinterpret_cast<uint4*>(im + KIMG + tid * VSTR * 2 + 2 * BN) = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    // squared norm of each key as the attention kernel sees it (bf16), four
+    // threads per key, 32 channels each; it goes into the key's row padding
+    // (first word, the rest zero) and into the tile's maximum
+    {
+        const int key = tid >> 2;
+        const uint32_t* row = reinterpret_cast<const uint32_t*>(im + key * KSTR * 2 + 64 * (tid & 3));
+        float n2 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float a = __uint_as_float(row[e] << 16), b = __uint_as_float(row[e] & 0xffff0000u);
+            n2 = fmaf(a, a, fmaf(b, b, n2));
+        }
+        n2 += __shfl_xor(n2, 1);
+        n2 += __shfl_xor(n2, 2);
+        if ((tid & 3) == 0) {
+            *reinterpret_cast<uint4*>(im + key * KSTR * 2 + 2 * D) = make_uint4(__float_as_uint(n2), 0, 0, 0);
+            atomicMax(&kmax, __float_as_uint(n2));
+        }
+    }
     __syncthreads();
     uint4* dst = reinterpret_cast<uint4*>(P.img + ((size_t)h * P.ntk + t) * TILE_BYTES);
     for (int i = tid; i < TILE_BYTES / 16; i += PACK_NT) dst[i] = reinterpret_cast<const uint4*>(im)[i];
+    if (tid == 0) P.knorm[(size_t)h * P.ntk + t] = __uint_as_float(kmax);
 }
 
 // ---------------------------------------------------------------------------
@@ -154,6 +177,7 @@ __global__ __launch_bounds__(PACK_NT) void pack_kernel(const PackArgs P) {
 struct AttnArgs {
     const uint16_t* q;
     const uint8_t* img;             // packed tile images
+    const float* knorm;             // [H][ntk] largest squared key norm per tile
     uint16_t* out;
     float* lse;
     float* po;                      // split > 1: partial outputs O/l [split][Ln][H][128] fp32
@@ -287,12 +311,15 @@ __device__ __forceinline__ void prob_stage(int stage, int q, const f32x16 (&s)[2
 
 // mx: row max of s (this lane half), taken at the end of the previous step;
 // returns the row max of sn, taken after the last product of this step.
+// FIXED: w.m is a bound that holds for the whole key range, so the step takes
+// no maxima and never rescales.
+template <bool FIXED>
 __device__ __forceinline__ float pipelined_step(const uint16_t* Kn, const uint16_t* V, int lim, int krd, int vrd,
                                                 WaveState& w, f32x16 (&s)[2], float mx, f32x16 (&sn)[2], float c,
                                                 int g) {
     if (lim < BN) {
         mask_tile(s, lim, g);
-        mx = fmaxf(max16(s, 0), max16(s, 8));
+        if (!FIXED) mx = fmaxf(max16(s, 0), max16(s, 8));
     }
     const f32x16 zero = {};
     uint32_t pk[16];
@@ -308,18 +335,21 @@ __device__ __forceinline__ float pipelined_step(const uint16_t* Kn, const uint16
         if (i < 16) sn[i & 1] = mfma(fr[i], w.qf[i >> 1], i < 2 ? zero : sn[i & 1]);
         else w.o[i & 3] = mfma(fr[i], pchunk(pk, (i - 16) >> 2), w.o[i & 3]);
         // rescale of tile j
-        if (i == 2) update_max(mx, w, c);
+        if (!FIXED && i == 2) update_max(mx, w, c);
         // probabilities: pair q in slots 3+q, 4+q, 5+q
 #pragma unroll
         for (int st = 0; st < 3; ++st)
             if (i - 3 - st >= 0 && i - 3 - st < 16) prob_stage(st, i - 3 - st, s, w, c, t, pk);
         SLOT_FENCE();
     }
-    return fmaxf(max16(sn, 0), max16(sn, 8));
+    return FIXED ? 0.0f : fmaxf(max16(sn, 0), max16(sn, 8));
 }
+
+template <bool B> struct Fixed { static constexpr bool value = B; };
 
 __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * TILE_BYTES];
+    __shared__ float kred[NW];      // per wave: largest squared key norm of the key range
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -357,6 +387,18 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
             ws.qf[kk] = __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, x.z, x.w});
         }
     }
+    // squared norm of the rotated query as the products see it (bf16)
+    float q2 = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const u32x4 x = __builtin_bit_cast(u32x4, ws.qf[kk]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = __uint_as_float(x[e] << 16), b = __uint_as_float(x[e] & 0xffff0000u);
+            q2 = fmaf(a, a, fmaf(b, b, q2));
+        }
+    }
+    q2 = half_sum(q2);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -373,6 +415,20 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const int nt = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * nt_all / A.nsplit) - t0);
     const int krd = l32 * KSTR + 8 * g;             // this lane's K / V^T fragment offsets
     const int vrd = l32 * VSTR + 8 * g;
+    {
+        // largest squared norm of the allowed keys of this range: the tile
+        // maxima of its full tiles, the keys' own norms (row padding of the
+        // image) in a last, partial tile
+        const int nfull = nt > 0 ? min(nt, (nkeys - t0 * BN) / BN) : 0;    // t0 * BN < nkeys when nt > 0
+        float k2 = 0.0f;
+        for (int t = tid; t < nfull; t += NT) k2 = fmaxf(k2, A.knorm[(int64_t)head * A.ntk + t0 + t]);
+        if (nfull < nt && tid < nkeys - (t0 + nfull) * BN)
+            k2 = fmaxf(k2, *reinterpret_cast<const float*>(A.img + ((int64_t)head * A.ntk + t0 + nfull) * TILE_BYTES +
+                                                           tid * KSTR * 2 + 2 * D));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, off));
+        if (lane == 0) kred[wave] = k2;
+    }
 
     // ---- tile copies: wave w copies kilobytes w, w+8, ... of each image
     const int wv = __builtin_amdgcn_readfirstlane(wave) & (NW - 1);
@@ -395,6 +451,19 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     };
     auto kbuf = [&](int b) { return reinterpret_cast<const uint16_t*>(lds + b * TILE_BYTES); };
     auto vbuf = [&](int b) { return reinterpret_cast<const uint16_t*>(lds + b * TILE_BYTES + KIMG); };
+    // Keys a row may not see get probability 0, but 0 x NaN is NaN: a later
+    // segment's non-finite value in the last tile would still reach P.V.  So
+    // the last tile's columns of such keys are zeroed in LDS, in its buffer
+    // and in the buffer of the clamped copy that the padding step after an
+    // odd tile count reads.
+    const int lim_last = nt > 0 ? nkeys - (t0 + nt - 1) * BN : BN;    // allowed keys of the last tile
+    auto zero_vt = [&](int b) {
+        uint16_t* vt = reinterpret_cast<uint16_t*>(lds + b * TILE_BYTES + KIMG);
+        for (int i = tid; i < D * BN; i += NT) {
+            const int key = i & (BN - 1);
+            if (key >= lim_last) vt[(i >> 6) * VSTR + vperm_key(key)] = 0;
+        }
+    };
 
     // Tile t lives in buffer t % 4.  Step j copies tile j+3 into the buffer
     // that tile j-1 left, works on tiles j and j+1, and ends once its copies
@@ -405,6 +474,11 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     copy_tile(2, 2);
     wait_dma<0>();      // tiles 0 and 1 (and 2) of this wave
     lds_barrier();
+    if (nt == 1 && lim_last < BN) {
+        zero_vt(0);
+        zero_vt(1);
+        lds_barrier();
+    }
 
     f32x16 sa[2], sb[2];
     {
@@ -413,21 +487,54 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
         for (int i = 0; i < 16; ++i) sa[i & 1] = mfma(kfrag(kbuf(0), krd, i), ws.qf[i >> 1], i < 2 ? zero : sa[i & 1]);
     }
     float ma = fmaxf(max16(sa, 0), max16(sa, 8)), mb = 0.0f;    // row maxima of the two score sets
+    // Cauchy-Schwarz: every score of this row is at most |q| max|k|.  When
+    // that bound lies within 64 (base 2) of the first tile's largest score,
+    // it serves as the softmax shift for the whole range: no probability
+    // exceeds 1 and the largest is at least 2^-64, far from underflow.  Else
+    // the shift follows the running maximum.  The choice is per wave.
+    float k2max = kred[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) k2max = fmaxf(k2max, kred[i]);
+    const float bound = c * __builtin_sqrtf(q2 * k2max);
+    const bool fixed = nkeys - t0 * BN >= BN && __all(bound - c * half_max(ma) <= 64.0f);
+    if (fixed) ws.m = bound;
     // Step j: scores of tile j in x, next tile's scores into y.  Steps past
     // the last tile see a fully masked tile and change nothing; steps go in
     // pairs so the two score sets swap roles without copies.
-    auto step = [&](int j, f32x16 (&x)[2], float mx, f32x16 (&y)[2]) {
+    // fx: Fixed<> (the shift); tail: the step may have to zero a buffer
+    auto step = [&](auto fx, auto tail, int j, f32x16 (&x)[2], float mx, f32x16 (&y)[2]) {
         const int b0 = j & 3, b1 = (j + 1) & 3;
         copy_tile(j + 3, (j + 3) & 3);
         const int lim = j < nt ? min(BN, nkeys - (t0 + j) * BN) : 0;
-        const float my = pipelined_step(kbuf(b1), vbuf(b0), lim, krd, vrd, ws, x, mx, y, c, g);
+        const float my = pipelined_step<decltype(fx)::value>(kbuf(b1), vbuf(b0), lim, krd, vrd, ws, x, mx, y, c, g);
+        // the last tile (landed, read from the next step on) and its copy
+        if (decltype(tail)::value && lim_last < BN && (j == nt - 2 || (j == nt - 1 && (nt & 1)))) zero_vt(b1);
         wait_prev_tile();
         lds_barrier();
         return my;
     };
-    for (int j = 0; j < nt; j += 2) {
-        mb = step(j, sa, ma, sb);
-        ma = step(j + 1, sb, mb, sa);
+    // steps nt-2 and, for odd nt, nt-1 zero; they fall in the last one or two pairs
+    const int jt = max(0, (nt & 1) ? nt - 3 : nt - 2);
+    if (fixed) {
+        int j = 0;
+        for (; j < jt; j += 2) {
+            step(Fixed<true>{}, Fixed<false>{}, j, sa, 0.0f, sb);
+            step(Fixed<true>{}, Fixed<false>{}, j + 1, sb, 0.0f, sa);
+        }
+        for (; j < nt; j += 2) {
+            step(Fixed<true>{}, Fixed<true>{}, j, sa, 0.0f, sb);
+            step(Fixed<true>{}, Fixed<true>{}, j + 1, sb, 0.0f, sa);
+        }
+    } else {
+        int j = 0;
+        for (; j < jt; j += 2) {
+            mb = step(Fixed<false>{}, Fixed<false>{}, j, sa, ma, sb);
+            ma = step(Fixed<false>{}, Fixed<false>{}, j + 1, sb, mb, sa);
+        }
+        for (; j < nt; j += 2) {
+            mb = step(Fixed<false>{}, Fixed<true>{}, j, sa, ma, sb);
+            ma = step(Fixed<false>{}, Fixed<true>{}, j + 1, sb, mb, sa);
+        }
     }
     wait_dma<0>();
     }
@@ -536,9 +643,13 @@ int plan_splits(const SegTable& segs, int Lc, int H, int n_split) {
     return best;
 }
 
+// per-tile key norms follow the images, padded to 256 bytes
+static int64_t knorm_bytes(int64_t tiles) { return (tiles * 4 + 255) / 256 * 256; }
+
 int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int n_split) {
     const int p = plan_splits(segs, Lc, H, n_split);
-    int64_t b = (int64_t)H * seg_attn_workspace_tiles(Lc, Ln) * TILE_BYTES;
+    const int64_t tiles = (int64_t)H * seg_attn_workspace_tiles(Lc, Ln);
+    int64_t b = tiles * TILE_BYTES + knorm_bytes(tiles);
     if (p > 1) b += (int64_t)p * Ln * H * (D + 1) * 4;
     return b;
 }
@@ -553,17 +664,18 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     P.kc = kc; P.vc = vc; P.ks = ks; P.vs = vs;
     P.k = k; P.v = v;
     P.img = static_cast<uint8_t*>(workspace);
+    P.knorm = reinterpret_cast<float*>(P.img + (int64_t)H * ntk * TILE_BYTES);
     P.cap = cap; P.Lc = Lc; P.Ln = Ln; P.H = H; P.ntk = ntk;
     P.segs = segs;
     P.rt = rt;
 
     AttnArgs A{};
-    A.q = q; A.img = P.img;
+    A.q = q; A.img = P.img; A.knorm = P.knorm;
     A.out = out; A.lse = lse;
     A.Lc = Lc; A.Ln = Ln; A.H = H; A.ntk = ntk;
     A.nsplit = nsplit;
     if (nsplit > 1) {
-        A.po = reinterpret_cast<float*>(P.img + (int64_t)H * ntk * TILE_BYTES);
+        A.po = reinterpret_cast<float*>(P.img + (int64_t)H * ntk * TILE_BYTES + knorm_bytes((int64_t)H * ntk));
         A.plse = A.po + (int64_t)nsplit * Ln * H * D;
     }
     A.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);

@@ -48,7 +48,7 @@ def test_seg_attn_host_checks():
     sa, n = segs((16, 0, 2, 4, 6))
     P = ctypes.c_void_p
     need = L.nomas_seg_attn_workspace(sa, n, 0, 2, 1)
-    assert need == 2 * 35840                           # 16 + 2*4*6 = 64 new keys: one tile per head
+    assert need == 2 * 35840 + 256                     # 16 + 2*4*6 = 64 new keys: one tile per head, + key norms
     good = dict(q=FAKE, k=FAKE, v=FAKE, segs=sa, n=n, kc=None, vc=None, ks=None, vs=None, cap=0, clen=0,
                 H=2, sm=0.088, out=FAKE, lse=None, split=1, ws=FAKE, wsb=need)
 
@@ -80,10 +80,12 @@ def test_seg_attn_host_checks():
     assert call(ws=None) == nomas.EINVAL               # workspace missing, too small or misaligned
     assert call(wsb=need - 1) == nomas.EINVAL
     assert call(ws=FAKE + 8) == nomas.EINVAL
-    # workspace size: H * ceil((cache + new tokens) / 64) tiles of 35840 bytes
-    assert L.nomas_seg_attn_workspace(sa, n, 1000, 3, 1) == 3 * ((1000 + 64 + 63) // 64) * 35840
+    # workspace size: H * ceil((cache + new tokens) / 64) tiles of 35840 bytes, then one float per tile
+    # (the tile's largest squared key norm) padded to 256 bytes
+    assert L.nomas_seg_attn_workspace(sa, n, 1000, 3, 1) == 3 * ((1000 + 64 + 63) // 64) * 35840 + 256
+    assert L.nomas_seg_attn_workspace(sa, n, 4000, 4, 1) == 4 * 64 * 35840 + 1024
     # split keys: fp32 partial outputs and log-sum-exps of every part on top
-    assert L.nomas_seg_attn_workspace(sa, n, 1000, 3, 2) == 3 * 17 * 35840 + 2 * 64 * 3 * 129 * 4
+    assert L.nomas_seg_attn_workspace(sa, n, 1000, 3, 2) == 3 * 17 * 35840 + 256 + 2 * 64 * 3 * 129 * 4
     assert L.nomas_seg_attn_workspace(sa, n, -1, 3, 1) == nomas.EINVAL
     assert L.nomas_seg_attn_workspace(sa, n, 0, 0, 1) == nomas.EINVAL
     assert L.nomas_seg_attn_workspace(sa, n, 0, 2, -1) == nomas.EINVAL

@@ -1,6 +1,8 @@
 """GPU parity of each libnomas entry point against the CPU oracle, on small and
 edge-case shapes (ragged tails, several query tiles, packed segments, short
 caches).  Calls go through the C ABI (ctypes binding)."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -207,6 +209,71 @@ def test_seg_attn_future_segments_never_leak():
     assert np.all(np.isfinite(got1[:64])) and np.all(np.isfinite(lse1[:, :64]))
     assert np.array_equal(got0[:64], got1[:64]) and np.array_equal(lse0[:, :64], lse1[:, :64])
     assert np.all(np.isnan(got1[128:]))
+
+
+@pytest.mark.parametrize("poison", ["x100", "nan"])
+def test_seg_attn_future_segments_never_leak_unaligned(poison):
+    """Packed segments whose boundaries fall inside 64-key tiles, over a
+    77-token cache: the last key tile a row may read also holds keys of later
+    segments.  Scaling those keys and values by 100 (or making them NaN)
+    leaves every earlier row's output and lse bit-identical."""
+    (segs, Lc, H), = [(c[1], c[2], c[3]) for c in EDGE if c[0] == "packed-5"]
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    ends = np.cumsum([s[0] + s[2] * s[3] * s[4] for s in segs])
+    got0, lse0, _ = _run_gpu(q, k, v, segs, cache, Lc, H)
+    for cut in (1, 2, 4):
+        n = int(ends[cut - 1])              # rows and keys of segments [0, cut)
+        k1, v1 = k.copy(), v.copy()
+        if poison == "nan":
+            k1[n:] = 0x7FC0
+            v1[n:] = 0x7FC0
+        else:
+            k1[n:] = oracle.f64_to_bf16_bits(oracle.bf16_round(oracle.bf16_bits_to_f64(k[n:]) * 100.0))
+            v1[n:] = oracle.f64_to_bf16_bits(oracle.bf16_round(oracle.bf16_bits_to_f64(v[n:]) * 100.0))
+        say("seg_attn leak", poison, "cut", cut, "rows", n)
+        got1, lse1, _ = _run_gpu(q, k1, v1, segs, cache, Lc, H)
+        assert np.array_equal(got0[:n], got1[:n]) and np.array_equal(lse0[:, :n], lse1[:, :n])
+
+
+def _shift_gaps(q, k, segs, cache, Lc):
+    """Per head and 32-row group of a one-segment input: c |q| max|k| over the
+    allowed keys minus the largest score of the first 64 keys, the quantity
+    whose size (against 64) decides between a fixed softmax shift and the
+    running maximum (float64, from the oracle's rotations and dequantised
+    cache)."""
+    c = SM / math.log(2.0)
+    qr = oracle.rope3d(oracle.bf16_bits_to_f64(q), segs)
+    kr = oracle.bf16_round(oracle.rope3d(oracle.bf16_bits_to_f64(k), segs))
+    kc, vc, ks, vs = cache
+    K = np.concatenate([oracle.dequant_bf16(kc[:, :Lc], ks[:, :Lc]).transpose(1, 0, 2), kr], axis=0)
+    gaps = []
+    for h in range(q.shape[1]):
+        kmax = np.sqrt((K[:, h] ** 2).sum(-1).max())
+        for g0 in range(0, q.shape[0], 32):
+            qg = qr[g0:g0 + 32, h]
+            bound = c * np.sqrt((qg ** 2).sum(-1)) * kmax
+            m0 = c * (qg @ K[:64, h].T).max(-1)
+            gaps.append((bound - m0).max())
+    return np.array(gaps)
+
+
+@pytest.mark.parametrize("n_split", [1, 2])
+def test_seg_attn_fixed_and_running_shift(n_split):
+    """Row groups whose Cauchy-Schwarz bound is close to their first tile's
+    largest score take a fixed softmax shift; groups of queries scaled x40
+    (scores of a few hundred, base 2) are far from it and keep the running
+    maximum with its rescaling.  The inputs hold both kinds; all rows meet
+    the parity bar against the oracle."""
+    segs, Lc, H = [(512, 0, 0, 0, 0)], 300, 2
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    qf = oracle.bf16_bits_to_f64(q)
+    for g0 in range(32, 512, 64):           # every other 32-row group
+        qf[g0:g0 + 32] *= 40.0
+    q = oracle.f64_to_bf16_bits(oracle.bf16_round(qf))
+    gaps = _shift_gaps(q, k, segs, cache, Lc)
+    say("shift gaps: min %.1f max %.1f" % (gaps.min(), gaps.max()))
+    assert (gaps < 48).sum() >= 8 and (gaps > 96).sum() >= 8
+    _check_case("fixed-and-running-shift", q, k, v, segs, cache, Lc, H, n_split=n_split)
 
 
 def test_seg_attn_deterministic_and_cache_copy():
