@@ -122,52 +122,63 @@ __device__ __forceinline__ uint4 key_chunk(const PackArgs& P, int h, int x, int 
 }
 
 __global__ __launch_bounds__(PACK_NT) void pack_kernel(const PackArgs P) {
-    __shared__ __attribute__((aligned(16))) uint8_t im[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VSTR];     // the V^T image
     __shared__ uint32_t kmax;       // bits of the largest squared key norm (non-negative floats order as integers)
     const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int x0 = t * BN;
+    uint8_t* img = P.img + ((size_t)h * P.ntk + t) * TILE_BYTES;
     if (tid == 0) kmax = 0;
-    // K: 64 keys x 16 chunks of 8 channels, 4 chunks per thread
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + PACK_NT * i, key = c >> 4, j = c & 15;
-        *reinterpret_cast<uint4*>(im + key * KSTR * 2 + 16 * j) = key_chunk(P, h, x0 + key, j, false);
-    }
-    // V^T: thread = (key, channel chunk); its 8 channels go to 8 rows
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + PACK_NT * i, key = c >> 4, j = c & 15;
-        const uint4 w = key_chunk(P, h, x0 + key, j, true);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-        uint16_t* col = reinterpret_cast<uint16_t*>(im + KIMG) + vperm_key(key);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) col[(8 * j + e) * VSTR] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
-    }
-    // padding of the V^T rows (128): zero
-    if (tid < D) *reinterpret_cast<uint4*>(im + KIMG + tid * VSTR * 2 + 2 * BN) = make_uint4(0, 0, 0, 0);
     __syncthreads();
-    // squared norm of each key as the attention kernel sees it (bf16), four
-    // threads per key, 32 channels each; it goes into the key's row padding
-    // (first word, the rest zero) and into the tile's maximum
+    // K: thread = (key, quarter of the channels); its 64 bytes go straight to
+    // the key's image row.  The key's squared norm as the attention kernel
+    // sees it (bf16) goes into the row padding (first word, the rest zero) and
+    // into the tile's maximum.
     {
-        const int key = tid >> 2;
-        const uint32_t* row = reinterpret_cast<const uint32_t*>(im + key * KSTR * 2 + 64 * (tid & 3));
+        const int key = tid >> 2, qd = tid & 3;
+        uint4 w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = key_chunk(P, h, x0 + key, 4 * qd + j, false);
         float n2 = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float a = __uint_as_float(row[e] << 16), b = __uint_as_float(row[e] & 0xffff0000u);
-            n2 = fmaf(a, a, fmaf(b, b, n2));
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __uint_as_float(ww[e] << 16), b = __uint_as_float(ww[e] & 0xffff0000u);
+                n2 = fmaf(a, a, fmaf(b, b, n2));
+            }
         }
         n2 += __shfl_xor(n2, 1);
         n2 += __shfl_xor(n2, 2);
-        if ((tid & 3) == 0) {
-            *reinterpret_cast<uint4*>(im + key * KSTR * 2 + 2 * D) = make_uint4(__float_as_uint(n2), 0, 0, 0);
+        uint4* row = reinterpret_cast<uint4*>(img + key * KSTR * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) row[4 * qd + j] = w[j];
+        if (qd == 0) {
+            row[D / 8] = make_uint4(__float_as_uint(n2), 0, 0, 0);
             atomicMax(&kmax, __float_as_uint(n2));
         }
     }
+    // V^T through LDS: thread = (key pair, 16 channels); each channel row gets
+    // one word holding both keys (adjacent columns under the chunk
+    // permutation), consecutive lanes on consecutive words
+    {
+        const int kp = tid & 31, cg = tid >> 5;
+        const uint4 a[2] = {key_chunk(P, h, x0 + 2 * kp, 2 * cg, true), key_chunk(P, h, x0 + 2 * kp, 2 * cg + 1, true)};
+        const uint4 b[2] = {key_chunk(P, h, x0 + 2 * kp + 1, 2 * cg, true),
+                            key_chunk(P, h, x0 + 2 * kp + 1, 2 * cg + 1, true)};
+        uint32_t* col = reinterpret_cast<uint32_t*>(vt + vperm_key(2 * kp));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t wa = (&a[e >> 3].x)[(e >> 1) & 3], wb = (&b[e >> 3].x)[(e >> 1) & 3];
+            const uint32_t lo = (e & 1) ? wa >> 16 : wa & 0xffffu, hi = (e & 1) ? wb >> 16 : wb & 0xffffu;
+            col[(16 * cg + e) * (VSTR / 2)] = lo | (hi << 16);
+        }
+    }
+    // padding of the V^T rows (128): zero
+    if (tid < D) *reinterpret_cast<uint4*>(vt + tid * VSTR + BN) = make_uint4(0, 0, 0, 0);
     __syncthreads();
-    uint4* dst = reinterpret_cast<uint4*>(P.img + ((size_t)h * P.ntk + t) * TILE_BYTES);
-    for (int i = tid; i < TILE_BYTES / 16; i += PACK_NT) dst[i] = reinterpret_cast<const uint4*>(im)[i];
+    uint4* dst = reinterpret_cast<uint4*>(img + KIMG);
+    for (int i = tid; i < VIMG / 16; i += PACK_NT) dst[i] = reinterpret_cast<const uint4*>(vt)[i];
     if (tid == 0) P.knorm[(size_t)h * P.ntk + t] = __uint_as_float(kmax);
 }
 
