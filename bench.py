@@ -20,6 +20,7 @@ The CPU baseline times the oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
        python bench.py --copy-calibration   (plain copy kernel for counter scaling)
+       python bench.py --workloads          (the other workloads, one JSON line each; see workloads())
 """
 from __future__ import annotations
 
@@ -87,6 +88,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--workloads", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -95,6 +97,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workloads:
+        workloads()
         return
 
     import numpy as np
@@ -212,6 +217,164 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def workloads():
+    """Throughput of the path on the other workloads, one JSON line each, all
+    inputs seeded synthetic and resident in HBM before timing, HIP events on
+    the launch stream:
+      turn3s      16,096 queries over 15,840 cached + 16,096 own keys (median of 10 calls)
+      seg4s       54 distinct layers (outlier channels x20) x 8 steps = 432 calls
+                  timed end to end (median of 3 sequences)
+      fiveturns   per turn k = 0..4: seg_attn over a cache of 63,360 k tokens,
+                  cam_xattn (72 camera tokens), rope3d and kv_quant_append, each
+                  the median of 5 calls, the HBM-bound ones in GB/s of
+                  algorithmic bytes
+      fullcache-h2  the full-cache shape with 2 heads: one GPU's share when the
+                  16 heads are split over 8 GPUs (median of 5 calls)
+    History caches are built on the GPU by rope3d + kv_quant_append (bit-exact
+    to the oracle's quantiser)."""
+    import numpy as np
+    import torch
+
+    import segment_causal_attention_amd as nomas
+    import synth
+
+    dev = torch.device("cuda:0")
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+    stream = torch.cuda.current_stream()
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    def build_cache(k_hist, v_hist, hist_segs, H, cap):
+        kc = torch.empty((H, cap, 128), dtype=torch.int8, device=dev)
+        vc = torch.empty((H, cap, 128), dtype=torch.int8, device=dev)
+        ks = torch.empty((H, cap), dtype=torch.float32, device=dev)
+        vs = torch.empty((H, cap), dtype=torch.float32, device=dev)
+        if k_hist is not None:
+            kh = d16(k_hist)
+            nomas.rope3d(kh, hist_segs, out=kh)
+            nomas.kv_quant_append(kh, d16(v_hist), kc, vc, ks, vs, 0)
+            del kh
+        return kc, vc, ks, vs
+
+    def timed(fn, n, warm=2):
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    def emit(name, **kw):
+        line = dict(workload=name, **kw)
+        print(json.dumps(line), flush=True)
+
+    def attn_line(name, ms, H, Lq, keys, extra=None):
+        fl = 4.0 * 128 * H * Lq * keys
+        tf = fl / (ms * 1e-3) / 1e12
+        emit(name, metric="seg_attn TFLOP/s", value=round(tf, 2), unit="TFLOP/s", ms=round(ms, 3),
+             pct_of_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2), heads=H, queries=Lq, keys_per_query=keys,
+             algorithmic_flop=fl, **(extra or {}))
+
+    # ---- turn3s
+    log("workload turn3s")
+    cfg = synth.CONFIGS[2]
+    inp = synth.layer_inputs(2)
+    (seg,) = cfg.new_segs
+    cache = build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs, cfg.H, cfg.Lc)
+    q, k, v = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])
+    out = torch.empty_like(q)
+    ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
+                                      stream=stream), 10, 3)
+    attn_line("turn3s", ms, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq)
+    del q, k, v, out, ws, cache, inp
+
+    # ---- seg4s: 54 layers resident, 8 steps over all of them
+    log("workload seg4s: 54 layers resident, 8 steps over all of them")
+    cfg = synth.CONFIGS[3]
+    (seg,) = cfg.new_segs
+    layers = []
+    t0 = time.time()
+    for l in range(cfg.layers):
+        inp = synth.layer_inputs(3, l)
+        cache = build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs, cfg.H, cfg.Lc)
+        layers.append((d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])) + cache)
+        del inp
+        if l % 6 == 5:
+            log("seg4s: %d of %d layers resident (%.0f s)" % (l + 1, cfg.layers, time.time() - t0))
+    out = torch.empty_like(layers[0][0])
+    ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H), dtype=torch.uint8, device=dev)
+
+    def sequence():
+        for _ in range(cfg.steps):
+            for (q, k, v, kc, vc, ks, vs) in layers:
+                nomas.seg_attn(q, k, v, [seg], kc, vc, ks, vs, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
+                               stream=stream)
+
+    ms = timed(sequence, 3, 1)
+    calls = cfg.layers * cfg.steps
+    attn_line("seg4s", ms / calls, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq,
+              dict(calls=calls, sequence_ms=round(ms, 1), outlier_channels=cfg.outliers))
+    del layers, out, ws
+
+    # ---- fiveturns
+    log("workload fiveturns")
+    cfg = synth.CONFIGS[5]
+    H = cfg.H
+    n = synth.turn_seg(0).ntok
+    cache = build_cache(None, None, None, H, 5 * n)
+    length = 0
+    for t in range(5):
+        inp = synth.turn_inputs(t)
+        seg = inp["seg"]
+        q, k, v, qc = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"]), d16(inp["q_cam"])
+        wk, wv = d16(inp["w_k"]), d16(inp["w_v"])
+        cam = torch.from_numpy(nomas.cam_tokens(inp["c2w"])).to(dev)
+        out, oc, kr = torch.empty_like(q), torch.empty_like(qc), torch.empty_like(k)
+        ws = torch.empty(nomas.seg_attn_workspace([seg], length, H), dtype=torch.uint8, device=dev)
+        ms_a = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=length, sm_scale=sm, out=out,
+                                            workspace=ws, stream=stream), 5)
+        ms_c = timed(lambda: nomas.cam_xattn(qc, cam, wk, wv, sm_scale=sm, out=oc, stream=stream), 5)
+        ms_r = timed(lambda: nomas.rope3d(k, [seg], out=kr, stream=stream), 5)
+        # appending the same rows at the same offset is idempotent
+        ms_q = timed(lambda: nomas.kv_quant_append(kr, v, *cache, length, stream=stream), 5)
+        elems = n * H * 128
+        gbs = lambda b, m: round(b / (m * 1e-3) / 1e9, 1)
+        attn_line("fiveturns-turn%d" % t, ms_a, H, n, length + n,
+                  dict(cache_tokens=length,
+                       cam_xattn=dict(ms=round(ms_c, 4), GBps=gbs(4 * elems, ms_c), camera_tokens=cam.shape[0]),
+                       rope3d=dict(ms=round(ms_r, 4), GBps=gbs(4 * elems, ms_r)),
+                       kv_quant_append=dict(ms=round(ms_q, 4), GBps=gbs(2 * 3 * elems + 2 * 4 * n * H, ms_q)),
+                       hbm_peak_GBps=PEAK_HBM_GBS))
+        length = nomas.kv_quant_append(kr, v, *cache, length, stream=stream)
+        torch.cuda.synchronize()
+        del q, k, v, qc, out, oc, kr, ws
+    del cache
+
+    # ---- fullcache-h2: one GPU's share of the full-cache shape
+    log("workload fullcache-h2: one GPU's share of the full-cache shape")
+    cfg = synth.CONFIGS[4]
+    H = 2
+    inp = synth.layer_inputs(4)
+    (seg,) = cfg.new_segs
+    (hseg,) = cfg.hist_segs
+    sub = lambda a: np.ascontiguousarray(a[:, :H])
+    cache = build_cache(sub(inp["k_hist"]), sub(inp["v_hist"]), [hseg], H, cfg.Lc)
+    q, k, v = d16(sub(inp["q"])), d16(sub(inp["k_new"])), d16(sub(inp["v_new"]))
+    del inp
+    out = torch.empty_like(q)
+    ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, H), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
+                                      stream=stream), 5)
+    attn_line("fullcache-h2", ms, H, cfg.Lq, cfg.Lc + cfg.Lq, dict(note="heads 0-1 of the full-cache inputs"))
 
 
 def cpu_baseline(inp, cfg, sm):
