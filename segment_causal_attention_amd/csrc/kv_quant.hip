@@ -29,49 +29,63 @@ __device__ __forceinline__ float quant_code(float x, float s) {
     return fminf(fmaxf(q, -127.0f), 127.0f);
 }
 
+constexpr int QT_PASSES = 4;        // 16-token passes per block
+
+// Block = 64 consecutive tokens of one head of K or of V, in passes of 16
+// whose loads are all issued first: each pass's codes land as 2 KB of
+// contiguous cache rows and its scales as 64 contiguous bytes.
 __global__ __launch_bounds__(256) void kv_quant_append_kernel(
-    const uint4* __restrict__ k, const uint4* __restrict__ v, int64_t rows_per_tensor, int H,
+    const uint4* __restrict__ k, const uint4* __restrict__ v, int64_t L, int H, int64_t ntb,
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
     int64_t cap, int64_t len) {
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int64_t per_tensor = (int64_t)H * ntb;
+    const bool is_v = blockIdx.x >= per_tensor;
+    const int64_t b = is_v ? blockIdx.x - per_tensor : blockIdx.x;
+    const int head = (int)(b / ntb);
     const int lane = threadIdx.x & 15;
-    if (row >= 2 * rows_per_tensor) return;     // uniform across the 16 lanes of a row
-    const bool is_v = row >= rows_per_tensor;
-    const int64_t r = is_v ? row - rows_per_tensor : row;   // token * H + head
-    const int64_t tok = r / H;
-    const int head = (int)(r - tok * H);
-
-    uint4 w = (is_v ? v : k)[r * 16 + lane];
-    float x[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
-                  bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
-    float a = 0.0f;
+    const int64_t tok0 = (b - head * ntb) * QT_PASSES * 16 + (threadIdx.x >> 4);
+    const uint4* src = is_v ? v : k;
+    uint4 w[QT_PASSES];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
-    const float s = a / 127.0f;
-
-    uint32_t packed[2] = {0u, 0u};
-    if (a > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int q = (int)quant_code(x[i], s);
-            packed[i >> 2] |= ((uint32_t)(q & 0xff)) << (8 * (i & 3));
-        }
+    for (int p = 0; p < QT_PASSES; ++p) {
+        const int64_t tok = tok0 + 16 * p;
+        w[p] = tok < L ? src[(tok * H + head) * 16 + lane] : make_uint4(0, 0, 0, 0);
     }
-    const int64_t dst = (int64_t)head * cap + len + tok;
     int8_t* codes = is_v ? vc : kc;
-    *reinterpret_cast<uint2*>(codes + dst * D + lane * 8) = make_uint2(packed[0], packed[1]);
-    if (lane == 0) (is_v ? vs : ks)[dst] = (a > 0.0f) ? s : 0.0f;
+    float* scales = is_v ? vs : ks;
+#pragma unroll
+    for (int p = 0; p < QT_PASSES; ++p) {
+        const int64_t tok = tok0 + 16 * p;
+        if (tok >= L) break;    // uniform across the 16 lanes of a row, and later passes are further on
+        float x[8] = {bf16lo(w[p].x), bf16hi(w[p].x), bf16lo(w[p].y), bf16hi(w[p].y),
+                      bf16lo(w[p].z), bf16hi(w[p].z), bf16lo(w[p].w), bf16hi(w[p].w)};
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
+        const float s = a / 127.0f;
+        uint32_t packed[2] = {0u, 0u};
+        if (a > 0.0f) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                int q = (int)quant_code(x[i], s);
+                packed[i >> 2] |= ((uint32_t)(q & 0xff)) << (8 * (i & 3));
+            }
+        }
+        const int64_t dst = (int64_t)head * cap + len + tok;
+        *reinterpret_cast<uint2*>(codes + dst * D + lane * 8) = make_uint2(packed[0], packed[1]);
+        if (lane == 0) scales[dst] = (a > 0.0f) ? s : 0.0f;
+    }
 }
 
 int launch_kv_quant_append(const uint16_t* k_rot, const uint16_t* v, int64_t L, int H,
                            int8_t* k_codes, int8_t* v_codes, float* k_scale, float* v_scale,
                            int64_t cap, int64_t len, hipStream_t stream) {
-    const int64_t rows = L * H;
-    const int64_t blocks = (2 * rows + 15) / 16;
+    const int64_t ntb = (L + 16 * QT_PASSES - 1) / (16 * QT_PASSES);    // blocks per head
+    const int64_t blocks = 2 * (int64_t)H * ntb;
     hipLaunchKernelGGL(kv_quant_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4*>(k_rot), reinterpret_cast<const uint4*>(v), rows, H,
+                       reinterpret_cast<const uint4*>(k_rot), reinterpret_cast<const uint4*>(v), L, H, ntb,
                        k_codes, v_codes, k_scale, v_scale, cap, len);
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
 }

@@ -2,30 +2,49 @@
 // 3D RoPE, axis sizes [16, 56, 56], theta 256), used on a segment's keys
 // before they are quantised into the cache.
 //
-// HBM-bound (4 B per element moved).  16 lanes own one (token, head) row,
-// 8 channels (4 pairs) each, rotated by rope_chunk_f64 (float64, rounded
-// once to bf16).
+// HBM-bound (4 B per element moved).  One wave per token: lane = (8-channel
+// group, head block), so the token's position and each group's float64
+// cos/sin entries are looked up once and applied to every head (lanes
+// 16b .. 16b+15 take heads b, b+4, ...); each head pass moves 1 KB of
+// contiguous rows.  The rotation is rope_chunk_f64's (float64, rounded once
+// to bf16).
 #include "common.hpp"
 
 namespace nomas {
 
-__global__ __launch_bounds__(256) void rope3d_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
-                                                     int64_t rows, int H, const SegTable st,
-                                                     const RopeTables rt) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = idx >> 4;
-    if (row >= rows) return;
-    const int grp = (int)(idx & 15);
-    const int tok = (int)(row / H);
-    y[idx] = rope_chunk_f64(x[idx], grp, tok, st, rt);
+constexpr int ROPE_NT = 256;        // 4 waves = 4 tokens per block
+
+__global__ __launch_bounds__(ROPE_NT) void rope3d_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
+                                                         int64_t L, int H, const SegTable st, const RopeTables rt) {
+    const int64_t tok = (int64_t)blockIdx.x * (ROPE_NT / 64) + (threadIdx.x >> 6);
+    if (tok >= L) return;
+    const int lane = threadIdx.x & 63, grp = lane & 15;
+    int t, h, w;
+    const bool video = token_pos(st, (int)tok, t, h, w);
+    double2 cs[4] = {};
+    if (video) {
+        const double2* tab = rt.f64 + rope_entry(grp, t, h, w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs[i] = tab[i];
+    }
+    for (int hd = lane >> 4; hd < H; hd += 4) {
+        const int64_t idx = (tok * H + hd) * 16 + grp;
+        uint4 v = x[idx];
+        if (video) {
+            v.x = rot_pair_f64(v.x, cs[0]);
+            v.y = rot_pair_f64(v.y, cs[1]);
+            v.z = rot_pair_f64(v.z, cs[2]);
+            v.w = rot_pair_f64(v.w, cs[3]);
+        }
+        y[idx] = v;
+    }
 }
 
 int launch_rope3d(const uint16_t* x, uint16_t* y, int64_t L, int H, const SegTable& st,
                   const RopeTables& rt, hipStream_t stream) {
-    const int64_t rows = L * H;
-    const int64_t blocks = (rows * 16 + 255) / 256;
-    hipLaunchKernelGGL(rope3d_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(y), rows, H, st, rt);
+    const int64_t blocks = (L + ROPE_NT / 64 - 1) / (ROPE_NT / 64);
+    hipLaunchKernelGGL(rope3d_kernel, dim3((unsigned)blocks), dim3(ROPE_NT), 0, stream,
+                       reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(y), L, H, st, rt);
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
 }
 
