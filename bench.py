@@ -402,12 +402,19 @@ def cpu_baseline(inp, cfg, sm):
     except Exception:
         cores = int(threads)
     log("cpu baseline: %.2f s for %.3e FLOP" % (dt, flops))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(flops / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
         "seconds": round(dt, 2),
+        "cpu_model": model,
         "sample": "numpy float64 oracle, head 0 of 16, query rows 0..8191 of 63,360, each over all 316,800 "
                   "allowed keys (%.2e algorithmic FLOP), timed including its per-head key dequantisation "
                   "and rotation" % flops,

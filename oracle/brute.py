@@ -111,11 +111,15 @@ def softmax_attend(qv, keys, vals, sm_scale):
     return o, mx + math.log(tot), p
 
 
-def seg_attn(q, k_new, v_new, new_segs, cache_k, cache_v, sm_scale, bf16_operands=True):
+def seg_attn(q, k_new, v_new, new_segs, cache_k, cache_v, sm_scale, bf16_operands=True, sel=None):
     """Brute-force segment-causal attention.
 
     q, k_new, v_new: nested lists [Ln][H][128] of floats (bf16 values, q/k
     pre-RoPE).  cache_k, cache_v: nested lists [H][Lc] of (codes, scale) rows.
+    sel: None (every segment sees the whole cache) or, per new segment, a list
+    of (start, end) cache-token ranges it may see (huaweicloud blog, section
+    2.2 and the section 3.5 table; comfyui-wiki, 单张 4090 配置: the history a
+    segment looks at is a chosen subset of the earlier frames).
     Returns out [Ln][H][128], lse [H][Ln], probs [H][Ln][keys]."""
     Ln, H = len(q), len(q[0])
     pos = positions(new_segs)
@@ -141,7 +145,9 @@ def seg_attn(q, k_new, v_new, new_segs, cache_k, cache_v, sm_scale, bf16_operand
         for i in range(Ln):
             a = next(n for n, e in enumerate(ends) if i < e)
             qv = [rnd(v) for v in rope_vec(q[i][h], pos[i])]
-            o, l, p = softmax_attend(qv, Kc + Kn[:ends[a]], Vc + Vn[:ends[a]], sm_scale)
+            seen = range(len(Kc)) if sel is None else [j for (lo, hi) in sel[a] for j in range(lo, hi)]
+            o, l, p = softmax_attend(qv, [Kc[j] for j in seen] + Kn[:ends[a]], [Vc[j] for j in seen] + Vn[:ends[a]],
+                                     sm_scale)
             out[i][h], lse[h][i], probs[h][i] = o, l, p
     return out, lse, probs
 

@@ -241,12 +241,21 @@ def attend(qr, K, V, sm_scale):
 
 
 def seg_attn(q_bits, k_new_bits, v_new_bits, new_segs, k_codes, v_codes, k_scale, v_scale,
-             cache_len, sm_scale, rows=None, heads=None, bf16_operands=True, block=None):
+             cache_len, sm_scale, rows=None, heads=None, bf16_operands=True, block=None, sel=None):
     """Segment-causal attention of the new tokens.
 
     Query i of new segment a attends to every cached token (the INT8 history of
     all earlier segments) and to the new tokens of segments 0..a (bidirectional
     inside its own segment, never to a later segment).
+
+    sel (history selection): None, or per new segment a list of (start, end)
+    ranges of cache tokens; segment a then attends to the cache tokens in its
+    ranges instead of the whole cache.  The pages let the history a segment
+    looks at be a chosen subset of the earlier frames: the most recent latent
+    frames or frames sampled by temporal_context ([HW] section 3.5 table;
+    [CW] 单张 4090 配置), chosen by the kind of action ([HW] section 2.2).
+    Reading: the caller names the cache tokens; the allowed set is their
+    union with the new tokens of segments 0..a.
 
     q, k_new, v_new: bf16 bits [Ln][H][128]; q and k_new are pre-RoPE.
     k_codes, v_codes: int8 [H][cap][128]; k_scale, v_scale: float32 [H][cap];
@@ -278,13 +287,19 @@ def seg_attn(q_bits, k_new_bits, v_new_bits, new_segs, k_codes, v_codes, k_scale
         qs = bf16_bits_to_f64(q[rows, h:h + 1, :])
         Qr = rnd(rope3d_pos(qs, *(p[rows] for p in pos)))[:, 0, :]
         for a in np.unique(seg_of):
-            sel = np.nonzero(seg_of == a)[0]
+            mine = np.nonzero(seg_of == a)[0]
             e = int(ends[a])
-            K = np.concatenate([Kc, Kn[:e]])
-            V = np.concatenate([Vc, Vn[:e]])
+            if sel is None:
+                Ka, Va = Kc, Vc
+            else:
+                idx = np.array([j for (lo, hi) in sel[a] for j in range(int(lo), int(hi))], dtype=np.int64)
+                assert len(idx) == 0 or (idx.min() >= 0 and idx.max() < Lc), "selection outside the cache"
+                Ka, Va = Kc[idx], Vc[idx]
+            K = np.concatenate([Ka, Kn[:e]])
+            V = np.concatenate([Va, Vn[:e]])
             blk = block or int(max(8, min(256, (1 << 24) // max(1, len(K)))))
-            for lo in range(0, len(sel), blk):
-                r = sel[lo:lo + blk]
+            for lo in range(0, len(mine), blk):
+                r = mine[lo:lo + blk]
                 o, l = attend(Qr[r], K, V, sm_scale)
                 out[r, hi] = o
                 lse[hi, r] = l

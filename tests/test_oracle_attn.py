@@ -186,3 +186,75 @@ def test_rows_and_heads_subsets_agree_with_full_run():
     o2, l2 = run(c, rows=rows, heads=[1])
     np.testing.assert_array_equal(o2[:, 0], out[rows, 1])
     np.testing.assert_array_equal(l2[0], lse[1, rows])
+
+
+# ----------------------------------------------------------------------------
+# history selection (huaweicloud blog, section 2.2 and the section 3.5 table;
+# comfyui-wiki, 单张 4090 配置: a segment attends to a chosen subset of the
+# earlier frames)
+
+SEL_THREE = [[(0, 10), (30, 64)], [(5, 20)]]      # "three" mode: new segments 1 and 2
+
+
+def test_selection_matches_brute_force():
+    """Different selections per segment (three-segment mode) against the
+    pure-Python brute force that gathers the selected cache rows itself."""
+    c = tiny_case("three")
+    out, lse = run(c, sel=SEL_THREE)
+    f = lambda b: oracle.bf16_bits_to_f64(b).tolist()
+    H = 2
+    cache_k = [[(c["kc"][h, j].astype(int).tolist(), float(c["ks"][h, j])) for j in range(c["Lc"])] for h in range(H)]
+    cache_v = [[(c["vc"][h, j].astype(int).tolist(), float(c["vs"][h, j])) for j in range(c["Lc"])] for h in range(H)]
+    ob, lb, pb = brute.seg_attn(f(c["q"]), f(c["k"]), f(c["v"]), c["segs"], cache_k, cache_v, SM, sel=SEL_THREE)
+    np.testing.assert_allclose(out, np.array(ob), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lb), rtol=0, atol=1e-12)
+    # segment 1 rows see 10 + 34 cache keys and 64 new ones; segment 2 rows 15 + 128
+    assert len(pb[0][0]) == 44 + 64 and len(pb[0][64]) == 15 + 128
+
+
+def test_whole_cache_selection_is_no_selection():
+    c = tiny_case("three")
+    out0, lse0 = run(c)
+    out1, lse1 = run(c, sel=[[(0, 64)], [(0, 30), (30, 64)]])
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+def test_window_selection_is_the_sliced_cache():
+    """A contiguous window of the cache gives exactly the result of a cache
+    holding only that window."""
+    c = tiny_case("cache")
+    out1, lse1 = run(c, sel=[[(20, 52)]])
+    c2 = dict(c, kc=np.ascontiguousarray(c["kc"][:, 20:52]), vc=np.ascontiguousarray(c["vc"][:, 20:52]),
+              ks=np.ascontiguousarray(c["ks"][:, 20:52]), vs=np.ascontiguousarray(c["vs"][:, 20:52]), Lc=32)
+    out2, lse2 = run(c2)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_empty_selection_is_no_cache():
+    c = tiny_case("cache")
+    out1, lse1 = run(c, sel=[[]])
+    out2, lse2 = run(dict(c, Lc=0))
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_unselected_cache_rows_do_not_matter():
+    """Changing every cache row outside the selection leaves outputs and lse
+    bit-identical."""
+    c = tiny_case("three")
+    out0, lse0 = run(c, sel=SEL_THREE)
+    keep = np.zeros(64, bool)
+    for rng_list in SEL_THREE:
+        for lo, hi in rng_list:
+            keep[lo:hi] = True
+    rng = np.random.default_rng(3)
+    c2 = dict(c)
+    for name in ("kc", "vc"):
+        a = c[name].copy()
+        a[:, ~keep] = rng.integers(-127, 128, size=a[:, ~keep].shape, dtype=np.int8)
+        c2[name] = a
+    for name in ("ks", "vs"):
+        a = c[name].copy()
+        a[:, ~keep] = np.float32(5.0)
+        c2[name] = a
+    out1, lse1 = run(c2, sel=SEL_THREE)
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
