@@ -92,7 +92,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: the library has no multi-GPU path "
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
@@ -230,6 +230,9 @@ def workloads():
                   cam_xattn (72 camera tokens), rope3d and kv_quant_append, each
                   the median of 5 calls, the HBM-bound ones in GB/s of
                   algorithmic bytes
+      fullcache-sel18  the full-cache shape attending to 18 of the 288 cached
+                  latent frames (the last of every 16) through the history
+                  selection, plus its own 63,360 tokens (median of 5 calls)
       fullcache-h2  the full-cache shape with 2 heads: one GPU's share when the
                   16 heads are split over 8 GPUs (median of 5 calls)
     History caches are built on the GPU by rope3d + kv_quant_append (bit-exact
@@ -359,13 +362,29 @@ def workloads():
         del q, k, v, qc, out, oc, kr, ws
     del cache
 
-    # ---- fullcache-h2: one GPU's share of the full-cache shape
-    log("workload fullcache-h2: one GPU's share of the full-cache shape")
+    # ---- fullcache-sel18 and fullcache-h2 share the full-cache inputs
+    log("workload fullcache-sel18 / fullcache-h2: generating the full-cache inputs")
     cfg = synth.CONFIGS[4]
-    H = 2
     inp = synth.layer_inputs(4)
     (seg,) = cfg.new_segs
     (hseg,) = cfg.hist_segs
+    frame = hseg.Hg * hseg.Wg
+    # history selection: 18 of the 288 cached latent frames, the last of every 16
+    sel = [[(f * frame, (f + 1) * frame) for f in range(15, hseg.T, 16)]]
+    nsel = sum(hi - lo for lo, hi in sel[0])
+    cache = build_cache(inp["k_hist"], inp["v_hist"], [hseg], cfg.H, cfg.Lc)
+    q, k, v = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])
+    out = torch.empty_like(q)
+    ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H, sel=sel), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
+                                      stream=stream, sel=sel), 5)
+    attn_line("fullcache-sel18", ms, cfg.H, cfg.Lq, nsel + cfg.Lq,
+              dict(cache_tokens=cfg.Lc, selected_frames=len(sel[0]), selected_tokens=nsel))
+    del q, k, v, out, ws, cache
+
+    # ---- fullcache-h2: one GPU's share of the full-cache shape
+    log("workload fullcache-h2: one GPU's share of the full-cache shape")
+    H = 2
     sub = lambda a: np.ascontiguousarray(a[:, :H])
     cache = build_cache(sub(inp["k_hist"]), sub(inp["v_hist"]), [hseg], H, cfg.Lc)
     q, k, v = d16(sub(inp["q"])), d16(sub(inp["k_new"])), d16(sub(inp["v_new"]))

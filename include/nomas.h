@@ -77,6 +77,7 @@ enum {
 #define NOMAS_MAX_CACHE (1 << 24)  /* nomas_seg_attn: cache capacity (tokens)  */
 #define NOMAS_MAX_TOKEN_HEADS (1 << 23)  /* nomas_seg_attn: new tokens x heads */
 #define NOMAS_MAX_SPLIT 4          /* nomas_seg_attn: key-range parts per query tile */
+#define NOMAS_MAX_SEL_RANGES 64    /* nomas_seg_attn_sel: cache-token ranges per call */
 
 /*
  * 3D RoPE (comfyui-wiki news, 模型内部: axes [16, 56, 56], theta 256).
@@ -146,6 +147,44 @@ int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf1
                    int64_t cap, int64_t cache_len, int H, float sm_scale,
                    nomas_bf16* out, float* lse, int n_split, void* workspace, int64_t workspace_bytes,
                    void* stream);
+
+/*
+ * nomas_seg_attn with a history selection: each new segment attends to a
+ * chosen subset of the cached tokens instead of the whole cache.  The pages
+ * let a segment look at a subset of the earlier frames: the most recent latent
+ * frames or frames sampled by temporal_context (huaweicloud blog, section 3.5
+ * table; comfyui-wiki news, 单张 4090 配置), chosen by the kind of action
+ * (huaweicloud blog, section 2.2).  The caller names the cache tokens:
+ * sel_off: host, n_new_segs + 1 non-decreasing int32 offsets, sel_off[0] = 0;
+ *   segment a uses ranges sel_off[a] .. sel_off[a+1]-1.
+ * sel_ranges: host, int64 pairs (start, end) of cache tokens, 0 <= start <
+ *   end <= cache_len, sorted and non-overlapping within a segment (NULL
+ *   allowed when there are no ranges).  A segment with no ranges sees no
+ *   cached token.  sel_off == NULL: every segment sees the whole cache, i.e.
+ *   nomas_seg_attn.
+ * Query i of segment a then attends to its selected cache tokens and to the
+ * new tokens of segments 0..a.  Segments with identical lists share packed
+ * key tiles; otherwise each segment's keys are packed separately, which the
+ * workspace size accounts for.  Other arguments, the workspace and the errors
+ * are those of nomas_seg_attn; an invalid selection gives NOMAS_EINVAL, more
+ * than NOMAS_MAX_SEL_RANGES ranges NOMAS_EUNSUPPORTED.
+ */
+int nomas_seg_attn_sel(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,
+                       const nomas_seg* new_segs, int n_new_segs,
+                       const int8_t* k_codes, const int8_t* v_codes,
+                       const float* k_scale, const float* v_scale,
+                       int64_t cap, int64_t cache_len,
+                       const int32_t* sel_off, const int64_t* sel_ranges,
+                       int H, float sm_scale,
+                       nomas_bf16* out, float* lse, int n_split, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Workspace bytes nomas_seg_attn_sel needs (same selection arguments), or a
+ * negative error code.  Host only.
+ */
+int64_t nomas_seg_attn_sel_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len,
+                                     const int32_t* sel_off, const int64_t* sel_ranges, int H, int n_split);
 
 /*
  * Workspace bytes nomas_seg_attn needs for these new segments, cache length,

@@ -6,7 +6,8 @@ this package only marshals arguments.  Build it with
 ``python -m segment_causal_attention_amd.build`` (or __graft_entry__.build()).
 """
 from ._lib import (  # noqa: F401
-    EHIP, ECAPACITY, EINVAL, EUNSUPPORTED, HEAD_DIM, MAX_CAM, MAX_SEGS, MAX_SPLIT, OK, SM_SCALE, SYMBOLS,
+    EHIP, ECAPACITY, EINVAL, EUNSUPPORTED, HEAD_DIM, MAX_CAM, MAX_SEGS, MAX_SEL_RANGES, MAX_SPLIT, OK, SM_SCALE,
+    SYMBOLS,
     NomasError, Seg, cam_tokens, cam_xattn, kv_quant_append, lib, rope3d, rope_table, seg_array,
-    seg_attn, seg_attn_workspace, seg_tokens, strerror, version,
+    seg_attn, seg_attn_workspace, seg_tokens, sel_arrays, strerror, version,
 )

@@ -21,9 +21,11 @@ HEAD_DIM = 128
 MAX_SEGS = 64
 MAX_CAM = 128
 MAX_SPLIT = 4
+MAX_SEL_RANGES = 64
 SM_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
 SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_workspace",
+           "nomas_seg_attn_sel", "nomas_seg_attn_sel_workspace",
            "nomas_cam_tokens", "nomas_cam_xattn", "nomas_rope_table", "nomas_strerror", "nomas_version")
 
 
@@ -59,6 +61,10 @@ def lib() -> ctypes.CDLL:
                                      _P, _P, _I, _P, _I64, _P]
         L.nomas_seg_attn_workspace.argtypes = [ctypes.POINTER(Seg), _I, _I64, _I, _I]
         L.nomas_seg_attn_workspace.restype = _I64
+        L.nomas_seg_attn_sel.argtypes = [_P, _P, _P, ctypes.POINTER(Seg), _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _I,
+                                         _F, _P, _P, _I, _P, _I64, _P]
+        L.nomas_seg_attn_sel_workspace.argtypes = [ctypes.POINTER(Seg), _I, _I64, _P, _P, _I, _I]
+        L.nomas_seg_attn_sel_workspace.restype = _I64
         L.nomas_cam_tokens.argtypes = [_P, _I, _D, _D, _P]
         L.nomas_cam_xattn.argtypes = [_P, _I64, _I, _P, _I, _P, _P, _F, _P, _P]
         L.nomas_rope_table.argtypes = [_I, _I, _P, _P]
@@ -66,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.nomas_strerror.restype = ctypes.c_char_p
         L.nomas_version.argtypes = []
         L.nomas_version.restype = ctypes.c_char_p
-        for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_cam_tokens",
+        for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_sel", "nomas_cam_tokens",
                      "nomas_cam_xattn", "nomas_rope_table"):
             getattr(L, name).restype = _I
         _lib = L
@@ -163,10 +169,29 @@ def kv_quant_append(k_rot, v, k_codes, v_codes, k_scale, v_scale, length: int, s
     return int(ln.value)
 
 
-def seg_attn_workspace(new_segs, cache_len: int, H: int, n_split: int = 0) -> int:
+def sel_arrays(sel, n_segs):
+    """History selection -> (sel_off int32 [n+1], sel_ranges int64 [2r]) host
+    arrays; sel is one list of (start, end) cache-token ranges per segment."""
+    if len(sel) != n_segs:
+        raise ValueError("sel needs one range list per new segment (%d), got %d" % (n_segs, len(sel)))
+    off = np.zeros(n_segs + 1, np.int32)
+    flat = []
+    for a, ranges in enumerate(sel):
+        for lo, hi in ranges:
+            flat += [int(lo), int(hi)]
+        off[a + 1] = len(flat) // 2
+    return off, np.array(flat if flat else [0, 0], np.int64)
+
+
+def seg_attn_workspace(new_segs, cache_len: int, H: int, n_split: int = 0, sel=None) -> int:
     """Bytes of device workspace seg_attn needs on the current device (host only)."""
     arr, n = seg_array(new_segs)
-    nbytes = lib().nomas_seg_attn_workspace(arr, n, int(cache_len), int(H), int(n_split))
+    if sel is None:
+        nbytes = lib().nomas_seg_attn_workspace(arr, n, int(cache_len), int(H), int(n_split))
+    else:
+        off, rng = sel_arrays(sel, n)
+        nbytes = lib().nomas_seg_attn_sel_workspace(arr, n, int(cache_len), off.ctypes.data, rng.ctypes.data, int(H),
+                                                    int(n_split))
     if nbytes < 0:
         raise NomasError(int(nbytes), "nomas_seg_attn_workspace")
     return int(nbytes)
@@ -174,12 +199,13 @@ def seg_attn_workspace(new_segs, cache_len: int, H: int, n_split: int = 0) -> in
 
 def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None, v_scale=None,
              cache_len: int = 0, sm_scale: float = SM_SCALE, out=None, lse=None, workspace=None, n_split: int = 0,
-             stream=None):
+             stream=None, sel=None):
     """Segment-causal attention; returns out [Ln][H][128] bf16 (lse filled if given).
     q and k_new are taken before RoPE (rotated inside).  workspace:
     a device uint8 tensor of at least seg_attn_workspace(...) bytes, allocated
     here when not given.  n_split: 0 = the library's choice of key-range parts,
-    1..4 forces that many."""
+    1..4 forces that many.  sel: None (whole cache) or, per new segment, a
+    list of (start, end) cache-token ranges it may see (nomas_seg_attn_sel)."""
     import torch
     Ln, H = q.shape[0], q.shape[1]
     shp = (seg_tokens(new_segs), H, HEAD_DIM)
@@ -200,17 +226,25 @@ def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
     _dev(out, "out", shp)
     if lse is not None:
         _dev(lse, "lse", (H, Ln), 4)
-    need = seg_attn_workspace(new_segs, cache_len, H, n_split)
+    need = seg_attn_workspace(new_segs, cache_len, H, n_split, sel)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device uint8 tensor")
     arr, n = seg_array(new_segs)
-    _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_new), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
-                                _ptr(k_scale), _ptr(v_scale), cap, int(cache_len), H, float(sm_scale),
-                                _ptr(out), _ptr(lse), int(n_split), _ptr(workspace), workspace.numel(),
-                                _stream(stream)),
-           "nomas_seg_attn")
+    if sel is None:
+        _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_new), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
+                                    _ptr(k_scale), _ptr(v_scale), cap, int(cache_len), H, float(sm_scale),
+                                    _ptr(out), _ptr(lse), int(n_split), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)),
+               "nomas_seg_attn")
+    else:
+        off, rng = sel_arrays(sel, n)
+        _check(lib().nomas_seg_attn_sel(_ptr(q), _ptr(k_new), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
+                                        _ptr(k_scale), _ptr(v_scale), cap, int(cache_len), off.ctypes.data,
+                                        rng.ctypes.data, H, float(sm_scale), _ptr(out), _ptr(lse), int(n_split),
+                                        _ptr(workspace), workspace.numel(), _stream(stream)),
+               "nomas_seg_attn_sel")
     return out
 
 

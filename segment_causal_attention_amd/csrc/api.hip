@@ -15,9 +15,10 @@ int launch_rope3d(const uint16_t* x, uint16_t* y, int64_t L, int H, const SegTab
                   hipStream_t stream);
 int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const SegTable& segs, int Ln,
                     const int8_t* kc, const int8_t* vc, const float* ks, const float* vs, int64_t cap, int Lc,
-                    int H, float sm_scale, uint16_t* out, float* lse, int n_split, void* workspace,
-                    const RopeTables& rt, hipStream_t stream);
-int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int n_split);
+                    const int32_t* sel_off, const int64_t* sel_ranges, int H, float sm_scale, uint16_t* out,
+                    float* lse, int n_split, void* workspace, const RopeTables& rt, hipStream_t stream);
+int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int n_split, const int32_t* sel_off,
+                                 const int64_t* sel_ranges);
 int launch_cam_xattn(const uint16_t* q, int64_t Lq, int H, const float* cam, int Nc, const uint16_t* wk,
                      const uint16_t* wv, float sm_scale, uint16_t* out, hipStream_t stream);
 }  // namespace nomas
@@ -164,8 +165,8 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
     return rc;
 }
 
-int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len, int H,
-                                 int n_split) {
+int64_t nomas_seg_attn_sel_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len,
+                                     const int32_t* sel_off, const int64_t* sel_ranges, int H, int n_split) {
     if (H < 1 || cache_len < 0 || n_split < 0) return NOMAS_EINVAL;
     if (n_split > NOMAS_MAX_SPLIT) return NOMAS_EUNSUPPORTED;
     if (H > kMaxHeads || cache_len > NOMAS_MAX_CACHE) return NOMAS_EUNSUPPORTED;
@@ -174,14 +175,19 @@ int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int6
     int rc = build_segs(new_segs, n_new_segs, &st, &Ln);
     if (rc != NOMAS_OK) return rc;
     if (Ln * H > NOMAS_MAX_TOKEN_HEADS) return NOMAS_EUNSUPPORTED;
-    return seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, n_split);
+    return seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, n_split, sel_off, sel_ranges);
 }
 
-int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,
-                   const nomas_seg* new_segs, int n_new_segs, const int8_t* k_codes, const int8_t* v_codes,
-                   const float* k_scale, const float* v_scale, int64_t cap, int64_t cache_len, int H,
-                   float sm_scale, nomas_bf16* out, float* lse, int n_split, void* workspace,
-                   int64_t workspace_bytes, void* stream) {
+int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len, int H,
+                                 int n_split) {
+    return nomas_seg_attn_sel_workspace(new_segs, n_new_segs, cache_len, nullptr, nullptr, H, n_split);
+}
+
+int nomas_seg_attn_sel(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,
+                       const nomas_seg* new_segs, int n_new_segs, const int8_t* k_codes, const int8_t* v_codes,
+                       const float* k_scale, const float* v_scale, int64_t cap, int64_t cache_len,
+                       const int32_t* sel_off, const int64_t* sel_ranges, int H, float sm_scale, nomas_bf16* out,
+                       float* lse, int n_split, void* workspace, int64_t workspace_bytes, void* stream) {
     if (!q || !k_new || !v_new || !out || H < 1 || !finite_pos(sm_scale) || n_split < 0) return NOMAS_EINVAL;
     if (n_split > NOMAS_MAX_SPLIT) return NOMAS_EUNSUPPORTED;
     if (!al16(q) || !al16(k_new) || !al16(v_new) || !al16(out) || (lse && !al4(lse))) return NOMAS_EINVAL;
@@ -195,14 +201,26 @@ int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf1
     int64_t Ln = 0;
     int rc = build_segs(new_segs, n_new_segs, &st, &Ln);
     if (rc != NOMAS_OK) return rc;
-    if (Ln == 0) return NOMAS_OK;
     if (cap > NOMAS_MAX_CACHE || Ln * H > NOMAS_MAX_TOKEN_HEADS) return NOMAS_EUNSUPPORTED;
-    const int64_t need = seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, n_split);
+    // the selection is checked (and the workspace sized) before anything else is looked at on the device
+    const int64_t need = seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, n_split, sel_off, sel_ranges);
+    if (need < 0) return (int)need;
+    if (Ln == 0) return NOMAS_OK;
     if (!workspace || !al16(workspace) || workspace_bytes < need) return NOMAS_EINVAL;
     RopeTables rt;
     if ((rc = rope_tables(&rt)) != NOMAS_OK) return rc;
-    return launch_seg_attn(q, k_new, v_new, st, (int)Ln, k_codes, v_codes, k_scale, v_scale, cap, (int)cache_len, H,
-                           sm_scale, out, lse, n_split, workspace, rt, (hipStream_t)stream);
+    return launch_seg_attn(q, k_new, v_new, st, (int)Ln, k_codes, v_codes, k_scale, v_scale, cap, (int)cache_len,
+                           sel_off, sel_ranges, H, sm_scale, out, lse, n_split, workspace, rt, (hipStream_t)stream);
+}
+
+int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,
+                   const nomas_seg* new_segs, int n_new_segs, const int8_t* k_codes, const int8_t* v_codes,
+                   const float* k_scale, const float* v_scale, int64_t cap, int64_t cache_len, int H,
+                   float sm_scale, nomas_bf16* out, float* lse, int n_split, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+    return nomas_seg_attn_sel(q, k_new, v_new, new_segs, n_new_segs, k_codes, v_codes, k_scale, v_scale, cap,
+                              cache_len, nullptr, nullptr, H, sm_scale, out, lse, n_split, workspace,
+                              workspace_bytes, stream);
 }
 
 int nomas_cam_tokens(const double* c2w, int n_frames, double translation_scale, double rotation_scale,

@@ -44,6 +44,7 @@
 // rescale: O and the sum are rescaled only when a row's max grows by more
 // than 8 (a factor 256), which keeps every exponent bounded.
 #include <algorithm>
+#include <cstring>
 
 #include "common.hpp"
 
@@ -85,6 +86,22 @@ __device__ __forceinline__ float i8(uint32_t word, int byte) {
 // x - Lc for x < Lc + Ln (its key rotated by 3D RoPE in float64 and rounded
 // once to bf16), and zero beyond.
 
+// The packed key ranges.  Region r holds nsel[r] selected cache tokens (the
+// ranges rng0[r] .. rng0[r+1]-1 of the range table, in order) followed by
+// the new tokens [0, nnew[r]), and starts at tile tile0[r] of a head's
+// images.  Without a history selection there is one region: the whole cache,
+// then every new token.  Segments that see different cache tokens get
+// regions of their own.
+struct KeyPlan {
+    int32_t nreg;
+    int32_t tile0[NOMAS_MAX_SEGS + 1];          // tile0[nreg]: tiles per head
+    int32_t nsel[NOMAS_MAX_SEGS];
+    int32_t nnew[NOMAS_MAX_SEGS];
+    int32_t rng0[NOMAS_MAX_SEGS + 1];
+    int32_t rstart[NOMAS_MAX_SEL_RANGES];       // cache token of the range's first key
+    int32_t rkey0[NOMAS_MAX_SEL_RANGES];        // packed key (within the region) of that token
+};
+
 struct PackArgs {
     const int8_t* kc;
     const int8_t* vc;
@@ -95,28 +112,45 @@ struct PackArgs {
     uint8_t* img;
     float* knorm;                   // [H][ntk]: largest squared key norm of each tile
     int64_t cap;
-    int32_t Lc, Ln, H, ntk;         // ntk: tiles per head
+    int32_t H, ntk;                 // ntk: tiles per head
+    KeyPlan kp;
     SegTable segs;                  // the new segments (positions of the new keys)
     RopeTables rt;
 };
+static_assert(sizeof(PackArgs) <= 4000, "kernel arguments are passed by value");
+
+// Where packed key x of region r comes from: a cache token, a new token, or
+// neither (zero padding past the region's end).
+struct KeySrc {
+    int32_t cache, fresh;
+};
+__device__ __forceinline__ KeySrc key_source(const KeyPlan& kp, int r, int x) {
+    if (x < kp.nsel[r]) {
+        int j = kp.rng0[r];
+        while (j + 1 < kp.rng0[r + 1] && kp.rkey0[j + 1] <= x) ++j;
+        return {kp.rstart[j] + (x - kp.rkey0[j]), -1};
+    }
+    x -= kp.nsel[r];
+    return {-1, x < kp.nnew[r] ? x : -1};
+}
 
 constexpr int PACK_NT = 256;
 
-// the 8 bf16 values of channels 8j .. 8j+7 of packed key x (as 4 words)
-__device__ __forceinline__ uint4 key_chunk(const PackArgs& P, int h, int x, int j, bool is_v) {
-    if (x < P.Lc) {
-        const size_t row = (size_t)h * P.cap + x;
+// the 8 bf16 values of channels 8j .. 8j+7 of a packed key (as 4 words)
+__device__ __forceinline__ uint4 key_chunk(const PackArgs& P, int h, KeySrc x, int j, bool is_v) {
+    if (x.cache >= 0) {
+        const size_t row = (size_t)h * P.cap + x.cache;
         const int8_t* codes = (is_v ? P.vc : P.kc) + row * D + 8 * j;
         const float s = (is_v ? P.vs : P.ks)[row];
         const uint2 w = *reinterpret_cast<const uint2*>(codes);
         return make_uint4(pack_bf16(i8(w.x, 0) * s, i8(w.x, 1) * s), pack_bf16(i8(w.x, 2) * s, i8(w.x, 3) * s),
                           pack_bf16(i8(w.y, 0) * s, i8(w.y, 1) * s), pack_bf16(i8(w.y, 2) * s, i8(w.y, 3) * s));
     }
-    if (x < P.Lc + P.Ln) {
-        const uint16_t* src = (is_v ? P.v : P.k) + ((size_t)(x - P.Lc) * P.H + h) * D + 8 * j;
+    if (x.fresh >= 0) {
+        const uint16_t* src = (is_v ? P.v : P.k) + ((size_t)x.fresh * P.H + h) * D + 8 * j;
         const uint4 w = *reinterpret_cast<const uint4*>(src);
         // new keys are rotated here exactly as nomas_rope3d rotates them
-        return is_v ? w : rope_chunk_f64(w, j, x - P.Lc, P.segs, P.rt);
+        return is_v ? w : rope_chunk_f64(w, j, x.fresh, P.segs, P.rt);
     }
     return make_uint4(0, 0, 0, 0);
 }
@@ -125,7 +159,9 @@ __global__ __launch_bounds__(PACK_NT) void pack_kernel(const PackArgs P) {
     __shared__ __attribute__((aligned(16))) uint16_t vt[D * VSTR];     // the V^T image
     __shared__ uint32_t kmax;       // bits of the largest squared key norm (non-negative floats order as integers)
     const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-    const int x0 = t * BN;
+    int r = 0;
+    while (r + 1 < P.kp.nreg && P.kp.tile0[r + 1] <= t) ++r;
+    const int x0 = (t - P.kp.tile0[r]) * BN;
     uint8_t* img = P.img + ((size_t)h * P.ntk + t) * TILE_BYTES;
     if (tid == 0) kmax = 0;
     __syncthreads();
@@ -136,8 +172,9 @@ __global__ __launch_bounds__(PACK_NT) void pack_kernel(const PackArgs P) {
     {
         const int key = tid >> 2, qd = tid & 3;
         uint4 w[4];
+        const KeySrc src = key_source(P.kp, r, x0 + key);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = key_chunk(P, h, x0 + key, 4 * qd + j, false);
+        for (int j = 0; j < 4; ++j) w[j] = key_chunk(P, h, src, 4 * qd + j, false);
         float n2 = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -163,9 +200,9 @@ __global__ __launch_bounds__(PACK_NT) void pack_kernel(const PackArgs P) {
     // permutation), consecutive lanes on consecutive words
     {
         const int kp = tid & 31, cg = tid >> 5;
-        const uint4 a[2] = {key_chunk(P, h, x0 + 2 * kp, 2 * cg, true), key_chunk(P, h, x0 + 2 * kp, 2 * cg + 1, true)};
-        const uint4 b[2] = {key_chunk(P, h, x0 + 2 * kp + 1, 2 * cg, true),
-                            key_chunk(P, h, x0 + 2 * kp + 1, 2 * cg + 1, true)};
+        const KeySrc sa = key_source(P.kp, r, x0 + 2 * kp), sb = key_source(P.kp, r, x0 + 2 * kp + 1);
+        const uint4 a[2] = {key_chunk(P, h, sa, 2 * cg, true), key_chunk(P, h, sa, 2 * cg + 1, true)};
+        const uint4 b[2] = {key_chunk(P, h, sb, 2 * cg, true), key_chunk(P, h, sb, 2 * cg + 1, true)};
         uint32_t* col = reinterpret_cast<uint32_t*>(vt + vperm_key(2 * kp));
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -193,13 +230,16 @@ struct AttnArgs {
     float* lse;
     float* po;                      // split > 1: partial outputs O/l [split][Ln][H][128] fp32
     float* plse;                    //            partial log2-sum-exp [split][H][Ln]
-    int32_t Lc, Ln, H, ntq, ntk;    // ntq: query tiles per head, ntk: key tiles per head
+    int32_t Ln, H, ntq, ntk;        // ntq: query tiles per head, ntk: key tiles per head
     int32_t nsplit;                 // key-range parts per query tile
     float scale_log2;               // sm_scale * log2(e)
     int32_t tile0[NOMAS_MAX_SEGS + 1];   // first query tile of each new segment
+    int32_t ktile0[NOMAS_MAX_SEGS];      // first key tile (of a head's images) of each segment's region
+    int32_t nsel[NOMAS_MAX_SEGS];        // cache tokens each segment sees (its region's first keys)
     SegTable segs;
     RopeTables rt;
 };
+static_assert(sizeof(AttnArgs) <= 4000, "kernel arguments are passed by value");
 
 // One kilobyte of a tile image into LDS: lane l's 16 bytes, read at byte
 // voff + soff of the resource, land at LDS byte m0 + 16 l.  Written as inline
@@ -419,7 +459,8 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
 
     // keys [0, nkeys) of the packed range are allowed: the cache and the new
     // tokens up to the end of this segment
-    const int nkeys = __builtin_amdgcn_readfirstlane(A.Lc + kend);
+    const int nkeys = __builtin_amdgcn_readfirstlane(A.nsel[a] + kend);
+    const int64_t kbase = (int64_t)head * A.ntk + A.ktile0[a];    // this segment's region of the images
     const int nt_all = (nkeys + BN - 1) / BN;
     // this workgroup's part of the key tiles: [t0, t0 + nt)
     const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * nt_all / A.nsplit));
@@ -432,9 +473,9 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
         // image) in a last, partial tile
         const int nfull = nt > 0 ? min(nt, (nkeys - t0 * BN) / BN) : 0;    // t0 * BN < nkeys when nt > 0
         float k2 = 0.0f;
-        for (int t = tid; t < nfull; t += NT) k2 = fmaxf(k2, A.knorm[(int64_t)head * A.ntk + t0 + t]);
+        for (int t = tid; t < nfull; t += NT) k2 = fmaxf(k2, A.knorm[kbase + t0 + t]);
         if (nfull < nt && tid < nkeys - (t0 + nfull) * BN)
-            k2 = fmaxf(k2, *reinterpret_cast<const float*>(A.img + ((int64_t)head * A.ntk + t0 + nfull) * TILE_BYTES +
+            k2 = fmaxf(k2, *reinterpret_cast<const float*>(A.img + (kbase + t0 + nfull) * TILE_BYTES +
                                                            tid * KSTR * 2 + 2 * D));
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, off));
@@ -443,7 +484,7 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
 
     // ---- tile copies: wave w copies kilobytes w, w+8, ... of each image
     const int wv = __builtin_amdgcn_readfirstlane(wave) & (NW - 1);
-    const uint64_t hbase = (uint64_t)(uintptr_t)A.img + (uint64_t)head * A.ntk * TILE_BYTES;
+    const uint64_t hbase = (uint64_t)(uintptr_t)A.img + (uint64_t)kbase * TILE_BYTES;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     const uint32_t lane16 = 16u * lane;
     auto copy_tile = [&](int tile, int b) {
@@ -614,8 +655,6 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs M) {
 // ---------------------------------------------------------------------------
 // Launch planning
 
-int seg_attn_workspace_tiles(int Lc, int Ln) { return (Lc + Ln + BN - 1) / BN; }
-
 int device_cu_count() {
     static int cache[64];
     int dev = 0;
@@ -628,11 +667,86 @@ int device_cu_count() {
     return cache[dev];
 }
 
+// Packed key regions of a call (see KeyPlan) and each segment's region.
+// sel_off == nullptr: one region, the whole cache then every new token.
+// Otherwise segment a sees the cache-token ranges sel_ranges[2i], [2i+1] for
+// i in [sel_off[a], sel_off[a+1]): sorted, non-overlapping, inside
+// [0, Lc).  Segments with identical lists share one region (holding every new
+// token); else each segment gets its own (its selection, then the new tokens
+// up to its end).  Returns NOMAS_OK, NOMAS_EINVAL or NOMAS_EUNSUPPORTED.
+int build_key_plan(const SegTable& segs, int Lc, int Ln, const int32_t* sel_off, const int64_t* sel_ranges,
+                   KeyPlan* kp, int32_t* seg_reg) {
+    std::memset(kp, 0, sizeof(*kp));
+    const int n = segs.n;
+    auto seg_end = [&](int a) {
+        const SegDev& d = segs.s[a];
+        return d.start + d.n_text + d.T * d.Hg * d.Wg;
+    };
+    auto finish = [&]() {
+        int64_t tiles = 0;
+        for (int r = 0; r < kp->nreg; ++r) {
+            kp->tile0[r] = (int32_t)tiles;
+            tiles += ((int64_t)kp->nsel[r] + kp->nnew[r] + BN - 1) / BN;
+        }
+        if (tiles >= ((int64_t)1 << 24)) return (int)NOMAS_EUNSUPPORTED;
+        kp->tile0[kp->nreg] = (int32_t)tiles;
+        return (int)NOMAS_OK;
+    };
+    if (!sel_off) {
+        kp->nreg = 1;
+        kp->nsel[0] = Lc;
+        kp->nnew[0] = Ln;
+        kp->rng0[0] = 0;
+        kp->rng0[1] = Lc > 0 ? 1 : 0;
+        kp->rstart[0] = 0;
+        kp->rkey0[0] = 0;
+        for (int a = 0; a < n; ++a) seg_reg[a] = 0;
+        return finish();
+    }
+    if (!sel_ranges && sel_off[n] > 0) return NOMAS_EINVAL;
+    if (sel_off[0] != 0) return NOMAS_EINVAL;
+    for (int a = 0; a < n; ++a)
+        if (sel_off[a + 1] < sel_off[a]) return NOMAS_EINVAL;
+    if (sel_off[n] > NOMAS_MAX_SEL_RANGES) return NOMAS_EUNSUPPORTED;
+    for (int a = 0; a < n; ++a) {
+        int64_t prev_end = 0;
+        for (int i = sel_off[a]; i < sel_off[a + 1]; ++i) {
+            const int64_t lo = sel_ranges[2 * i], hi = sel_ranges[2 * i + 1];
+            if (lo < prev_end || hi <= lo || hi > Lc) return NOMAS_EINVAL;
+            prev_end = hi;
+        }
+    }
+    bool same = true;
+    for (int a = 1; a < n && same; ++a) {
+        const int na = sel_off[a + 1] - sel_off[a];
+        if (na != sel_off[1] - sel_off[0]) { same = false; break; }
+        for (int i = 0; i < 2 * na; ++i)
+            if (sel_ranges[2 * sel_off[a] + i] != sel_ranges[2 * sel_off[0] + i]) { same = false; break; }
+    }
+    kp->nreg = same ? 1 : n;
+    int nr = 0;
+    for (int r = 0; r < kp->nreg; ++r) {
+        kp->rng0[r] = nr;
+        int32_t key = 0;
+        for (int i = sel_off[r]; i < sel_off[r + 1]; ++i) {
+            kp->rstart[nr] = (int32_t)sel_ranges[2 * i];
+            kp->rkey0[nr] = key;
+            key += (int32_t)(sel_ranges[2 * i + 1] - sel_ranges[2 * i]);
+            ++nr;
+        }
+        kp->nsel[r] = key;
+        kp->nnew[r] = same ? Ln : seg_end(r);
+    }
+    kp->rng0[kp->nreg] = nr;
+    for (int a = 0; a < n; ++a) seg_reg[a] = same ? 0 : a;
+    return finish();
+}
+
 // Key-range parts per query tile.  Forced when n_split > 0; otherwise the
 // count (1..4) that fills the last round of workgroups best, keeping every
 // part at 16 tiles or more: one workgroup per CU, so a grid of u units takes
 // ceil(u / CUs) rounds, each 1/parts as long.
-int plan_splits(const SegTable& segs, int Lc, int H, int n_split) {
+int plan_splits(const SegTable& segs, const KeyPlan& kp, const int32_t* seg_reg, int H, int n_split) {
     if (n_split > 0) return n_split;
     int nq = 0, nt_min = 1 << 30;
     for (int i = 0; i < segs.n; ++i) {
@@ -640,7 +754,7 @@ int plan_splits(const SegTable& segs, int Lc, int H, int n_split) {
         const int ntok = s.n_text + s.T * s.Hg * s.Wg;
         if (ntok == 0) continue;
         nq += (ntok + BM - 1) / BM;
-        nt_min = std::min(nt_min, (Lc + s.start + ntok + BN - 1) / BN);
+        nt_min = std::min(nt_min, (kp.nsel[seg_reg[i]] + s.start + ntok + BN - 1) / BN);
     }
     const int cus = device_cu_count();
     if (nq == 0 || cus <= 0) return 1;
@@ -657,9 +771,15 @@ int plan_splits(const SegTable& segs, int Lc, int H, int n_split) {
 // per-tile key norms follow the images, padded to 256 bytes
 static int64_t knorm_bytes(int64_t tiles) { return (tiles * 4 + 255) / 256 * 256; }
 
-int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int n_split) {
-    const int p = plan_splits(segs, Lc, H, n_split);
-    const int64_t tiles = (int64_t)H * seg_attn_workspace_tiles(Lc, Ln);
+// Workspace bytes, or a negative error code for an invalid selection.
+int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int n_split, const int32_t* sel_off,
+                                 const int64_t* sel_ranges) {
+    KeyPlan kp;
+    int32_t seg_reg[NOMAS_MAX_SEGS];
+    const int rc = build_key_plan(segs, Lc, Ln, sel_off, sel_ranges, &kp, seg_reg);
+    if (rc != NOMAS_OK) return rc;
+    const int p = plan_splits(segs, kp, seg_reg, H, n_split);
+    const int64_t tiles = (int64_t)H * kp.tile0[kp.nreg];
     int64_t b = tiles * TILE_BYTES + knorm_bytes(tiles);
     if (p > 1) b += (int64_t)p * Ln * H * (D + 1) * 4;
     return b;
@@ -667,23 +787,27 @@ int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, in
 
 int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const SegTable& segs,
                     int Ln, const int8_t* kc, const int8_t* vc, const float* ks, const float* vs,
-                    int64_t cap, int Lc, int H, float sm_scale, uint16_t* out, float* lse, int n_split,
-                    void* workspace, const RopeTables& rt, hipStream_t stream) {
-    const int nsplit = plan_splits(segs, Lc, H, n_split);
-    const int ntk = seg_attn_workspace_tiles(Lc, Ln);
+                    int64_t cap, int Lc, const int32_t* sel_off, const int64_t* sel_ranges, int H, float sm_scale,
+                    uint16_t* out, float* lse, int n_split, void* workspace, const RopeTables& rt,
+                    hipStream_t stream) {
     PackArgs P{};
+    int32_t seg_reg[NOMAS_MAX_SEGS];
+    const int rc = build_key_plan(segs, Lc, Ln, sel_off, sel_ranges, &P.kp, seg_reg);
+    if (rc != NOMAS_OK) return rc;
+    const int nsplit = plan_splits(segs, P.kp, seg_reg, H, n_split);
+    const int ntk = P.kp.tile0[P.kp.nreg];
     P.kc = kc; P.vc = vc; P.ks = ks; P.vs = vs;
     P.k = k; P.v = v;
     P.img = static_cast<uint8_t*>(workspace);
     P.knorm = reinterpret_cast<float*>(P.img + (int64_t)H * ntk * TILE_BYTES);
-    P.cap = cap; P.Lc = Lc; P.Ln = Ln; P.H = H; P.ntk = ntk;
+    P.cap = cap; P.H = H; P.ntk = ntk;
     P.segs = segs;
     P.rt = rt;
 
     AttnArgs A{};
     A.q = q; A.img = P.img; A.knorm = P.knorm;
     A.out = out; A.lse = lse;
-    A.Lc = Lc; A.Ln = Ln; A.H = H; A.ntk = ntk;
+    A.Ln = Ln; A.H = H; A.ntk = ntk;
     A.nsplit = nsplit;
     if (nsplit > 1) {
         A.po = reinterpret_cast<float*>(P.img + (int64_t)H * ntk * TILE_BYTES + knorm_bytes((int64_t)H * ntk));
@@ -693,6 +817,8 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     int nt = 0;
     for (int i = 0; i < segs.n; ++i) {
         A.tile0[i] = nt;
+        A.ktile0[i] = P.kp.tile0[seg_reg[i]];
+        A.nsel[i] = P.kp.nsel[seg_reg[i]];
         const SegDev& s = segs.s[i];
         const int ntok = s.n_text + s.T * s.Hg * s.Wg;
         nt += (ntok + BM - 1) / BM;

@@ -148,3 +148,45 @@ def test_cam_tokens_match_oracle():
     np.testing.assert_allclose(got2, oracle.cam_tokens(c2w, 2.0, 1.0), rtol=0, atol=2e-6)
     with pytest.raises(nomas.NomasError):
         nomas.cam_tokens(c2w[:6])
+
+
+def test_seg_attn_sel_host_checks():
+    """History selection: workspace sizes of shared and per-segment key
+    regions, and the errors of an invalid selection (host only)."""
+    L = nomas.lib()
+    P = ctypes.c_void_p
+    one, n1 = segs((16, 0, 2, 4, 6))                      # 64 new tokens
+    two, n2 = segs((16, 0, 2, 4, 6), (0, 2, 1, 4, 5))     # 64 + 20 new tokens
+
+    def ws(arr, n, clen, sel, H=3, split=1):
+        if sel is None:
+            return L.nomas_seg_attn_sel_workspace(arr, n, clen, None, None, H, split)
+        off, rng = nomas.sel_arrays(sel, n)
+        return L.nomas_seg_attn_sel_workspace(arr, n, clen, off.ctypes.data, rng.ctypes.data, H, split)
+
+    tiles = lambda t, H=3: H * t * 35840 + (H * t * 4 + 255) // 256 * 256
+    assert ws(one, n1, 1000, None) == L.nomas_seg_attn_workspace(one, n1, 1000, 3, 1) == tiles(17)
+    # one segment: its 2 ranges (100 + 31 cache tokens) then the 64 new tokens
+    assert ws(one, n1, 1000, [[(0, 100), (500, 531)]]) == tiles((131 + 64 + 63) // 64)
+    # two segments with the same list share one region holding all 84 new tokens
+    assert ws(two, n2, 1000, [[(10, 20)], [(10, 20)]]) == tiles((10 + 84 + 63) // 64)
+    # different lists: a region each, new tokens up to the segment's end
+    assert ws(two, n2, 1000, [[(10, 20)], [(0, 600)]]) == tiles((10 + 64 + 63) // 64 + (600 + 84 + 63) // 64)
+    assert ws(two, n2, 1000, [[], [(0, 1000)]]) == tiles(1 + (1000 + 84 + 63) // 64)
+    # invalid selections
+    for bad in ([[(5, 5)]], [[(-1, 3)]], [[(0, 1001)]], [[(10, 20), (15, 30)]], [[(20, 30), (0, 10)]]):
+        assert ws(one, n1, 1000, bad) == nomas.EINVAL, bad
+    off = np.array([1, 1], np.int32)                      # must start at 0
+    rng = np.array([0, 5], np.int64)
+    assert L.nomas_seg_attn_sel_workspace(one, n1, 1000, off.ctypes.data, rng.ctypes.data, 3, 1) == nomas.EINVAL
+    off = np.array([0, 2, 1], np.int32)                   # decreasing
+    rng = np.array([0, 5, 6, 9], np.int64)
+    assert L.nomas_seg_attn_sel_workspace(two, n2, 1000, off.ctypes.data, rng.ctypes.data, 3, 1) == nomas.EINVAL
+    many = [[(2 * i, 2 * i + 1) for i in range(nomas.MAX_SEL_RANGES + 1)]]
+    assert ws(one, n1, 1000, many) == nomas.EUNSUPPORTED
+    assert ws(one, n1, 1000, [[(2 * i, 2 * i + 1) for i in range(nomas.MAX_SEL_RANGES)]]) > 0
+    # the call itself refuses an invalid selection before touching anything
+    off, rng = nomas.sel_arrays([[(10, 20), (15, 30)]], n1)
+    rc = L.nomas_seg_attn_sel(P(FAKE), P(FAKE), P(FAKE), one, n1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 2000, 1000,
+                              off.ctypes.data, rng.ctypes.data, 2, 0.088, P(FAKE), None, 1, P(FAKE), 1 << 40, None)
+    assert rc == nomas.EINVAL

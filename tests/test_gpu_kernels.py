@@ -97,7 +97,7 @@ def test_kv_quant_append_bit_exact_and_offsets():
 # seg_attn
 
 
-def _run_gpu(q, k, v, segs, cache, Lc, H, with_lse=True, n_split=0):
+def _run_gpu(q, k, v, segs, cache, Lc, H, with_lse=True, n_split=0, sel=None):
     Ln = q.shape[0]
     lse = torch.empty((H, Ln), dtype=torch.float32, device="cuda:0") if with_lse else None
     if Lc > 0:
@@ -105,16 +105,16 @@ def _run_gpu(q, k, v, segs, cache, Lc, H, with_lse=True, n_split=0):
     else:
         kc = vc = ks = vs = None
     out = nomas.seg_attn(dev16(q), dev16(k), dev16(v), segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, lse=lse,
-                         n_split=n_split)
+                         n_split=n_split, sel=sel)
     torch.cuda.synchronize()
     return f64(out), (lse.cpu().numpy() if with_lse else None), out
 
 
-def _check_case(name, q, k, v, segs, cache, Lc, H, n_split=0):
-    say("seg_attn", name, "Ln", q.shape[0], "Lc", Lc, "H", H, "n_split", n_split)
-    got, lse, _ = _run_gpu(q, k, v, segs, cache, Lc, H, n_split=n_split)
+def _check_case(name, q, k, v, segs, cache, Lc, H, n_split=0, sel=None):
+    say("seg_attn", name, "Ln", q.shape[0], "Lc", Lc, "H", H, "n_split", n_split, "sel", sel)
+    got, lse, _ = _run_gpu(q, k, v, segs, cache, Lc, H, n_split=n_split, sel=sel)
     kc, vc, ks, vs = cache if Lc > 0 else (np.zeros((H, 0, 128), np.int8),) * 2 + (np.zeros((H, 0), np.float32),) * 2
-    ref, lref = oracle.seg_attn(q, k, v, segs, kc, vc, ks, vs, Lc, SM)
+    ref, lref = oracle.seg_attn(q, k, v, segs, kc, vc, ks, vs, Lc, SM, sel=sel)
     assert_close(got, ref, name)
     # the row sum is taken over the bf16-rounded probabilities that also feed
     # P.V (relative error <= 2^-9 per term), so |lse error| <= ~2^-9 + fp32 terms
@@ -274,6 +274,57 @@ def test_seg_attn_fixed_and_running_shift(n_split):
     say("shift gaps: min %.1f max %.1f" % (gaps.min(), gaps.max()))
     assert (gaps < 48).sum() >= 8 and (gaps > 96).sum() >= 8
     _check_case("fixed-and-running-shift", q, k, v, segs, cache, Lc, H, n_split=n_split)
+
+
+# ----------------------------------------------------------------------------
+# history selection (nomas_seg_attn_sel): each segment sees chosen cache tokens
+
+SEL = [
+    ("one-seg-3-ranges", [(7, 3, 2, 5, 9)], 300, 2, [[(0, 37), (100, 163), (250, 300)]], 0),
+    ("one-seg-3-ranges-split3", [(7, 3, 2, 5, 9)], 300, 2, [[(0, 37), (100, 163), (250, 300)]], 3),
+    ("packed-5-own-lists", [(3, 0, 1, 2, 3), (0, 1, 2, 3, 5), (10, 3, 1, 1, 1), (1, 4, 3, 2, 2), (0, 7, 1, 8, 8)], 77, 2,
+     [[(0, 10)], [], [(5, 77)], [(0, 77)], [(30, 31), (40, 77)]], 0),
+    ("two-seg-shared-list", [(5, 0, 1, 3, 4), (40, 1, 3, 10, 9)], 130, 3, [[(3, 90)], [(3, 90)]], 0),
+    ("empty-selection", [(7, 3, 2, 5, 9)], 130, 2, [[]], 0),
+]
+
+
+@pytest.mark.parametrize("name,segs,Lc,H,sel,n_split", SEL, ids=[c[0] for c in SEL])
+def test_seg_attn_selection_matches_oracle(name, segs, Lc, H, sel, n_split):
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    _check_case(name, q, k, v, segs, cache, Lc, H, n_split=n_split, sel=sel)
+
+
+def test_seg_attn_selection_of_the_whole_cache_is_bit_identical():
+    """Selecting every cache token (in one range or two) packs the same keys
+    as no selection: outputs and lse agree bit for bit."""
+    segs, Lc, H = [(7, 3, 2, 5, 9)], 300, 2
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    got0, lse0, _ = _run_gpu(q, k, v, segs, cache, Lc, H)
+    for sel in ([[(0, Lc)]], [[(0, 64), (64, Lc)]]):
+        got1, lse1, _ = _run_gpu(q, k, v, segs, cache, Lc, H, sel=sel)
+        assert np.array_equal(got0, got1) and np.array_equal(lse0, lse1), sel
+
+
+def test_seg_attn_selection_ignores_unselected_rows():
+    """Rewriting every unselected cache row (codes and scales) leaves outputs
+    and lse bit-identical."""
+    (segs, Lc, H, sel, _), = [c[1:] for c in SEL if c[0] == "packed-5-own-lists"]
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    got0, lse0, _ = _run_gpu(q, k, v, segs, cache, Lc, H, sel=sel)
+    keep = np.zeros(Lc, bool)
+    for ranges in sel:
+        for lo, hi in ranges:
+            keep[lo:hi] = True
+    say("unselected cache rows:", int((~keep).sum()))
+    kc, vc, ks, vs = (a.copy() for a in cache)
+    rng = np.random.default_rng(7)
+    for a in (kc, vc):
+        a[:, :Lc][:, ~keep] = rng.integers(-127, 128, size=a[:, :Lc][:, ~keep].shape, dtype=np.int8)
+    for a in (ks, vs):
+        a[:, :Lc][:, ~keep] = np.float32(7.5)
+    got1, lse1, _ = _run_gpu(q, k, v, segs, (kc, vc, ks, vs), Lc, H, sel=sel)
+    assert np.array_equal(got0, got1) and np.array_equal(lse0, lse1)
 
 
 def test_seg_attn_deterministic_and_cache_copy():

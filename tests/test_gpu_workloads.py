@@ -120,6 +120,21 @@ def test_full_cache_workload():
     rows = sample_rows(Lq, 1024, tail=16, extra=range(880, 890))
     check_rows("full cache", out, lse, sub(inp["q"]), sub(inp["k_new"]), sub(inp["v_new"]),
                cfg.new_segs, ocache, Lc, rows, heads=list(range(len(heads))), gpu_heads=heads)
+    # history selection at this shape: 18 of the 288 cached latent frames (the
+    # last of every 16), as the benchmark's selection workload runs it
+    (hseg,) = cfg.hist_segs
+    frame = hseg.Hg * hseg.Wg
+    sel = [[(f * frame, (f + 1) * frame) for f in range(15, hseg.T, 16)]]
+    lse2 = torch.empty((H, Lq), dtype=torch.float32, device="cuda:0")
+    out2 = nomas.seg_attn(dev16(inp["q"]), dev16(inp["k_new"]), dev16(inp["v_new"]), cfg.new_segs, *cache,
+                          cache_len=Lc, sm_scale=SM, lse=lse2, sel=sel)
+    torch.cuda.synchronize()
+    say("full cache, 18 selected frames")
+    kc, vc, ks, vs = ocache
+    ref, lref = oracle.seg_attn(sub(inp["q"]), sub(inp["k_new"]), sub(inp["v_new"]), cfg.new_segs, kc, vc, ks, vs,
+                                Lc, SM, rows=rows, sel=sel)
+    assert_close(f64(out2)[rows][:, heads], ref, "full cache, 18 selected frames")
+    np.testing.assert_allclose(lse2.cpu().numpy()[heads][:, rows], lref, rtol=0, atol=2.0 ** -8)
 
 
 def test_five_turns_growing_cache():
