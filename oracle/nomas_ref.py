@@ -53,7 +53,7 @@ __all__ = [
     "bf16_bits_to_f64", "bf16_round", "f64_to_bf16_bits",
     "token_positions", "rope_omega", "rope_table_f32", "rope3d", "rope3d_pos",
     "quantise", "dequant", "dequant_bf16", "build_cache",
-    "seg_ends", "attend", "seg_attn", "cam_tokens", "cam_kv", "cam_xattn",
+    "seg_ends", "attend", "seg_attn", "gqa_attn", "cam_tokens", "cam_kv", "cam_xattn",
 ]
 
 
@@ -303,6 +303,43 @@ def seg_attn(q_bits, k_new_bits, v_new_bits, new_segs, k_codes, v_codes, k_scale
                 o, l = attend(Qr[r], K, V, sm_scale)
                 out[r, hi] = o
                 lse[hi, r] = l
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# decoder window attention  ([CW] 模型内部: the PixelUMM decoder has 32 query
+# heads and 8 KV heads over a 4096-wide hidden state and reconstructs RGB from
+# 4 x 16 x 16 tubelets on 10-latent-frame windows that overlap by 5 frames)
+
+
+def gqa_attn(q_bits, k_bits, v_bits, sm_scale, rows=None, heads=None):
+    """Attention of one decoder window with grouped KV heads.
+
+    q: bf16 bits [L][Hq][128]; k, v: bf16 bits [L][Hkv][128], Hq a multiple
+    of Hkv.  Query head h uses KV head h // (Hq / Hkv).  Reading (the pages
+    give no mask or positions for the decoder): every token of the window
+    attends to every token of it, the operands are the BF16 values as given
+    (positions, if any, already applied), sm_scale is an argument.
+    Returns out [len(rows)][len(heads)][128] and lse [len(heads)][len(rows)],
+    float64 (lse in natural log)."""
+    q = np.asarray(q_bits)
+    L, Hq, _ = q.shape
+    Hkv = np.asarray(k_bits).shape[1]
+    assert Hq % Hkv == 0, "query heads must be a multiple of the KV heads"
+    grp = Hq // Hkv
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    out = np.zeros((len(rows), len(heads), D))
+    lse = np.zeros((len(heads), len(rows)))
+    for hi, h in enumerate(heads):
+        K = bf16_bits_to_f64(k_bits[:, h // grp, :])
+        V = bf16_bits_to_f64(v_bits[:, h // grp, :])
+        Q = bf16_bits_to_f64(q[rows, h, :])
+        blk = int(max(8, min(256, (1 << 24) // max(1, L))))
+        for lo in range(0, len(rows), blk):
+            o, l = attend(Q[lo:lo + blk], K, V, sm_scale)
+            out[lo:lo + blk, hi] = o
+            lse[hi, lo:lo + blk] = l
     return out, lse
 
 

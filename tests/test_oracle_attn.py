@@ -258,3 +258,49 @@ def test_unselected_cache_rows_do_not_matter():
         c2[name] = a
     out1, lse1 = run(c2, sel=SEL_THREE)
     assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+# ----------------------------------------------------------------------------
+# decoder window attention with grouped KV heads (comfyui-wiki, 模型内部)
+
+
+def _gqa_inputs(L, Hq, Hkv, seed=21):
+    q = synth.random_bf16(seed, (L, Hq, 128))
+    k = synth.random_bf16(seed + 1, (L, Hkv, 128))
+    v = synth.random_bf16(seed + 2, (L, Hkv, 128))
+    return q, k, v
+
+
+def test_gqa_matches_brute_force():
+    q, k, v = _gqa_inputs(12, 4, 2)
+    out, lse = oracle.gqa_attn(q, k, v, SM)
+    f = lambda b: oracle.bf16_bits_to_f64(b).tolist()
+    qf, kf, vf = f(q), f(k), f(v)
+    for h in range(4):
+        for i in range(12):
+            o, l, p = brute.softmax_attend(qf[i][h], [kf[j][h // 2] for j in range(12)],
+                                           [vf[j][h // 2] for j in range(12)], SM)
+            np.testing.assert_allclose(out[i, h], o, rtol=0, atol=1e-12)
+            assert abs(lse[h, i] - l) <= 1e-12
+
+
+def test_gqa_is_sdpa_with_repeated_kv_heads():
+    """Grouped heads equal torch's scaled_dot_product_attention (float64, CPU)
+    with each KV head repeated for its query heads."""
+    q, k, v = _gqa_inputs(50, 8, 2, seed=33)
+    out, _ = oracle.gqa_attn(q, k, v, SM)
+    t = lambda b, rep: torch.from_numpy(oracle.bf16_bits_to_f64(b)).repeat_interleave(rep, dim=1).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q, 1), t(k, 4), t(v, 4), scale=SM).permute(1, 0, 2)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_gqa_with_equal_heads_is_segment_attention_of_one_text_segment():
+    """Hq = Hkv: one all-text segment (no rotation) with no cache gives the
+    same numbers through seg_attn."""
+    q, k, v = _gqa_inputs(40, 2, 2, seed=44)
+    out, lse = oracle.gqa_attn(q, k, v, SM)
+    z8 = np.zeros((2, 0, 128), np.int8)
+    z = np.zeros((2, 0), np.float32)
+    o2, l2 = oracle.seg_attn(q, k, v, [(40, 0, 0, 0, 0)], z8, z8, z, z, 0, SM)
+    np.testing.assert_allclose(out, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, l2, rtol=0, atol=1e-13)
