@@ -235,6 +235,8 @@ def workloads():
                   selection, plus its own 63,360 tokens (median of 5 calls)
       fullcache-h2  the full-cache shape with 2 heads: one GPU's share when the
                   16 heads are split over 8 GPUs (median of 5 calls)
+      decoder-window  gqa_attn over one 10-latent-frame decoder window at
+                  1280x704 (35,200 tokens, 32 query / 8 KV heads; median of 5)
     History caches are built on the GPU by rope3d + kv_quant_append (bit-exact
     to the oracle's quantiser)."""
     import numpy as np
@@ -282,7 +284,7 @@ def workloads():
     def attn_line(name, ms, H, Lq, keys, extra=None):
         fl = 4.0 * 128 * H * Lq * keys
         tf = fl / (ms * 1e-3) / 1e12
-        emit(name, metric="seg_attn TFLOP/s", value=round(tf, 2), unit="TFLOP/s", ms=round(ms, 3),
+        emit(name, metric="attention TFLOP/s", value=round(tf, 2), unit="TFLOP/s", ms=round(ms, 3),
              pct_of_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2), heads=H, queries=Lq, keys_per_query=keys,
              algorithmic_flop=fl, **(extra or {}))
 
@@ -361,6 +363,18 @@ def workloads():
         torch.cuda.synchronize()
         del q, k, v, qc, out, oc, kr, ws
     del cache
+
+    # ---- decoder window: 10 latent frames of 4x16x16 tubelets at 1280x704
+    log("workload decoder-window")
+    L, Hq, Hkv = 10 * 44 * 80, 32, 8
+    q = d16(synth.random_bf16(501, (L, Hq, 128)))
+    k = d16(synth.random_bf16(502, (L, Hkv, 128)))
+    v = d16(synth.random_bf16(503, (L, Hkv, 128)))
+    out = torch.empty_like(q)
+    ws = torch.empty(nomas.gqa_attn_workspace(L, Hq, Hkv), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: nomas.gqa_attn(q, k, v, sm_scale=sm, out=out, workspace=ws, stream=stream), 5)
+    attn_line("decoder-window", ms, Hq, L, L, dict(kv_heads=Hkv, entry="nomas_gqa_attn"))
+    del q, k, v, out, ws
 
     # ---- fullcache-sel18 and fullcache-h2 share the full-cache inputs
     log("workload fullcache-sel18 / fullcache-h2: generating the full-cache inputs")

@@ -198,6 +198,29 @@ int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int6
                                  int n_split);
 
 /*
+ * Attention of one decoder window with grouped key/value heads.  The
+ * PixelUMM decoder has 32 query heads and 8 KV heads over a 4096-wide hidden
+ * state and reconstructs RGB from 4 x 16 x 16 tubelets on 10-latent-frame
+ * windows overlapping by 5 frames (comfyui-wiki news, 模型内部).  Every token
+ * of the window attends to every token of it; query head h uses KV head
+ * h / (Hq / Hkv); no positions are applied here (rotate q and k first with
+ * nomas_rope3d if the caller's model uses them):
+ *   s_ij = sm_scale * <q_i, k_j>,  o_i = softmax_j(s_ij) . v_j,  lse_i = ln sum_j exp(s_ij)
+ * q: device [L][Hq][128] bf16; k, v: device [L][Hkv][128] bf16; out: device
+ * [L][Hq][128] bf16; lse: device [Hq][L] float32 or NULL.  Hq a multiple of
+ * Hkv, sm_scale > 0.  workspace: device scratch of at least
+ * nomas_gqa_attn_workspace(L, Hq, Hkv) bytes, 16-byte aligned, owned by the
+ * caller (the keys laid out as 64-key tiles per KV head).  Errors as
+ * nomas_seg_attn; L * Hq <= NOMAS_MAX_TOKEN_HEADS.
+ */
+int nomas_gqa_attn(const nomas_bf16* q, const nomas_bf16* k, const nomas_bf16* v, int64_t L, int Hq, int Hkv,
+                   float sm_scale, nomas_bf16* out, float* lse, void* workspace, int64_t workspace_bytes,
+                   void* stream);
+
+/* Workspace bytes nomas_gqa_attn needs, or a negative error code.  Host only. */
+int64_t nomas_gqa_attn_workspace(int64_t L, int Hq, int Hkv);
+
+/*
  * Camera tokens of one turn (comfyui-wiki news, 相机控制作为一等输入).
  * Poses are made relative to the first frame (R0^T R_k, R0^T (t_k - t0)),
  * translations are multiplied by translation_scale and rotation angles

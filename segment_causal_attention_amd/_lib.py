@@ -25,7 +25,7 @@ MAX_SEL_RANGES = 64
 SM_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
 SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_workspace",
-           "nomas_seg_attn_sel", "nomas_seg_attn_sel_workspace",
+           "nomas_seg_attn_sel", "nomas_seg_attn_sel_workspace", "nomas_gqa_attn", "nomas_gqa_attn_workspace",
            "nomas_cam_tokens", "nomas_cam_xattn", "nomas_rope_table", "nomas_strerror", "nomas_version")
 
 
@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
                                          _F, _P, _P, _I, _P, _I64, _P]
         L.nomas_seg_attn_sel_workspace.argtypes = [ctypes.POINTER(Seg), _I, _I64, _P, _P, _I, _I]
         L.nomas_seg_attn_sel_workspace.restype = _I64
+        L.nomas_gqa_attn.argtypes = [_P, _P, _P, _I64, _I, _I, _F, _P, _P, _P, _I64, _P]
+        L.nomas_gqa_attn_workspace.argtypes = [_I64, _I, _I]
+        L.nomas_gqa_attn_workspace.restype = _I64
         L.nomas_cam_tokens.argtypes = [_P, _I, _D, _D, _P]
         L.nomas_cam_xattn.argtypes = [_P, _I64, _I, _P, _I, _P, _P, _F, _P, _P]
         L.nomas_rope_table.argtypes = [_I, _I, _P, _P]
@@ -72,7 +75,8 @@ def lib() -> ctypes.CDLL:
         L.nomas_strerror.restype = ctypes.c_char_p
         L.nomas_version.argtypes = []
         L.nomas_version.restype = ctypes.c_char_p
-        for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_sel", "nomas_cam_tokens",
+        for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_sel", "nomas_gqa_attn",
+                     "nomas_cam_tokens",
                      "nomas_cam_xattn", "nomas_rope_table"):
             getattr(L, name).restype = _I
         _lib = L
@@ -245,6 +249,38 @@ def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
                                         rng.ctypes.data, H, float(sm_scale), _ptr(out), _ptr(lse), int(n_split),
                                         _ptr(workspace), workspace.numel(), _stream(stream)),
                "nomas_seg_attn_sel")
+    return out
+
+
+def gqa_attn_workspace(L: int, Hq: int, Hkv: int) -> int:
+    """Bytes of device workspace gqa_attn needs (host only)."""
+    nbytes = lib().nomas_gqa_attn_workspace(int(L), int(Hq), int(Hkv))
+    if nbytes < 0:
+        raise NomasError(int(nbytes), "nomas_gqa_attn_workspace")
+    return int(nbytes)
+
+
+def gqa_attn(q, k, v, sm_scale: float = SM_SCALE, out=None, lse=None, workspace=None, stream=None):
+    """Decoder window attention with grouped KV heads: q [L][Hq][128],
+    k, v [L][Hkv][128] (bf16); every token attends to every token; query head
+    h uses KV head h // (Hq // Hkv).  Returns out [L][Hq][128]."""
+    import torch
+    L, Hq, Hkv = q.shape[0], q.shape[1], k.shape[1]
+    _dev(q, "q", (L, Hq, HEAD_DIM))
+    _dev(k, "k", (L, Hkv, HEAD_DIM))
+    _dev(v, "v", (L, Hkv, HEAD_DIM))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.shape)
+    if lse is not None:
+        _dev(lse, "lse", (Hq, L), 4)
+    need = gqa_attn_workspace(L, Hq, Hkv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device uint8 tensor")
+    _check(lib().nomas_gqa_attn(_ptr(q), _ptr(k), _ptr(v), L, Hq, Hkv, float(sm_scale), _ptr(out), _ptr(lse),
+                                _ptr(workspace), workspace.numel(), _stream(stream)), "nomas_gqa_attn")
     return out
 
 

@@ -15,10 +15,11 @@ int launch_rope3d(const uint16_t* x, uint16_t* y, int64_t L, int H, const SegTab
                   hipStream_t stream);
 int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const SegTable& segs, int Ln,
                     const int8_t* kc, const int8_t* vc, const float* ks, const float* vs, int64_t cap, int Lc,
-                    const int32_t* sel_off, const int64_t* sel_ranges, int H, float sm_scale, uint16_t* out,
-                    float* lse, int n_split, void* workspace, const RopeTables& rt, hipStream_t stream);
-int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int n_split, const int32_t* sel_off,
-                                 const int64_t* sel_ranges);
+                    const int32_t* sel_off, const int64_t* sel_ranges, int H, int Hkv, float sm_scale,
+                    uint16_t* out, float* lse, int n_split, void* workspace, const RopeTables& rt,
+                    hipStream_t stream);
+int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int Hkv, int n_split,
+                                 const int32_t* sel_off, const int64_t* sel_ranges);
 int launch_cam_xattn(const uint16_t* q, int64_t Lq, int H, const float* cam, int Nc, const uint16_t* wk,
                      const uint16_t* wv, float sm_scale, uint16_t* out, hipStream_t stream);
 }  // namespace nomas
@@ -175,7 +176,7 @@ int64_t nomas_seg_attn_sel_workspace(const nomas_seg* new_segs, int n_new_segs, 
     int rc = build_segs(new_segs, n_new_segs, &st, &Ln);
     if (rc != NOMAS_OK) return rc;
     if (Ln * H > NOMAS_MAX_TOKEN_HEADS) return NOMAS_EUNSUPPORTED;
-    return seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, n_split, sel_off, sel_ranges);
+    return seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, H, n_split, sel_off, sel_ranges);
 }
 
 int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int64_t cache_len, int H,
@@ -203,14 +204,50 @@ int nomas_seg_attn_sel(const nomas_bf16* q, const nomas_bf16* k_new, const nomas
     if (rc != NOMAS_OK) return rc;
     if (cap > NOMAS_MAX_CACHE || Ln * H > NOMAS_MAX_TOKEN_HEADS) return NOMAS_EUNSUPPORTED;
     // the selection is checked (and the workspace sized) before anything else is looked at on the device
-    const int64_t need = seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, n_split, sel_off, sel_ranges);
+    const int64_t need = seg_attn_workspace_bytes(st, (int)cache_len, (int)Ln, H, H, n_split, sel_off, sel_ranges);
     if (need < 0) return (int)need;
     if (Ln == 0) return NOMAS_OK;
     if (!workspace || !al16(workspace) || workspace_bytes < need) return NOMAS_EINVAL;
     RopeTables rt;
     if ((rc = rope_tables(&rt)) != NOMAS_OK) return rc;
     return launch_seg_attn(q, k_new, v_new, st, (int)Ln, k_codes, v_codes, k_scale, v_scale, cap, (int)cache_len,
-                           sel_off, sel_ranges, H, sm_scale, out, lse, n_split, workspace, rt, (hipStream_t)stream);
+                           sel_off, sel_ranges, H, H, sm_scale, out, lse, n_split, workspace, rt,
+                           (hipStream_t)stream);
+}
+
+// decoder window attention: one all-text segment (no rotation), no cache,
+// KV heads shared by groups of query heads
+static int gqa_plan(int64_t L, int Hq, int Hkv, SegTable* st) {
+    if (L < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return NOMAS_EINVAL;
+    if (Hq > kMaxHeads || L > kMaxTokens || L * Hq > NOMAS_MAX_TOKEN_HEADS) return NOMAS_EUNSUPPORTED;
+    const nomas_seg s = {(int32_t)L, 0, 0, 0, 0};
+    int64_t Ln = 0;
+    return build_segs(&s, 1, st, &Ln);
+}
+
+int64_t nomas_gqa_attn_workspace(int64_t L, int Hq, int Hkv) {
+    SegTable st;
+    const int rc = gqa_plan(L, Hq, Hkv, &st);
+    if (rc != NOMAS_OK) return rc;
+    return seg_attn_workspace_bytes(st, 0, (int)L, Hq, Hkv, 0, nullptr, nullptr);
+}
+
+int nomas_gqa_attn(const nomas_bf16* q, const nomas_bf16* k, const nomas_bf16* v, int64_t L, int Hq, int Hkv,
+                   float sm_scale, nomas_bf16* out, float* lse, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+    if (!q || !k || !v || !out || !finite_pos(sm_scale)) return NOMAS_EINVAL;
+    if (!al16(q) || !al16(k) || !al16(v) || !al16(out) || (lse && !al4(lse))) return NOMAS_EINVAL;
+    SegTable st;
+    int rc = gqa_plan(L, Hq, Hkv, &st);
+    if (rc != NOMAS_OK) return rc;
+    if (L == 0) return NOMAS_OK;
+    const int64_t need = seg_attn_workspace_bytes(st, 0, (int)L, Hq, Hkv, 0, nullptr, nullptr);
+    if (need < 0) return (int)need;
+    if (!workspace || !al16(workspace) || workspace_bytes < need) return NOMAS_EINVAL;
+    RopeTables rt;
+    if ((rc = rope_tables(&rt)) != NOMAS_OK) return rc;
+    return launch_seg_attn(q, k, v, st, (int)L, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr, Hq, Hkv,
+                           sm_scale, out, lse, 0, workspace, rt, (hipStream_t)stream);
 }
 
 int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf16* v_new,

@@ -112,7 +112,7 @@ struct PackArgs {
     uint8_t* img;
     float* knorm;                   // [H][ntk]: largest squared key norm of each tile
     int64_t cap;
-    int32_t H, ntk;                 // ntk: tiles per head
+    int32_t H, ntk;                 // H: key/value heads (of k, v and the cache); ntk: tiles per head
     KeyPlan kp;
     SegTable segs;                  // the new segments (positions of the new keys)
     RopeTables rt;
@@ -230,7 +230,8 @@ struct AttnArgs {
     float* lse;
     float* po;                      // split > 1: partial outputs O/l [split][Ln][H][128] fp32
     float* plse;                    //            partial log2-sum-exp [split][H][Ln]
-    int32_t Ln, H, ntq, ntk;        // ntq: query tiles per head, ntk: key tiles per head
+    int32_t Ln, H, ntq, ntk;        // H: query heads; ntq: query tiles per head, ntk: key tiles per KV head
+    int32_t grp;                    // query heads per key/value head (head h reads KV head h / grp)
     int32_t nsplit;                 // key-range parts per query tile
     float scale_log2;               // sm_scale * log2(e)
     int32_t tile0[NOMAS_MAX_SEGS + 1];   // first query tile of each new segment
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     // keys [0, nkeys) of the packed range are allowed: the cache and the new
     // tokens up to the end of this segment
     const int nkeys = __builtin_amdgcn_readfirstlane(A.nsel[a] + kend);
-    const int64_t kbase = (int64_t)head * A.ntk + A.ktile0[a];    // this segment's region of the images
+    const int64_t kbase = (int64_t)(head / A.grp) * A.ntk + A.ktile0[a];   // this segment's region of the images
     const int nt_all = (nkeys + BN - 1) / BN;
     // this workgroup's part of the key tiles: [t0, t0 + nt)
     const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * nt_all / A.nsplit));
@@ -771,15 +772,16 @@ int plan_splits(const SegTable& segs, const KeyPlan& kp, const int32_t* seg_reg,
 // per-tile key norms follow the images, padded to 256 bytes
 static int64_t knorm_bytes(int64_t tiles) { return (tiles * 4 + 255) / 256 * 256; }
 
-// Workspace bytes, or a negative error code for an invalid selection.
-int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int n_split, const int32_t* sel_off,
-                                 const int64_t* sel_ranges) {
+// Workspace bytes, or a negative error code for an invalid selection.  H
+// query heads, Hkv key/value heads (tile images are per KV head).
+int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int Hkv, int n_split,
+                                 const int32_t* sel_off, const int64_t* sel_ranges) {
     KeyPlan kp;
     int32_t seg_reg[NOMAS_MAX_SEGS];
     const int rc = build_key_plan(segs, Lc, Ln, sel_off, sel_ranges, &kp, seg_reg);
     if (rc != NOMAS_OK) return rc;
     const int p = plan_splits(segs, kp, seg_reg, H, n_split);
-    const int64_t tiles = (int64_t)H * kp.tile0[kp.nreg];
+    const int64_t tiles = (int64_t)Hkv * kp.tile0[kp.nreg];
     int64_t b = tiles * TILE_BYTES + knorm_bytes(tiles);
     if (p > 1) b += (int64_t)p * Ln * H * (D + 1) * 4;
     return b;
@@ -787,8 +789,8 @@ int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, in
 
 int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const SegTable& segs,
                     int Ln, const int8_t* kc, const int8_t* vc, const float* ks, const float* vs,
-                    int64_t cap, int Lc, const int32_t* sel_off, const int64_t* sel_ranges, int H, float sm_scale,
-                    uint16_t* out, float* lse, int n_split, void* workspace, const RopeTables& rt,
+                    int64_t cap, int Lc, const int32_t* sel_off, const int64_t* sel_ranges, int H, int Hkv,
+                    float sm_scale, uint16_t* out, float* lse, int n_split, void* workspace, const RopeTables& rt,
                     hipStream_t stream) {
     PackArgs P{};
     int32_t seg_reg[NOMAS_MAX_SEGS];
@@ -799,8 +801,8 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     P.kc = kc; P.vc = vc; P.ks = ks; P.vs = vs;
     P.k = k; P.v = v;
     P.img = static_cast<uint8_t*>(workspace);
-    P.knorm = reinterpret_cast<float*>(P.img + (int64_t)H * ntk * TILE_BYTES);
-    P.cap = cap; P.H = H; P.ntk = ntk;
+    P.knorm = reinterpret_cast<float*>(P.img + (int64_t)Hkv * ntk * TILE_BYTES);
+    P.cap = cap; P.H = Hkv; P.ntk = ntk;
     P.segs = segs;
     P.rt = rt;
 
@@ -808,9 +810,10 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.q = q; A.img = P.img; A.knorm = P.knorm;
     A.out = out; A.lse = lse;
     A.Ln = Ln; A.H = H; A.ntk = ntk;
+    A.grp = H / Hkv;
     A.nsplit = nsplit;
     if (nsplit > 1) {
-        A.po = reinterpret_cast<float*>(P.img + (int64_t)H * ntk * TILE_BYTES + knorm_bytes((int64_t)H * ntk));
+        A.po = reinterpret_cast<float*>(P.img + (int64_t)Hkv * ntk * TILE_BYTES + knorm_bytes((int64_t)Hkv * ntk));
         A.plse = A.po + (int64_t)nsplit * Ln * H * D;
     }
     A.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
@@ -828,7 +831,7 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.segs = segs;
     A.rt = rt;
     if (nt == 0) return NOMAS_OK;
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)ntk, (unsigned)H), dim3(PACK_NT), 0, stream, P);
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)ntk, (unsigned)Hkv), dim3(PACK_NT), 0, stream, P);
     const int64_t blocks = (int64_t)nt * H * nsplit;
     hipLaunchKernelGGL(seg_attn_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, A);
     if (nsplit > 1) {

@@ -190,3 +190,22 @@ def test_seg_attn_sel_host_checks():
     rc = L.nomas_seg_attn_sel(P(FAKE), P(FAKE), P(FAKE), one, n1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 2000, 1000,
                               off.ctypes.data, rng.ctypes.data, 2, 0.088, P(FAKE), None, 1, P(FAKE), 1 << 40, None)
     assert rc == nomas.EINVAL
+
+
+def test_gqa_attn_host_checks():
+    L = nomas.lib()
+    P = ctypes.c_void_p
+    # tiles are per KV head: ceil(100 / 64) = 2 tiles x 2 KV heads, norms padded to 256 bytes
+    assert L.nomas_gqa_attn_workspace(100, 4, 2) == 2 * 2 * 35840 + 256
+    assert L.nomas_gqa_attn_workspace(100, 4, 3) == nomas.EINVAL      # not a multiple
+    assert L.nomas_gqa_attn_workspace(100, 0, 1) == nomas.EINVAL
+    assert L.nomas_gqa_attn_workspace(-1, 4, 2) == nomas.EINVAL
+    assert L.nomas_gqa_attn_workspace(1 << 22, 32, 8) == nomas.EUNSUPPORTED   # L * Hq beyond the limit
+    args = lambda **kw: [P(kw.get("q", FAKE)), P(FAKE), P(FAKE), kw.get("L", 100), kw.get("Hq", 4), kw.get("Hkv", 2),
+                         kw.get("sm", 0.088), P(FAKE), None, P(kw.get("ws", FAKE)), kw.get("wsb", 1 << 30), None]
+    assert L.nomas_gqa_attn(*args(q=None)) == nomas.EINVAL
+    assert L.nomas_gqa_attn(*args(q=FAKE + 4)) == nomas.EINVAL
+    assert L.nomas_gqa_attn(*args(Hkv=3)) == nomas.EINVAL
+    assert L.nomas_gqa_attn(*args(sm=-1.0)) == nomas.EINVAL
+    assert L.nomas_gqa_attn(*args(wsb=100)) == nomas.EINVAL
+    assert L.nomas_gqa_attn(*args(L=0)) == nomas.OK

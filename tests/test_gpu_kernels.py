@@ -346,6 +346,26 @@ def test_seg_attn_deterministic_and_cache_copy():
 
 
 # ----------------------------------------------------------------------------
+# decoder window attention with grouped KV heads (nomas_gqa_attn)
+
+GQA = [(100, 4, 2), (700, 8, 2), (3000, 32, 8), (257, 2, 1), (64, 3, 3), (1, 4, 4)]
+
+
+@pytest.mark.parametrize("L,Hq,Hkv", GQA, ids=["L%d-%dq-%dkv" % c for c in GQA])
+def test_gqa_attn_matches_oracle(L, Hq, Hkv):
+    say("gqa_attn", L, Hq, Hkv)
+    q = synth.random_bf16(401, (L, Hq, 128))
+    k = synth.random_bf16(402, (L, Hkv, 128))
+    v = synth.random_bf16(403, (L, Hkv, 128))
+    lse = torch.empty((Hq, L), dtype=torch.float32, device="cuda:0")
+    out = nomas.gqa_attn(dev16(q), dev16(k), dev16(v), sm_scale=SM, lse=lse)
+    torch.cuda.synchronize()
+    ref, lref = oracle.gqa_attn(q, k, v, SM)
+    assert_close(f64(out), ref, "gqa L=%d Hq=%d Hkv=%d" % (L, Hq, Hkv))
+    np.testing.assert_allclose(lse.cpu().numpy(), lref, rtol=0, atol=2.0 ** -8)
+
+
+# ----------------------------------------------------------------------------
 # cam_xattn
 
 

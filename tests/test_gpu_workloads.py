@@ -8,6 +8,7 @@ are independent.
   4 s segment  21,376 x 37,216, outlier channels x20, layers 0 and 53
   full cache   63,360 x 316,800, cache built on the GPU (rope3d + quantise)
   five turns   cache grown turn by turn to 253,440 tokens, camera cross-attention
+  decoder      one 10-latent-frame window: 35,200 tokens, 32 query / 8 KV heads
 """
 import numpy as np
 import pytest
@@ -187,3 +188,21 @@ def test_five_turns_growing_cache():
         length = n
         del k_rot, kd, vd
     assert length == cap
+
+
+def test_decoder_window():
+    """One decoder window at 1280x704: 10 latent frames of 4x16x16 tubelets
+    (10 x 44 x 80 = 35,200 tokens), 32 query heads over 8 KV heads."""
+    L, Hq, Hkv = 10 * 44 * 80, 32, 8
+    q = synth.random_bf16(501, (L, Hq, 128))
+    k = synth.random_bf16(502, (L, Hkv, 128))
+    v = synth.random_bf16(503, (L, Hkv, 128))
+    say("decoder window", L, Hq, Hkv)
+    lse = torch.empty((Hq, L), dtype=torch.float32, device="cuda:0")
+    out = nomas.gqa_attn(dev16(q), dev16(k), dev16(v), sm_scale=SM, lse=lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(L, 512, tail=16)
+    heads = [0, 3, 4, 13, 31]
+    ref, lref = oracle.gqa_attn(q, k, v, SM, rows=rows, heads=heads)
+    assert_close(f64(out)[rows][:, heads], ref, "decoder window")
+    np.testing.assert_allclose(lse.cpu().numpy()[heads][:, rows], lref, rtol=0, atol=2.0 ** -8)
