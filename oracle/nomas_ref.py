@@ -53,7 +53,7 @@ __all__ = [
     "bf16_bits_to_f64", "bf16_round", "f64_to_bf16_bits",
     "token_positions", "rope_omega", "rope_table_f32", "rope3d", "rope3d_pos",
     "quantise", "dequant", "dequant_bf16", "build_cache",
-    "seg_ends", "attend", "seg_attn", "gqa_attn", "cam_tokens", "cam_kv", "cam_xattn",
+    "seg_ends", "attend", "seg_attn", "gqa_attn", "w8a16_linear", "cam_tokens", "cam_kv", "cam_xattn",
 ]
 
 
@@ -341,6 +341,26 @@ def gqa_attn(q_bits, k_bits, v_bits, sm_scale, rows=None, heads=None):
             out[lo:lo + blk, hi] = o
             lse[hi, lo:lo + blk] = l
     return out, lse
+
+
+# ----------------------------------------------------------------------------
+# INT8-weight linear layers  ([CW] 单张 4090 配置 and [HW] section 3.5 table:
+# the DiT weights are stored INT8 while the linear layers compute in BF16;
+# [CW] 模型内部: hidden size 2048)
+
+
+def w8a16_linear(x_bits, w_codes, w_scale, rows=None):
+    """y = x . W^T with INT8-stored weights and BF16 math.
+
+    x: bf16 bits [M][K]; w_codes: int8 [N][K]; w_scale: float32 [N], one
+    scale per output channel (the build's reading: the pages fix only INT8
+    storage; the scale layout follows the KV cache's, one fp32 scale per
+    row).  Each weight enters the product as the BF16 value
+    bf16(fl32(code * scale)), as cached keys do; products and sums are exact
+    here (float64).  Returns y [len(rows)][N] float64."""
+    x = bf16_bits_to_f64(np.asarray(x_bits) if rows is None else np.asarray(x_bits)[np.asarray(rows)])
+    W = dequant_bf16(w_codes, w_scale)
+    return x @ W.T
 
 
 # ----------------------------------------------------------------------------
