@@ -237,6 +237,10 @@ def workloads():
                   16 heads are split over 8 GPUs (median of 5 calls)
       decoder-window  gqa_attn over one 10-latent-frame decoder window at
                   1280x704 (35,200 tokens, 32 query / 8 KV heads; median of 5)
+      w8a16-qkv, w8a16-ffn-up  INT8-weight linear layers of one 12 s segment
+                  (63,360 x 2048 -> 6144 and -> 8192; median of 10), with the
+                  dequantisation pass alone and torch's BF16 matmul on the
+                  dequantised weights as context
     History caches are built on the GPU by rope3d + kv_quant_append (bit-exact
     to the oracle's quantiser)."""
     import numpy as np
@@ -375,6 +379,30 @@ def workloads():
     ms = timed(lambda: nomas.gqa_attn(q, k, v, sm_scale=sm, out=out, workspace=ws, stream=stream), 5)
     attn_line("decoder-window", ms, Hq, L, L, dict(kv_heads=Hkv, entry="nomas_gqa_attn"))
     del q, k, v, out, ws
+
+    # ---- INT8-weight linear layers of one 12 s segment (63,360 tokens, hidden 2048)
+    for name, N in (("w8a16-qkv", 6144), ("w8a16-ffn-up", 8192)):
+        log("workload " + name)
+        M, K = 63360, 2048
+        x = d16(synth.random_bf16(601, (M, K)))
+        g = np.random.default_rng(602)
+        codes = torch.from_numpy(g.integers(-127, 128, size=(N, K), dtype=np.int8)).to(dev)
+        scale = torch.from_numpy((1.0 / (73.0 * math.sqrt(K)) * (0.5 + g.random(N))).astype(np.float32)).to(dev)
+        y = torch.empty((M, N), dtype=torch.int16, device=dev)
+        ws = torch.empty(nomas.w8a16_linear_workspace(K, N), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: nomas.w8a16_linear(x, codes, scale, out=y, workspace=ws, stream=stream), 10, 3)
+        # context: the dequantisation pass alone (M = 0), and torch's BF16 matmul on the dequantised weights
+        ms_dq = timed(lambda: nomas.w8a16_linear(x[:0], codes, scale, out=y[:0], workspace=ws, stream=stream), 10, 3)
+        wb = ws[:N * K * 2].view(torch.bfloat16).view(N, K)
+        xb = x.view(torch.bfloat16)
+        wt = wb.t().contiguous()
+        ms_t = timed(lambda: torch.matmul(xb, wt), 10, 3)
+        fl = 2.0 * M * N * K
+        tf = fl / (ms * 1e-3) / 1e12
+        emit(name, metric="linear TFLOP/s", value=round(tf, 2), unit="TFLOP/s", ms=round(ms, 4),
+             pct_of_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2), M=M, K=K, N=N, algorithmic_flop=fl,
+             dequant_ms=round(ms_dq, 4), context_torch_bf16_matmul_ms=round(ms_t, 4))
+        del x, codes, scale, y, ws, wt
 
     # ---- fullcache-sel18 and fullcache-h2 share the full-cache inputs
     log("workload fullcache-sel18 / fullcache-h2: generating the full-cache inputs")

@@ -221,6 +221,25 @@ int nomas_gqa_attn(const nomas_bf16* q, const nomas_bf16* k, const nomas_bf16* v
 int64_t nomas_gqa_attn_workspace(int64_t L, int Hq, int Hkv);
 
 /*
+ * Linear layer with INT8-stored weights and BF16 math: y = x . W^T.  The DiT
+ * weights are stored INT8 while the linear layers compute in BF16
+ * (comfyui-wiki news, 单张 4090 配置; huaweicloud blog, section 3.5 table).
+ * Each weight enters as bf16(fl32(code * scale)) with one fp32 scale per
+ * output channel; products accumulate in fp32 and y is rounded to bf16.
+ * x: device [M][K] bf16; w_codes: device [N][K] int8; w_scale: device [N]
+ * float32; y: device [M][N] bf16.  K a multiple of 64 and N of 256 (the
+ * model's 2048 / 6144 / 8192), else NOMAS_EUNSUPPORTED; M >= 0 any.
+ * workspace: device scratch of at least nomas_w8a16_linear_workspace(K, N)
+ * bytes (the weights dequantised to bf16 for this call), 16-byte aligned,
+ * owned by the caller.  Pointers 16-byte aligned (scales 4).
+ */
+int nomas_w8a16_linear(const nomas_bf16* x, int64_t M, int64_t K, const int8_t* w_codes, const float* w_scale,
+                       int64_t N, nomas_bf16* y, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes nomas_w8a16_linear needs (N * K * 2), or a negative error code.  Host only. */
+int64_t nomas_w8a16_linear_workspace(int64_t K, int64_t N);
+
+/*
  * Camera tokens of one turn (comfyui-wiki news, 相机控制作为一等输入).
  * Poses are made relative to the first frame (R0^T R_k, R0^T (t_k - t0)),
  * translations are multiplied by translation_scale and rotation angles

@@ -26,6 +26,7 @@ SM_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
 SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_workspace",
            "nomas_seg_attn_sel", "nomas_seg_attn_sel_workspace", "nomas_gqa_attn", "nomas_gqa_attn_workspace",
+           "nomas_w8a16_linear", "nomas_w8a16_linear_workspace",
            "nomas_cam_tokens", "nomas_cam_xattn", "nomas_rope_table", "nomas_strerror", "nomas_version")
 
 
@@ -68,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.nomas_gqa_attn.argtypes = [_P, _P, _P, _I64, _I, _I, _F, _P, _P, _P, _I64, _P]
         L.nomas_gqa_attn_workspace.argtypes = [_I64, _I, _I]
         L.nomas_gqa_attn_workspace.restype = _I64
+        L.nomas_w8a16_linear.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _P]
+        L.nomas_w8a16_linear_workspace.argtypes = [_I64, _I64]
+        L.nomas_w8a16_linear_workspace.restype = _I64
         L.nomas_cam_tokens.argtypes = [_P, _I, _D, _D, _P]
         L.nomas_cam_xattn.argtypes = [_P, _I64, _I, _P, _I, _P, _P, _F, _P, _P]
         L.nomas_rope_table.argtypes = [_I, _I, _P, _P]
@@ -76,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.nomas_version.argtypes = []
         L.nomas_version.restype = ctypes.c_char_p
         for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_sel", "nomas_gqa_attn",
+                     "nomas_w8a16_linear",
                      "nomas_cam_tokens",
                      "nomas_cam_xattn", "nomas_rope_table"):
             getattr(L, name).restype = _I
@@ -281,6 +286,36 @@ def gqa_attn(q, k, v, sm_scale: float = SM_SCALE, out=None, lse=None, workspace=
         raise ValueError("workspace must be a contiguous device uint8 tensor")
     _check(lib().nomas_gqa_attn(_ptr(q), _ptr(k), _ptr(v), L, Hq, Hkv, float(sm_scale), _ptr(out), _ptr(lse),
                                 _ptr(workspace), workspace.numel(), _stream(stream)), "nomas_gqa_attn")
+    return out
+
+
+def w8a16_linear_workspace(K: int, N: int) -> int:
+    """Bytes of device workspace w8a16_linear needs (host only)."""
+    nbytes = lib().nomas_w8a16_linear_workspace(int(K), int(N))
+    if nbytes < 0:
+        raise NomasError(int(nbytes), "nomas_w8a16_linear_workspace")
+    return int(nbytes)
+
+
+def w8a16_linear(x, w_codes, w_scale, out=None, workspace=None, stream=None):
+    """y = x . W^T with INT8 weights (codes [N][K] int8, scales [N] float32)
+    and BF16 math; x [M][K] bf16 -> y [M][N] bf16."""
+    import torch
+    M, K = x.shape
+    N = w_codes.shape[0]
+    _dev(x, "x", (M, K))
+    _dev(w_codes, "w_codes", (N, K), 1)
+    _dev(w_scale, "w_scale", (N,), 4)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _dev(out, "out", (M, N))
+    need = w8a16_linear_workspace(K, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device uint8 tensor")
+    _check(lib().nomas_w8a16_linear(_ptr(x), M, K, _ptr(w_codes), _ptr(w_scale), N, _ptr(out), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)), "nomas_w8a16_linear")
     return out
 
 

@@ -20,6 +20,9 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
                     hipStream_t stream);
 int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, int Hkv, int n_split,
                                  const int32_t* sel_off, const int64_t* sel_ranges);
+int launch_w8a16(const uint16_t* x, int64_t M, int64_t K, const int8_t* codes, const float* scale, int64_t N,
+                 uint16_t* y, void* workspace, hipStream_t stream);
+int64_t w8a16_workspace_bytes(int64_t N, int64_t K);
 int launch_cam_xattn(const uint16_t* q, int64_t Lq, int H, const float* cam, int Nc, const uint16_t* wk,
                      const uint16_t* wv, float sm_scale, uint16_t* out, hipStream_t stream);
 }  // namespace nomas
@@ -258,6 +261,33 @@ int nomas_seg_attn(const nomas_bf16* q, const nomas_bf16* k_new, const nomas_bf1
     return nomas_seg_attn_sel(q, k_new, v_new, new_segs, n_new_segs, k_codes, v_codes, k_scale, v_scale, cap,
                               cache_len, nullptr, nullptr, H, sm_scale, out, lse, n_split, workspace,
                               workspace_bytes, stream);
+}
+
+namespace {
+int w8a16_shape(int64_t M, int64_t K, int64_t N) {
+    if (M < 0 || K < 1 || N < 1) return NOMAS_EINVAL;
+    if (K % 64 != 0 || N % 256 != 0) return NOMAS_EUNSUPPORTED;
+    if (M * K * 2 >= ((int64_t)1 << 31) || N * K * 2 >= ((int64_t)1 << 31) || M * N >= ((int64_t)1 << 40))
+        return NOMAS_EUNSUPPORTED;
+    return NOMAS_OK;
+}
+}  // namespace
+
+int64_t nomas_w8a16_linear_workspace(int64_t K, int64_t N) {
+    const int rc = w8a16_shape(0, K, N);
+    return rc != NOMAS_OK ? rc : w8a16_workspace_bytes(N, K);
+}
+
+int nomas_w8a16_linear(const nomas_bf16* x, int64_t M, int64_t K, const int8_t* w_codes, const float* w_scale,
+                       int64_t N, nomas_bf16* y, void* workspace, int64_t workspace_bytes, void* stream) {
+    int rc = w8a16_shape(M, K, N);
+    if (rc != NOMAS_OK) return rc;
+    if (!w_codes || !w_scale || !workspace) return NOMAS_EINVAL;
+    if (M > 0 && (!x || !y)) return NOMAS_EINVAL;
+    if ((x && !al16(x)) || (y && !al16(y)) || !al16(w_codes) || !al4(w_scale) || !al16(workspace))
+        return NOMAS_EINVAL;
+    if (workspace_bytes < w8a16_workspace_bytes(N, K)) return NOMAS_EINVAL;
+    return launch_w8a16(x, M, K, w_codes, w_scale, N, y, workspace, (hipStream_t)stream);
 }
 
 int nomas_cam_tokens(const double* c2w, int n_frames, double translation_scale, double rotation_scale,

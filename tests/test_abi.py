@@ -209,3 +209,28 @@ def test_gqa_attn_host_checks():
     assert L.nomas_gqa_attn(*args(sm=-1.0)) == nomas.EINVAL
     assert L.nomas_gqa_attn(*args(wsb=100)) == nomas.EINVAL
     assert L.nomas_gqa_attn(*args(L=0)) == nomas.OK
+
+
+def test_w8a16_host_checks():
+    L = nomas.lib()
+    P = ctypes.c_void_p
+    assert L.nomas_w8a16_linear_workspace(2048, 8192) == 8192 * 2048 * 2
+    assert L.nomas_w8a16_linear_workspace(2000, 8192) == nomas.EUNSUPPORTED   # K not a multiple of 64
+    assert L.nomas_w8a16_linear_workspace(2048, 1000) == nomas.EUNSUPPORTED   # N not a multiple of 256
+    assert L.nomas_w8a16_linear_workspace(0, 256) == nomas.EINVAL
+    good = dict(x=FAKE, M=100, K=128, w=FAKE, s=FAKE, N=256, y=FAKE, ws=FAKE, wsb=256 * 128 * 2)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.nomas_w8a16_linear(P(a["x"]), a["M"], a["K"], P(a["w"]), P(a["s"]), a["N"], P(a["y"]), P(a["ws"]),
+                                    a["wsb"], None)
+
+    assert call(M=-1) == nomas.EINVAL
+    assert call(x=None) == nomas.EINVAL
+    assert call(w=None) == nomas.EINVAL
+    assert call(x=FAKE + 2) == nomas.EINVAL
+    assert call(s=FAKE + 2) == nomas.EINVAL
+    assert call(wsb=256 * 128 * 2 - 1) == nomas.EINVAL
+    assert call(K=96) == nomas.EUNSUPPORTED
+    assert call(N=300) == nomas.EUNSUPPORTED
+    assert call(M=1 << 20, K=2048) == nomas.EUNSUPPORTED     # x beyond 2 GiB

@@ -366,6 +366,49 @@ def test_gqa_attn_matches_oracle(L, Hq, Hkv):
 
 
 # ----------------------------------------------------------------------------
+# INT8-weight linear layer (nomas_w8a16_linear)
+
+
+def _w8_inputs(M, K, N, seed):
+    """x ~ N(0, 1) bf16; codes uniform in [-127, 127]; scales around
+    1 / (73 sqrt K) so that outputs are O(1) (the codes' std is ~73)."""
+    x = synth.random_bf16(seed, (M, K))
+    g = np.random.default_rng(seed)
+    codes = g.integers(-127, 128, size=(N, K), dtype=np.int8)
+    s = (1.0 / (73.0 * math.sqrt(K)) * (0.5 + g.random(N))).astype(np.float32)
+    return x, codes, s
+
+
+W8 = [(300, 128, 256), (1000, 2048, 512), (513, 2048, 6144), (64, 8192, 2048), (1, 64, 256), (0, 128, 256)]
+
+
+@pytest.mark.parametrize("M,K,N", W8, ids=["M%d-K%d-N%d" % c for c in W8])
+def test_w8a16_linear_matches_oracle(M, K, N):
+    say("w8a16", M, K, N)
+    x, codes, s = _w8_inputs(M, K, N, 701 + M)
+    y = nomas.w8a16_linear(dev16(x) if M else torch.empty((0, K), dtype=torch.int16, device="cuda:0"),
+                           dev(codes), dev(s))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (M, N)
+    if M == 0:
+        return
+    ref = oracle.w8a16_linear(x, codes, s)
+    assert_close(f64(y), ref, "w8a16 M=%d K=%d N=%d" % (M, K, N))
+
+
+def test_w8a16_linear_model_shape_sampled():
+    """The FFN up projection of one 12 s segment: 63,360 tokens x 2048 -> 8192,
+    sampled rows (including the ragged last tile) against the oracle."""
+    M, K, N = 63360, 2048, 8192
+    x, codes, s = _w8_inputs(M, K, N, 777)
+    y = nomas.w8a16_linear(dev16(x), dev(codes), dev(s))
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(range(0, M, 997)) | set(range(M - 40, M))))
+    ref = oracle.w8a16_linear(x, codes, s, rows=rows)
+    assert_close(f64(y)[rows], ref, "w8a16 model shape")
+
+
+# ----------------------------------------------------------------------------
 # cam_xattn
 
 
