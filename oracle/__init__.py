@@ -9,14 +9,17 @@ generator in ``synth`` feeds both.
 
 Modules
   nomas_ref  numpy float64 definitions (token layout, 3D RoPE, INT8
-             quantiser, segment-causal attention, camera tokens and camera
+             quantiser, segment-causal attention and its gradients for
+             packed training sequences, decoder window attention, the
+             INT8-weight linear layer, camera tokens and camera
              cross-attention), chunked only over independent (head, query
              block) pieces.
   brute      pure-Python loops with math.fsum / fractions.Fraction, for tiny
              inputs; written separately so that it pins nomas_ref.
 
 Parity status: every function is pinned by the not-gpu tests (brute force,
-closed forms, invariants, special cases).  The match to the released Hy-Nomas
+closed forms, invariants, special cases; the gradients by finite differences
+of the pinned forward and by torch autograd).  The match to the released Hy-Nomas
 model itself (RoPE pair convention, text-token positions, scale layout) is
 "parity unpinned": the pages give no code, weights or worked example.
 """

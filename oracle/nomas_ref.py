@@ -29,6 +29,9 @@ Readings where the pages are silent (each is listed in the design notes):
     products are BF16 values -- rotated Q and K rounded to BF16, cached K/V
     dequantised as bf16(fl32(code * scale)).  Scores, softmax and sums are
     exact here (float64).
+  * Gradients (packed training, [HW] 2.3): the bf16 rounding of the rotated
+    q and k is a cast whose derivative is the identity; the backward pass is
+    otherwise the exact chain rule of the exact forward.
   * Camera tokens: poses made relative to the first frame of the turn,
     translation x translation_scale, rotation angle x rotation_scale
     (axis-angle), 4 consecutive 4x4 matrices flattened row-major into 64
@@ -53,7 +56,7 @@ __all__ = [
     "bf16_bits_to_f64", "bf16_round", "f64_to_bf16_bits",
     "token_positions", "rope_omega", "rope_table_f32", "rope3d", "rope3d_pos",
     "quantise", "dequant", "dequant_bf16", "build_cache",
-    "seg_ends", "attend", "seg_attn", "gqa_attn", "w8a16_linear", "cam_tokens", "cam_kv", "cam_xattn",
+    "values", "seg_ends", "attend", "seg_attn", "seg_attn_bwd", "gqa_attn", "w8a16_linear", "cam_tokens", "cam_kv", "cam_xattn",
 ]
 
 
@@ -64,6 +67,14 @@ __all__ = [
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     """uint16 bfloat16 bit patterns -> float64 values (exact)."""
     return (np.asarray(b).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def values(x) -> np.ndarray:
+    """Tensor values as float64: uint16 arrays are bfloat16 bit patterns,
+    floating-point arrays are taken as they are (finite-difference checks
+    perturb inputs by amounts no bfloat16 can hold)."""
+    x = np.asarray(x)
+    return bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
 
 
 def bf16_round(x) -> np.ndarray:
@@ -128,13 +139,14 @@ def rope_table_f32(axis: int, npos: int):
     return np.cos(phi).astype(np.float32), np.sin(phi).astype(np.float32)
 
 
-def rope3d_pos(x, vid, t, h, w) -> np.ndarray:
+def rope3d_pos(x, vid, t, h, w, inverse=False) -> np.ndarray:
     """Rotate x [L][H][128] (float64) by the 3D RoPE angles of each token.
 
     Channel chunk a (t: [0,16), h: [16,72), w: [72,128)) of width d holds d/2
     pairs (2i, 2i+1); pair i turns by phi = p_a * omega_i:
         (x0, x1) -> (x0 cos phi - x1 sin phi, x0 sin phi + x1 cos phi).
-    Text tokens (vid False) are left unchanged.
+    Text tokens (vid False) are left unchanged.  inverse=True turns by -phi,
+    the transpose of the rotation (how a gradient goes back through it).
     """
     x = np.asarray(x, dtype=np.float64)
     out = x.copy()
@@ -147,7 +159,7 @@ def rope3d_pos(x, vid, t, h, w) -> np.ndarray:
         off, d = AXIS_OFFSETS[a], AXES[a]
         phi = pos[a][vid].astype(np.float64)[:, None] * rope_omega(a)[None, :]
         c = np.cos(phi)[:, None, :]
-        s = np.sin(phi)[:, None, :]
+        s = -np.sin(phi)[:, None, :] if inverse else np.sin(phi)[:, None, :]
         x0 = xv[:, :, off:off + d:2]
         x1 = xv[:, :, off + 1:off + d:2]
         ov[:, :, off:off + d:2] = x0 * c - x1 * s
@@ -281,10 +293,10 @@ def seg_attn(q_bits, k_new_bits, v_new_bits, new_segs, k_codes, v_codes, k_scale
         Kc = deq(k_codes[h, :Lc], k_scale[h, :Lc]) if Lc else np.zeros((0, D))
         Vc = deq(v_codes[h, :Lc], v_scale[h, :Lc]) if Lc else np.zeros((0, D))
         kmax = int(ends[seg_of.max()]) if len(rows) else 0
-        kn = bf16_bits_to_f64(k_new_bits[:kmax, h:h + 1, :])
+        kn = values(k_new_bits[:kmax, h:h + 1, :])
         Kn = rnd(rope3d_pos(kn, *(p[:kmax] for p in pos)))[:, 0, :]
-        Vn = bf16_bits_to_f64(v_new_bits[:kmax, h, :])
-        qs = bf16_bits_to_f64(q[rows, h:h + 1, :])
+        Vn = values(v_new_bits[:kmax, h, :])
+        qs = values(q[rows, h:h + 1, :])
         Qr = rnd(rope3d_pos(qs, *(p[rows] for p in pos)))[:, 0, :]
         for a in np.unique(seg_of):
             mine = np.nonzero(seg_of == a)[0]
@@ -304,6 +316,74 @@ def seg_attn(q_bits, k_new_bits, v_new_bits, new_segs, k_codes, v_codes, k_scale
                 out[r, hi] = o
                 lse[hi, r] = l
     return out, lse
+
+
+def seg_attn_bwd(q_bits, k_bits, v_bits, do_bits, segs, sm_scale, rows=None, heads=None,
+                 bf16_operands=True, want_kv=True, block=None):
+    """Gradients of packed segment-causal attention (training direction).
+
+    The packed training sequence of the segment-forcing LoRA recipe
+    ([HW] section 2.3: packed sequences of up to 360,000 tokens) is a chain of
+    segments with the block-causal mask of seg_attn and no cache: query i of
+    segment a attends to the tokens of segments 0..a.  For a loss whose
+    gradient with respect to the attention output is dO, the chain rule
+    through softmax attention gives, per head, with the allowed keys only:
+        S = sm_scale Qr Kr^T,  P = softmax_row(S),  O = P V
+        dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
+        dS = P * (dP - D),  dQr = sm_scale dS Kr,  dKr = sm_scale dS^T Qr
+    and through the rotation (Qr = R q, Kr = R k, R orthogonal per token):
+        dq = R^T dQr,  dk = R^T dKr.
+    Reading: the bf16 rounding of the rotated q and k (bf16_operands) is a
+    cast whose derivative is taken as the identity; P and every sum are exact.
+
+    q, k, v, dO: [Ln][H][128], bf16 bits (uint16) or float64 values; q and k
+    before RoPE.  Returns (dq, dk, dv): dq [len(rows)][len(heads)][128] and,
+    with want_kv, dk and dv [Ln][len(heads)][128] (else None), float64.
+    """
+    q = np.asarray(q_bits)
+    Ln, H, _ = q.shape
+    heads = list(range(H)) if heads is None else list(heads)
+    rows = np.arange(Ln) if rows is None else np.asarray(rows, dtype=np.int64)
+    ends = seg_ends(segs)
+    assert ends[-1] == Ln, "token counts disagree with the segment descriptors"
+    pos = token_positions(segs)
+    rnd = bf16_round if bf16_operands else (lambda a: a)
+    sc = float(sm_scale)
+    # query rows whose softmax rows are needed: all of them for dk and dv
+    need = np.arange(Ln) if want_kv else rows
+    seg_of = np.searchsorted(ends, need, side="right")
+    dq_r = np.zeros((Ln, len(heads), D))
+    dk_r = np.zeros((Ln, len(heads), D)) if want_kv else None
+    dv = np.zeros((Ln, len(heads), D)) if want_kv else None
+    for hi, h in enumerate(heads):
+        Qr = rnd(rope3d_pos(values(q[:, h:h + 1, :]), *pos))[:, 0, :]
+        Kr = rnd(rope3d_pos(values(np.asarray(k_bits)[:, h:h + 1, :]), *pos))[:, 0, :]
+        V = values(np.asarray(v_bits)[:, h, :])
+        dO = values(np.asarray(do_bits)[:, h, :])
+        for a in np.unique(seg_of):
+            mine = need[seg_of == a]
+            e = int(ends[a])
+            K, Va = Kr[:e], V[:e]
+            blk = block or int(max(8, min(256, (1 << 23) // max(1, e))))
+            for lo in range(0, len(mine), blk):
+                r = mine[lo:lo + blk]
+                S = sc * (Qr[r] @ K.T)
+                E = np.exp(S - S.max(axis=1, keepdims=True))
+                P = E / E.sum(axis=1, keepdims=True)
+                O = P @ Va
+                dP = dO[r] @ Va.T
+                Dr = np.sum(dO[r] * O, axis=1)
+                dS = P * (dP - Dr[:, None])
+                dq_r[r, hi] = sc * (dS @ K)
+                if want_kv:
+                    dk_r[:e, hi] += sc * (dS.T @ Qr[r])
+                    dv[:e, hi] += P.T @ dO[r]
+        del Qr, Kr, V, dO
+    dq = rope3d_pos(dq_r[rows], *(p[rows] for p in pos), inverse=True)
+    if not want_kv:
+        return dq, None, None
+    dk = rope3d_pos(dk_r, *pos, inverse=True)
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------

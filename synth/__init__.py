@@ -31,7 +31,7 @@ import os
 import numpy as np
 
 STREAMS = ("q", "k_new", "v_new", "k_hist", "v_hist", "outlier_idx",
-           "cam_path", "w_k", "w_v", "q_cam")
+           "cam_path", "w_k", "w_v", "q_cam", "d_out")
 BASE_SEED = 20261021
 CHUNK = 1 << 22
 D = 128
@@ -268,6 +268,30 @@ def turn_inputs(k: int, with_cam: bool = True):
         out["w_k"] = bf16_tensor(5, 0, "w_k", (64, cfg.H * D), scale=1.0 / 8.0)
         out["w_v"] = bf16_tensor(5, 0, "w_v", (64, cfg.H * D), scale=1.0 / 8.0)
     return out
+
+
+# Segment-forcing training (huaweicloud blog, section 2.3): sequences packed
+# up to 360,000 tokens.  Reading: one packed sequence is one long video cut
+# into 3 s turns (18 latent frames of 880 tokens plus 256 text tokens each,
+# the turn3s segment shape); 22 turns, 354,112 tokens, fit the packing limit.
+TRAIN_CID = 6
+TRAIN_TURNS = 22
+
+
+def train_segs(n: int = TRAIN_TURNS, n_text: int = 256, T: int = 18, Hg: int = HG, Wg: int = WG):
+    """n consecutive turns of T latent frames each, t0 = T * turn."""
+    return tuple(Seg(n_text, T * i, T, Hg, Wg) for i in range(n))
+
+
+def train_inputs(segs, H: int, inst: int = 0):
+    """q, k, v (pre-RoPE) and the output gradient d_out, [L][H][128] bf16
+    bits, N(0, 1), for a packed training sequence of the given segments."""
+    shp = (seg_tokens(segs), H, D)
+    return dict(segs=tuple(segs), H=H,
+                q=bf16_tensor(TRAIN_CID, inst, "q", shp),
+                k=bf16_tensor(TRAIN_CID, inst, "k_new", shp),
+                v=bf16_tensor(TRAIN_CID, inst, "v_new", shp),
+                d_out=bf16_tensor(TRAIN_CID, inst, "d_out", shp))
 
 
 def random_bf16(seed: int, shape, scale: float = 1.0) -> np.ndarray:
