@@ -198,6 +198,43 @@ int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int6
                                  int n_split);
 
 /*
+ * Backward pass of packed segment-causal attention, for segment-forcing
+ * training on packed sequences (huaweicloud blog, section 2.3: sequences
+ * packed up to 360,000 tokens; the block-causal mask of comfyui-wiki news,
+ * 一个世界，分段生成): the gradients with respect to q, k and v of
+ * nomas_seg_attn in packed mode (several segments, no cache), given dO, the
+ * gradient with respect to its output.  Per head, over the allowed pairs:
+ *   P = exp(s - lse),  dV = P^T dO,  dP = dO V^T,  D_i = <dO_i, out_i>,
+ *   dS = P * (dP - D),  dq = R^T sm_scale dS Kr,  dk = R^T sm_scale dS^T Qr
+ * where Qr, Kr are the rotated bf16 operands of the forward call (rebuilt
+ * bit for bit) and R^T undoes the 3D RoPE rotation; the bf16 rounding of the
+ * rotated q and k is taken as a cast with identity derivative.  P and dS
+ * enter their products as bf16, sums are fp32.
+ * q, k, v: device [L][H][128] bf16, exactly as given to nomas_seg_attn
+ *   (q and k before RoPE).  out, lse: device, the forward's output [L][H][128]
+ *   bf16 and log-sum-exp [H][L] float32 (natural log) for the same
+ *   arguments and sm_scale.  d_out: device [L][H][128] bf16.
+ * dq, dk, dv: device [L][H][128] float32, overwritten (never accumulated).
+ * segs: the packed segments (the forward's new_segs), L = their token count.
+ * workspace: device scratch of at least nomas_seg_attn_bwd_workspace(...)
+ *   bytes, 16-byte aligned, owned by the caller (each segment's tokens laid
+ *   out as 64-token tiles: 124,928 bytes per tile and head); two calls in
+ *   flight must not share one.  Pointers 16-byte aligned (lse 4).
+ * Errors as nomas_seg_attn; L * H <= NOMAS_MAX_TOKEN_HEADS.
+ */
+int nomas_seg_attn_bwd(const nomas_bf16* q, const nomas_bf16* k, const nomas_bf16* v,
+                       const nomas_bf16* out, const float* lse, const nomas_bf16* d_out,
+                       const nomas_seg* segs, int n_segs, int H, float sm_scale,
+                       float* dq, float* dk, float* dv, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Workspace bytes nomas_seg_attn_bwd needs: H * 124,928 * (sum over the
+ * segments of ceil(tokens / 64)); or a negative error code.  Host only.
+ */
+int64_t nomas_seg_attn_bwd_workspace(const nomas_seg* segs, int n_segs, int H);
+
+/*
  * Attention of one decoder window with grouped key/value heads.  The
  * PixelUMM decoder has 32 query heads and 8 KV heads over a 4096-wide hidden
  * state and reconstructs RGB from 4 x 16 x 16 tubelets on 10-latent-frame

@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     EHIP, ECAPACITY, EINVAL, EUNSUPPORTED, HEAD_DIM, MAX_CAM, MAX_SEGS, MAX_SEL_RANGES, MAX_SPLIT, OK, SM_SCALE,
     SYMBOLS,
     NomasError, Seg, cam_tokens, cam_xattn, gqa_attn, gqa_attn_workspace, kv_quant_append, lib, rope3d, rope_table, seg_array,
-    seg_attn, seg_attn_workspace, seg_tokens, sel_arrays, strerror, version, w8a16_linear, w8a16_linear_workspace,
+    seg_attn, seg_attn_bwd, seg_attn_bwd_workspace, seg_attn_workspace, seg_tokens, sel_arrays, strerror, version, w8a16_linear, w8a16_linear_workspace,
 )

@@ -26,6 +26,7 @@ SM_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
 SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_workspace",
            "nomas_seg_attn_sel", "nomas_seg_attn_sel_workspace", "nomas_gqa_attn", "nomas_gqa_attn_workspace",
+           "nomas_seg_attn_bwd", "nomas_seg_attn_bwd_workspace",
            "nomas_w8a16_linear", "nomas_w8a16_linear_workspace",
            "nomas_cam_tokens", "nomas_cam_xattn", "nomas_rope_table", "nomas_strerror", "nomas_version")
 
@@ -69,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.nomas_gqa_attn.argtypes = [_P, _P, _P, _I64, _I, _I, _F, _P, _P, _P, _I64, _P]
         L.nomas_gqa_attn_workspace.argtypes = [_I64, _I, _I]
         L.nomas_gqa_attn_workspace.restype = _I64
+        L.nomas_seg_attn_bwd.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(Seg), _I, _I, _F, _P, _P, _P, _P,
+                                         _I64, _P]
+        L.nomas_seg_attn_bwd_workspace.argtypes = [ctypes.POINTER(Seg), _I, _I]
+        L.nomas_seg_attn_bwd_workspace.restype = _I64
         L.nomas_w8a16_linear.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _P]
         L.nomas_w8a16_linear_workspace.argtypes = [_I64, _I64]
         L.nomas_w8a16_linear_workspace.restype = _I64
@@ -80,6 +85,7 @@ def lib() -> ctypes.CDLL:
         L.nomas_version.argtypes = []
         L.nomas_version.restype = ctypes.c_char_p
         for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_sel", "nomas_gqa_attn",
+                     "nomas_seg_attn_bwd",
                      "nomas_w8a16_linear",
                      "nomas_cam_tokens",
                      "nomas_cam_xattn", "nomas_rope_table"):
@@ -255,6 +261,44 @@ def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
                                         _ptr(workspace), workspace.numel(), _stream(stream)),
                "nomas_seg_attn_sel")
     return out
+
+
+def seg_attn_bwd_workspace(segs, H: int) -> int:
+    """Bytes of device workspace seg_attn_bwd needs (host only)."""
+    arr, n = seg_array(segs)
+    nbytes = lib().nomas_seg_attn_bwd_workspace(arr, n, int(H))
+    if nbytes < 0:
+        raise NomasError(int(nbytes), "nomas_seg_attn_bwd_workspace")
+    return int(nbytes)
+
+
+def seg_attn_bwd(q, k, v, out, lse, d_out, segs, sm_scale: float = SM_SCALE, dq=None, dk=None, dv=None,
+                 workspace=None, stream=None):
+    """Gradients of packed segment-causal attention (seg_attn with several
+    segments and no cache): q, k (before RoPE), v, the forward's out and lse,
+    and d_out; returns (dq, dk, dv), float32 [L][H][128]."""
+    import torch
+    L, H = q.shape[0], q.shape[1]
+    shp = (seg_tokens(segs), H, HEAD_DIM)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (d_out, "d_out")):
+        _dev(t, name, shp)
+    _dev(lse, "lse", (H, L), 4)
+    grads = []
+    for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if g is None:
+            g = torch.empty(shp, dtype=torch.float32, device=q.device)
+        _dev(g, name, shp, 4)
+        grads.append(g)
+    need = seg_attn_bwd_workspace(segs, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device uint8 tensor")
+    arr, n = seg_array(segs)
+    _check(lib().nomas_seg_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), arr, n, H,
+                                    float(sm_scale), _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)), "nomas_seg_attn_bwd")
+    return tuple(grads)
 
 
 def gqa_attn_workspace(L: int, Hq: int, Hkv: int) -> int:

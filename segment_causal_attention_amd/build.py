@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnomas.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "rope_tables.hip", "kv_quant.hip", "rope3d.hip", "seg_attn.hip", "cam_xattn.hip", "w8a16.hip"]
+SOURCES = ["api.hip", "rope_tables.hip", "kv_quant.hip", "rope3d.hip", "seg_attn.hip", "cam_xattn.hip", "w8a16.hip",
+           "seg_attn_bwd.hip"]
 # The attention kernels take maxima with v_max/v_max3; without IEEE mode they
 # need no NaN-quieting copies of every operand.  NaN inputs still propagate to
 # every row that can see them through the products.

@@ -23,6 +23,10 @@ int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, in
 int launch_w8a16(const uint16_t* x, int64_t M, int64_t K, const int8_t* codes, const float* scale, int64_t N,
                  uint16_t* y, void* workspace, hipStream_t stream);
 int64_t w8a16_workspace_bytes(int64_t N, int64_t K);
+int launch_seg_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                        const float* lse, const uint16_t* dout, const SegTable& st, int Ln, int H, float sm_scale,
+                        float* dq, float* dk, float* dv, void* workspace, const RopeTables& rt, hipStream_t stream);
+int64_t seg_attn_bwd_workspace_bytes(const SegTable& st, int H);
 int launch_cam_xattn(const uint16_t* q, int64_t Lq, int H, const float* cam, int Nc, const uint16_t* wk,
                      const uint16_t* wv, float sm_scale, uint16_t* out, hipStream_t stream);
 }  // namespace nomas
@@ -216,6 +220,39 @@ int nomas_seg_attn_sel(const nomas_bf16* q, const nomas_bf16* k_new, const nomas
     return launch_seg_attn(q, k_new, v_new, st, (int)Ln, k_codes, v_codes, k_scale, v_scale, cap, (int)cache_len,
                            sel_off, sel_ranges, H, H, sm_scale, out, lse, n_split, workspace, rt,
                            (hipStream_t)stream);
+}
+
+int64_t nomas_seg_attn_bwd_workspace(const nomas_seg* segs, int n_segs, int H) {
+    if (H < 1) return NOMAS_EINVAL;
+    if (H > kMaxHeads) return NOMAS_EUNSUPPORTED;
+    SegTable st;
+    int64_t Ln = 0;
+    const int rc = build_segs(segs, n_segs, &st, &Ln);
+    if (rc != NOMAS_OK) return rc;
+    if (Ln * H > NOMAS_MAX_TOKEN_HEADS) return NOMAS_EUNSUPPORTED;
+    return seg_attn_bwd_workspace_bytes(st, H);
+}
+
+int nomas_seg_attn_bwd(const nomas_bf16* q, const nomas_bf16* k, const nomas_bf16* v, const nomas_bf16* out,
+                       const float* lse, const nomas_bf16* d_out, const nomas_seg* segs, int n_segs, int H,
+                       float sm_scale, float* dq, float* dk, float* dv, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+    if (!q || !k || !v || !out || !lse || !d_out || !dq || !dk || !dv) return NOMAS_EINVAL;
+    if (H < 1 || !finite_pos(sm_scale)) return NOMAS_EINVAL;
+    if (!al16(q) || !al16(k) || !al16(v) || !al16(out) || !al16(d_out) || !al4(lse)) return NOMAS_EINVAL;
+    if (!al16(dq) || !al16(dk) || !al16(dv)) return NOMAS_EINVAL;
+    const int64_t need = nomas_seg_attn_bwd_workspace(segs, n_segs, H);
+    if (need < 0) return (int)need;
+    SegTable st;
+    int64_t Ln = 0;
+    build_segs(segs, n_segs, &st, &Ln);
+    if (Ln == 0) return NOMAS_OK;
+    if (!workspace || !al16(workspace) || workspace_bytes < need) return NOMAS_EINVAL;
+    RopeTables rt;
+    const int rc = rope_tables(&rt);
+    if (rc != NOMAS_OK) return rc;
+    return launch_seg_attn_bwd(q, k, v, out, lse, d_out, st, (int)Ln, H, sm_scale, dq, dk, dv, workspace, rt,
+                               (hipStream_t)stream);
 }
 
 // decoder window attention: one all-text segment (no rotation), no cache,

@@ -1,0 +1,552 @@
+// Backward pass of packed segment-causal attention, for gfx950.
+//
+// What it computes.  Segment-forcing training packs a long video into one
+// sequence of segments (huaweicloud blog, section 2.3: packed length up to
+// 360,000 tokens) under the block-causal mask of the forward pass (comfyui-
+// wiki news page, 一个世界，分段生成): query i of segment a attends to the
+// tokens of segments 0..a.  Given dO, the gradient of the loss with respect to
+// the attention output, and the forward's output O and log-sum-exp, per head
+// and over the allowed pairs only:
+//   S = sm_scale Qr Kr^T,  P = exp(S - lse),  dV = P^T dO,  dP = dO V^T,
+//   D_i = sum_c dO_ic O_ic,  dS = P * (dP - D),
+//   dQr = sm_scale dS Kr,  dKr = sm_scale dS^T Qr,
+// then dq = R^T dQr and dk = R^T dKr back through the 3D RoPE rotation R.
+// Qr and Kr are the rotated bf16 operands of the forward pass, rebuilt here
+// bit for bit; P and dS enter their products as bf16, products accumulate in
+// fp32 and the three gradients are returned in fp32.
+//
+// Layout.  Every segment starts a new 64-token tile, so a tile never mixes
+// segments and the mask is whole tiles: query tiles of segment a see the key
+// tiles of segments 0..a and nothing else.  Padding tokens past a segment's
+// end are zero (keys, values, queries, dO) with lse = +inf, and contribute
+// exactly zero to every gradient, so no kernel masks anything.  A pack kernel
+// writes two images per tile, each a byte image of what an attention kernel
+// wants in LDS:
+//   query tile (71,680 B): Q rows [64][136] and dO rows [64][136] bf16;
+//     Q^T and dO^T [128][72] bf16 with each 16-token chunk in the order
+//     [0-3, 8-11, 4-7, 12-15]; the row padding of Q^T rows 0-15 holds
+//     lse * log2(e) of the tile's tokens, that of dO^T rows 0-15 holds D.
+//   key tile (53,248 B): K rows, V rows [64][136], K^T [128][72] permuted.
+// Row strides are padded by 16 bytes against LDS bank conflicts.
+//
+// Two attention kernels, both on v_mfma_f32_32x32x16_bf16, 8 waves of 32
+// tokens per workgroup, tiles copied into LDS by buffer-to-LDS DMA:
+//   dK/dV kernel, key on the MFMA's N side (one lane column = one key):
+//     S = Q K^T and dP = dO V^T (A = Q, dO rows from LDS; B = the wave's K, V
+//     held in registers), then dV^T += dO^T P and dK^T += Q^T dS (A = dO^T,
+//     Q^T from LDS; B = P, dS straight from the accumulators, which is why
+//     the transposed images carry the chunk permutation).  It walks the
+//     query tiles of its segment and every later one.
+//   dQ kernel, query on the N side: S^T = K Q^T and dP^T = V dO^T (A = K, V
+//     rows; B = the wave's Q, dO in registers), then dQ^T += K^T dS^T.  It
+//     walks the key tiles of segments 0..a.
+// S and dP are recomputed by both kernels instead of exchanging dQ partials
+// between workgroups; the pairs outnumber the tokens by four orders of
+// magnitude, so any per-pair or per-block-pair exchange would be bound by HBM.
+#include <algorithm>
+#include <cstring>
+
+#include "common.hpp"
+
+namespace nomas {
+namespace {
+
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+constexpr int TB = 64;                          // tokens per image tile
+constexpr int RSTR = D + 8;                     // row stride (bf16) of [token][channel] images
+constexpr int CSTR = TB + 8;                    // row stride (bf16) of [channel][token] images
+constexpr int ROWIMG = TB * RSTR * 2;           // 17408
+constexpr int COLIMG = D * CSTR * 2;            // 18432
+constexpr int QI_DO = ROWIMG;                   // query image: dO rows
+constexpr int QI_QT = 2 * ROWIMG;               //              Q^T
+constexpr int QI_DOT = 2 * ROWIMG + COLIMG;     //              dO^T
+constexpr int QIMG = 2 * ROWIMG + 2 * COLIMG;   // 71680
+constexpr int KI_V = ROWIMG;                    // key image: V rows
+constexpr int KI_KT = 2 * ROWIMG;               //            K^T
+constexpr int KIMG = 2 * ROWIMG + COLIMG;       // 53248
+constexpr int QIMG_KB = QIMG / 1024;            // 70 one-kilobyte DMA copies
+constexpr int KIMG_KB = KIMG / 1024;            // 52
+constexpr int PAD = 2 * TB;                     // byte offset of the padding in a [channel][token] row
+static_assert(QIMG % 1024 == 0 && KIMG % 1024 == 0, "tile images are copied in 1 KB pieces");
+
+constexpr int NW = 8;                           // waves per workgroup (2 per SIMD)
+constexpr int NT = NW * 64;
+constexpr int WT = 32;                          // tokens per wave
+constexpr int WG_TILES = NW * WT / TB;          // image tiles per workgroup (4)
+constexpr int KBUF = 3;                         // key-tile buffers of the dQ kernel
+constexpr int QBUF = 2;                         // query-tile buffers of the dK/dV kernel
+constexpr int PACK_NT = 256;
+
+// position of token k of a tile in a permuted [channel][token] row
+__device__ __forceinline__ int tperm(int k) {
+    const int w = k & 15;
+    const int p = w < 4 ? w : w < 8 ? w + 4 : w < 12 ? w - 4 : w;
+    return (k & ~15) + p;
+}
+
+__device__ __forceinline__ f16v mma(b8 a, b8 b, f16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ b8 ldfrag(const uint8_t* p) { return *reinterpret_cast<const b8*>(p); }
+
+__device__ __forceinline__ b8 chunk4(const uint32_t* w) {
+    return __builtin_bit_cast(b8, u4v{w[0], w[1], w[2], w[3]});
+}
+
+// one kilobyte of an image into LDS (lane l's 16 bytes at LDS byte m0 + 16 l)
+__device__ __forceinline__ void dma1k(uint32_t m0, uint32_t voff, u4v rs, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void dma_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Segments and tiles as the kernels see them.  Tile t of a head's images
+// belongs to segment a with tile0[a] <= t < tile0[a+1]; workgroups of the
+// attention kernels come in the segment order `order`, segment order[i]
+// owning blocks blk0[i] .. blk0[i+1]-1 (head-major, then its workgroups).
+struct BwdPlan {
+    int32_t nseg, T;                            // segments; tiles per head
+    int32_t tile0[NOMAS_MAX_SEGS + 1];
+    int32_t order[NOMAS_MAX_SEGS];
+    int32_t blk0[NOMAS_MAX_SEGS + 1];
+};
+
+__device__ __forceinline__ int seg_end(const SegDev& s) { return s.start + s.n_text + s.T * s.Hg * s.Wg; }
+
+// ---------------------------------------------------------------------------
+// pack kernel: blockIdx = (tile, head, 0 query image | 1 key image)
+
+struct PackBwdArgs {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float* lse;
+    uint8_t *qimg, *kimg;
+    int32_t Ln, H;
+    BwdPlan pl;
+    SegTable segs;
+    RopeTables rt;
+};
+static_assert(sizeof(PackBwdArgs) <= 4000, "kernel arguments are passed by value");
+
+__global__ __launch_bounds__(PACK_NT) void bwd_pack_kernel(const PackBwdArgs P) {
+    __shared__ __attribute__((aligned(16))) uint16_t ct[2][D * CSTR];   // transposed images
+    __shared__ float pad[2][TB];
+    const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const bool is_q = blockIdx.z == 0;
+    int a = 0;
+    while (a + 1 < P.pl.nseg && P.pl.tile0[a + 1] <= t) ++a;
+    const SegDev& sg = P.segs.s[a];
+    const int x0 = sg.start + (t - P.pl.tile0[a]) * TB;
+    const int end = seg_end(sg);
+    uint8_t* img = is_q ? P.qimg + ((size_t)h * P.pl.T + t) * QIMG : P.kimg + ((size_t)h * P.pl.T + t) * KIMG;
+
+    // thread = (token, quarter of the channels): chunks 4 qd .. 4 qd + 3 of 8 channels
+    const int row = tid >> 2, qd = tid & 3;
+    const int tok = x0 + row;
+    const bool valid = tok < end;
+    const size_t src = ((size_t)(valid ? tok : 0) * P.H + h) * D;
+    uint4 a0[4], a1[4];
+    float dsum = 0.0f;
+    if (is_q) {
+        int tt = 0, hh = 0, ww = 0;
+        if (!(valid && token_pos(P.segs, tok, tt, hh, ww))) tt = hh = ww = 0;   // text: identity rotation
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * qd + j;
+            if (valid) {
+                // queries rotated exactly as the forward kernel rotates them
+                a0[j] = rope_group_f32(reinterpret_cast<const uint4*>(P.q + src)[c], c, tt, hh, ww, P.rt);
+                a1[j] = reinterpret_cast<const uint4*>(P.dout + src)[c];
+                const uint4 ow = reinterpret_cast<const uint4*>(P.o + src)[c];
+                const uint32_t dw[4] = {a1[j].x, a1[j].y, a1[j].z, a1[j].w};
+                const uint32_t owv[4] = {ow.x, ow.y, ow.z, ow.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dsum = fmaf(bf16lo(dw[e]), bf16lo(owv[e]), fmaf(bf16hi(dw[e]), bf16hi(owv[e]), dsum));
+            } else {
+                a0[j] = a1[j] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        dsum += __shfl_xor(dsum, 1);
+        dsum += __shfl_xor(dsum, 2);
+        if (qd == 0) {
+            pad[0][row] = valid ? P.lse[(size_t)h * P.Ln + tok] * 1.44269504088896341f : INFINITY;
+            pad[1][row] = valid ? dsum : 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * qd + j;
+            // keys rotated in float64 exactly as the forward pack kernel does
+            a0[j] = valid ? rope_chunk_f64(reinterpret_cast<const uint4*>(P.k + src)[c], c, tok, P.segs, P.rt)
+                          : make_uint4(0, 0, 0, 0);
+            a1[j] = valid ? reinterpret_cast<const uint4*>(P.v + src)[c] : make_uint4(0, 0, 0, 0);
+        }
+    }
+    // the two row images (Q, dO or K, V), padding zero
+    uint4* r0 = reinterpret_cast<uint4*>(img + row * RSTR * 2);
+    uint4* r1 = reinterpret_cast<uint4*>(img + ROWIMG + row * RSTR * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        r0[4 * qd + j] = a0[j];
+        r1[4 * qd + j] = a1[j];
+    }
+    if (qd == 0) {
+        r0[D / 8] = make_uint4(0, 0, 0, 0);
+        r1[D / 8] = make_uint4(0, 0, 0, 0);
+    }
+    // transposed images through LDS (Q^T, dO^T or K^T)
+    const int ncol = is_q ? 2 : 1;
+    const int pc = tperm(row);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t w0[4] = {a0[j].x, a0[j].y, a0[j].z, a0[j].w};
+        const uint32_t w1[4] = {a1[j].x, a1[j].y, a1[j].z, a1[j].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int ch = 8 * (4 * qd + j) + e;
+            ct[0][ch * CSTR + pc] = (uint16_t)(w0[e >> 1] >> (16 * (e & 1)));
+            if (is_q) ct[1][ch * CSTR + pc] = (uint16_t)(w1[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+    __syncthreads();
+    // padding of the transposed rows: rows 0-15 of Q^T carry lse*log2(e) of
+    // tokens 4i..4i+3, those of dO^T carry D; the rest zero
+    if (tid < ncol * D) {
+        const int m = tid / D, i = tid % D;
+        uint4 pv = make_uint4(0, 0, 0, 0);
+        if (is_q && i < TB / 4)
+            pv = make_uint4(__float_as_uint(pad[m][4 * i]), __float_as_uint(pad[m][4 * i + 1]),
+                            __float_as_uint(pad[m][4 * i + 2]), __float_as_uint(pad[m][4 * i + 3]));
+        *reinterpret_cast<uint4*>(&ct[m][i * CSTR + TB]) = pv;
+    }
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(img + 2 * ROWIMG);
+    const uint4* srcl = reinterpret_cast<const uint4*>(&ct[0][0]);
+    for (int i = tid; i < ncol * COLIMG / 16; i += PACK_NT) dst[i] = srcl[i];
+}
+
+// ---------------------------------------------------------------------------
+// attention kernels
+
+struct BwdArgs {
+    const uint8_t* qimg;
+    const uint8_t* kimg;
+    float *dq, *dk, *dv;
+    int32_t Ln, H;
+    float c;                        // sm_scale * log2(e)
+    float sm_scale;
+    BwdPlan pl;
+    SegTable segs;
+    RopeTables rt;
+};
+static_assert(sizeof(BwdArgs) <= 4000, "kernel arguments are passed by value");
+
+// Workgroup -> (segment, head, first tile).  Wave w takes tile tile0 + 4 wg +
+// w/2, tokens 32 (w%2) .. +32 of it; waves past the segment's last tile
+// repeat that tile and store nothing.
+struct WgPos {
+    int a, head, tile, row;
+    bool live;
+};
+__device__ __forceinline__ WgPos wg_pos(const BwdPlan& pl, int wave) {
+    const int b = blockIdx.x;
+    int i = 0;
+    while (i + 1 < pl.nseg && pl.blk0[i + 1] <= b) ++i;
+    WgPos p;
+    p.a = __builtin_amdgcn_readfirstlane(pl.order[i]);
+    const int nt = pl.tile0[p.a + 1] - pl.tile0[p.a];
+    const int nwg = (nt + WG_TILES - 1) / WG_TILES;
+    const int local = b - pl.blk0[i];
+    p.head = __builtin_amdgcn_readfirstlane(local / nwg);
+    const int wg = local - p.head * nwg;
+    const int tl = WG_TILES * wg + (wave >> 1);
+    p.live = tl < nt;
+    p.tile = pl.tile0[p.a] + min(tl, nt - 1);
+    p.row = WT * (wave & 1);
+    return p;
+}
+
+// The transpose of the RoPE rotation applied to 4 channels 8 grp + 4 g .. +3
+// (two pairs) of a token at (t, h, w), text tokens unchanged; x scaled by s.
+__device__ __forceinline__ float4 unrotate4(float4 x, float s, bool vid, int grp, int g, int t, int h, int w,
+                                            const RopeTables& rt) {
+    x.x *= s; x.y *= s; x.z *= s; x.w *= s;
+    if (!vid) return x;
+    const float4 cs = *reinterpret_cast<const float4*>(rt.f32 + rope_entry(grp, t, h, w) + 2 * g);
+    return make_float4(x.x * cs.x + x.y * cs.y, x.y * cs.x - x.x * cs.y,
+                       x.z * cs.z + x.w * cs.w, x.w * cs.z - x.z * cs.w);
+}
+
+// dO^T / Q^T / K^T fragment: channel row `ch`, 16-token chunk `k16`, lane half g
+__device__ __forceinline__ b8 colfrag(const uint8_t* img, int ch, int k16, int g) {
+    return ldfrag(img + ch * CSTR * 2 + 32 * k16 + 16 * g);
+}
+// Q / dO / K / V row fragment: token row `r`, channels 16 s + 8 g
+__device__ __forceinline__ b8 rowfrag(const uint8_t* img, int r, int s, int g) {
+    return ldfrag(img + r * RSTR * 2 + 32 * s + 16 * g);
+}
+
+// ---- dQ: lane = query --------------------------------------------------------
+
+__global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[KBUF * KIMG];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const WgPos wp = wg_pos(A.pl, wave);
+    const int qrow = wp.row + l32;
+    const uint8_t* qi = A.qimg + ((size_t)wp.head * A.pl.T + wp.tile) * QIMG;
+    b8 qf[8], df[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        qf[s] = rowfrag(qi, qrow, s, g);
+        df[s] = rowfrag(qi + QI_DO, qrow, s, g);
+    }
+    const float lse2 = *reinterpret_cast<const float*>(qi + QI_QT + (qrow >> 2) * CSTR * 2 + PAD + 4 * (qrow & 3));
+    const float dd = *reinterpret_cast<const float*>(qi + QI_DOT + (qrow >> 2) * CSTR * 2 + PAD + 4 * (qrow & 3));
+    f16v acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+    // key tiles 0 .. tile0[a+1]-1: segments 0..a
+    const int nk = __builtin_amdgcn_readfirstlane(A.pl.tile0[wp.a + 1]);
+    const uint64_t kbase = (uint64_t)(uintptr_t)A.kimg + (uint64_t)wp.head * A.pl.T * KIMG;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto copy = [&](int j) {
+        const uint64_t base = kbase + (uint64_t)min(j, nk - 1) * KIMG;
+        const u4v rs = {(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, (uint32_t)KIMG, 0x00020000u};
+        const uint32_t m = lds0 + (uint32_t)(j % KBUF) * KIMG;
+#pragma unroll
+        for (int p = 0; p < (KIMG_KB + NW - 1) / NW; ++p) {
+            const int kb = wv + NW * p;
+            if (kb < KIMG_KB) dma1k(m + 1024 * kb, 16u * lane, rs, 1024u * kb);
+        }
+    };
+    const float c = A.c;
+    copy(0);
+    copy(1);
+    for (int j = 0; j < nk; ++j) {
+        // this wave's copies of tile j have landed once at most those of tile j+1 are in flight
+        if (wv < KIMG_KB % NW) dma_wait<(KIMG_KB + NW - 1) / NW>();
+        else dma_wait<KIMG_KB / NW>();
+        lds_barrier();
+        copy(j + 2);        // into the buffer of tile j-1, which every wave has finished
+        const uint8_t* K = lds + (j % KBUF) * KIMG;
+        f16v s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.0f;
+        // S^T = K Q^T and dP^T = V dO^T: key blocks kb (keys 32 kb + l32 of the A rows)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i & 1] = mma(rowfrag(K, 32 * (i & 1) + l32, i >> 1, g), qf[i >> 1], s[i & 1]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            dp[i & 1] = mma(rowfrag(K + KI_V, 32 * (i & 1) + l32, i >> 1, g), df[i >> 1], dp[i & 1]);
+        // dS = P (dP - D), P = 2^(S c - lse2); register r of block kb holds key
+        // 32 kb + 8 (r/4) + 4 g + r%4, so 16-key chunk ch = 2 kb + r/8
+        uint32_t pk[16];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -lse2));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -lse2));
+                pk[8 * kb + r / 2] = pack_bf16(p0 * (dp[kb][r] - dd), p1 * (dp[kb][r + 1] - dd));
+            }
+        // dQ^T += K^T dS^T: channel blocks db, 16-key chunks ch
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            acc[i & 3] = mma(colfrag(K + KI_KT, 32 * (i & 3) + l32, i >> 2, g), chunk4(pk + 4 * (i >> 2)), acc[i & 3]);
+    }
+    dma_wait<0>();
+
+    // epilogue: dq = R^T (sm_scale dQ^T), fp32
+    const SegDev& sg = A.segs.s[wp.a];
+    const int tok = sg.start + (wp.tile - A.pl.tile0[wp.a]) * TB + qrow;
+    if (wp.live && tok < seg_end(sg)) {
+        int t = 0, h = 0, w = 0;
+        const bool vid = token_pos(A.segs, tok, t, h, w);
+        float* dst = A.dq + ((size_t)tok * A.H + wp.head) * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 x = make_float4(acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]);
+                *reinterpret_cast<float4*>(dst + 32 * db + 8 * i + 4 * g) =
+                    unrotate4(x, A.sm_scale, vid, 4 * db + i, g, t, h, w, A.rt);
+            }
+    }
+}
+
+// ---- dK, dV: lane = key ------------------------------------------------------
+
+__global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[QBUF * QIMG];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const WgPos wp = wg_pos(A.pl, wave);
+    const int krow = wp.row + l32;
+    const uint8_t* ki = A.kimg + ((size_t)wp.head * A.pl.T + wp.tile) * KIMG;
+    b8 kf[8], vf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        kf[s] = rowfrag(ki, krow, s, g);
+        vf[s] = rowfrag(ki + KI_V, krow, s, g);
+    }
+    f16v dk[4], dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.0f;
+
+    // query tiles tile0[a] .. T-1: segment a and every later one
+    const int q0 = __builtin_amdgcn_readfirstlane(A.pl.tile0[wp.a]);
+    const int nq = __builtin_amdgcn_readfirstlane(A.pl.T - q0);
+    const uint64_t qbase = (uint64_t)(uintptr_t)A.qimg + ((uint64_t)wp.head * A.pl.T + q0) * QIMG;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto copy = [&](int j) {
+        const uint64_t base = qbase + (uint64_t)min(j, nq - 1) * QIMG;
+        const u4v rs = {(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, (uint32_t)QIMG, 0x00020000u};
+        const uint32_t m = lds0 + (uint32_t)(j % QBUF) * QIMG;
+#pragma unroll
+        for (int p = 0; p < (QIMG_KB + NW - 1) / NW; ++p) {
+            const int kb = wv + NW * p;
+            if (kb < QIMG_KB) dma1k(m + 1024 * kb, 16u * lane, rs, 1024u * kb);
+        }
+    };
+    const float c = A.c;
+    copy(0);
+    for (int j = 0; j < nq; ++j) {
+        dma_wait<0>();
+        lds_barrier();
+        if (j + 1 < nq) copy(j + 1);    // into the buffer of tile j-1, which every wave has finished
+        const uint8_t* Q = lds + (j % QBUF) * QIMG;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f16v s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
+            // S = Q K^T, dP = dO V^T for queries 32 u .. +32 of the tile
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s = mma(rowfrag(Q, 32 * u + l32, i, g), kf[i], s);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dp = mma(rowfrag(Q + QI_DO, 32 * u + l32, i, g), vf[i], dp);
+            // register r holds query 32 u + 8 (r/4) + 4 g + r%4: its lse2 and D
+            // sit in the padding of transposed row 8 u + 2 (r/4) + g
+            uint32_t pp[8], ps[8];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int pr = 8 * u + 2 * r4 + g;
+                const float4 l4 = *reinterpret_cast<const float4*>(Q + QI_QT + pr * CSTR * 2 + PAD);
+                const float4 d4 = *reinterpret_cast<const float4*>(Q + QI_DOT + pr * CSTR * 2 + PAD);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int j2 = 0; j2 < 4; j2 += 2) {
+                    const int r = 4 * r4 + j2;
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[j2]));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -lv[j2 + 1]));
+                    pp[r / 2] = pack_bf16(p0, p1);
+                    ps[r / 2] = pack_bf16(p0 * (dp[r] - dvv[j2]), p1 * (dp[r + 1] - dvv[j2 + 1]));
+                }
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS: channel blocks db, 16-query chunks 2 u + ch
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    dv[db] = mma(colfrag(Q + QI_DOT, 32 * db + l32, 2 * u + ch, g), chunk4(pp + 4 * ch), dv[db]);
+                    dk[db] = mma(colfrag(Q + QI_QT, 32 * db + l32, 2 * u + ch, g), chunk4(ps + 4 * ch), dk[db]);
+                }
+        }
+    }
+    dma_wait<0>();
+
+    // epilogue: dk = R^T (sm_scale dK^T), dv, fp32
+    const SegDev& sg = A.segs.s[wp.a];
+    const int tok = sg.start + (wp.tile - A.pl.tile0[wp.a]) * TB + krow;
+    if (wp.live && tok < seg_end(sg)) {
+        int t = 0, h = 0, w = 0;
+        const bool vid = token_pos(A.segs, tok, t, h, w);
+        float* dkd = A.dk + ((size_t)tok * A.H + wp.head) * D;
+        float* dvd = A.dv + ((size_t)tok * A.H + wp.head) * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ch = 32 * db + 8 * i + 4 * g;
+                const float4 x = make_float4(dk[db][4 * i], dk[db][4 * i + 1], dk[db][4 * i + 2], dk[db][4 * i + 3]);
+                *reinterpret_cast<float4*>(dkd + ch) = unrotate4(x, A.sm_scale, vid, 4 * db + i, g, t, h, w, A.rt);
+                *reinterpret_cast<float4*>(dvd + ch) =
+                    make_float4(dv[db][4 * i], dv[db][4 * i + 1], dv[db][4 * i + 2], dv[db][4 * i + 3]);
+            }
+    }
+}
+
+// tiles per head and the per-segment tile offsets
+int64_t plan_tiles(const SegTable& st, BwdPlan* pl) {
+    std::memset(pl, 0, sizeof(*pl));
+    pl->nseg = st.n;
+    int64_t t = 0;
+    for (int a = 0; a < st.n; ++a) {
+        pl->tile0[a] = (int32_t)t;
+        const SegDev& s = st.s[a];
+        const int64_t n = (int64_t)s.n_text + (int64_t)s.T * s.Hg * s.Wg;
+        t += (n + TB - 1) / TB;
+    }
+    pl->tile0[st.n] = (int32_t)t;
+    pl->T = (int32_t)t;
+    return t;
+}
+
+// block ranges in the given segment order; returns the block count
+int64_t plan_blocks(BwdPlan* pl, int H, bool late_first) {
+    int64_t b = 0;
+    for (int i = 0; i < pl->nseg; ++i) {
+        const int a = late_first ? pl->nseg - 1 - i : i;
+        pl->order[i] = a;
+        pl->blk0[i] = (int32_t)b;
+        const int nt = pl->tile0[a + 1] - pl->tile0[a];
+        b += (int64_t)H * ((nt + WG_TILES - 1) / WG_TILES);
+    }
+    pl->blk0[pl->nseg] = (int32_t)b;
+    return b;
+}
+
+}  // namespace
+
+int64_t seg_attn_bwd_workspace_bytes(const SegTable& st, int H) {
+    BwdPlan pl;
+    return (int64_t)H * plan_tiles(st, &pl) * (QIMG + KIMG);
+}
+
+int launch_seg_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                        const float* lse, const uint16_t* dout, const SegTable& st, int Ln, int H, float sm_scale,
+                        float* dq, float* dk, float* dv, void* workspace, const RopeTables& rt, hipStream_t stream) {
+    BwdPlan pl;
+    const int64_t T = plan_tiles(st, &pl);
+    uint8_t* qimg = static_cast<uint8_t*>(workspace);
+    uint8_t* kimg = qimg + (size_t)H * T * QIMG;
+    PackBwdArgs P{q, k, v, o, dout, lse, qimg, kimg, Ln, H, pl, st, rt};
+    hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)T, (unsigned)H, 2), dim3(PACK_NT), 0, stream, P);
+    BwdArgs A{qimg, kimg, dq, dk, dv, Ln, H, sm_scale * 1.44269504088896341f, sm_scale, pl, st, rt};
+    // dK/dV: early segments (the most query tiles) first
+    const int64_t nb_kv = plan_blocks(&A.pl, H, false);
+    hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)nb_kv), dim3(NT), 0, stream, A);
+    // dQ: late segments (the most key tiles) first
+    const int64_t nb_q = plan_blocks(&A.pl, H, true);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)nb_q), dim3(NT), 0, stream, A);
+    return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
+}
+
+}  // namespace nomas

@@ -234,3 +234,38 @@ def test_w8a16_host_checks():
     assert call(K=96) == nomas.EUNSUPPORTED
     assert call(N=300) == nomas.EUNSUPPORTED
     assert call(M=1 << 20, K=2048) == nomas.EUNSUPPORTED     # x beyond 2 GiB
+
+
+def test_seg_attn_bwd_host_checks():
+    """Backward pass: workspace = H x (tiles) x 124,928 bytes, every segment
+    starting a new 64-token tile; bad arguments are rejected on the host."""
+    L = nomas.lib()
+    P = ctypes.c_void_p
+    sa, n = segs((16, 0, 2, 4, 6), (3, 2, 1, 2, 2), (0, 0, 0, 0, 0), (70, 0, 0, 1, 1))
+    assert L.nomas_seg_attn_bwd_workspace(sa, n, 2) == 2 * (1 + 1 + 0 + 2) * 124928
+    assert L.nomas_seg_attn_bwd_workspace(sa, n, 0) == nomas.EINVAL
+    assert L.nomas_seg_attn_bwd_workspace(sa, 0, 2) == nomas.EINVAL
+    assert L.nomas_seg_attn_bwd_workspace(sa, n, 300) == nomas.EUNSUPPORTED
+    big, nb = segs((1 << 20, 0, 0, 1, 1))
+    assert L.nomas_seg_attn_bwd_workspace(big, nb, 16) == nomas.EUNSUPPORTED   # L * H beyond the limit
+    need = L.nomas_seg_attn_bwd_workspace(sa, n, 2)
+    good = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, segs=sa, n=n, H=2, sm=0.088,
+                dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.nomas_seg_attn_bwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["o"]), P(a["lse"]), P(a["do"]), a["segs"],
+                                    a["n"], a["H"], a["sm"], P(a["dq"]), P(a["dk"]), P(a["dv"]), P(a["ws"]), a["wsb"],
+                                    None)
+
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"):
+        assert call(**{name: None}) == nomas.EINVAL, name
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv", "ws"):
+        assert call(**{name: FAKE + 4}) == nomas.EINVAL, name
+    assert call(lse=FAKE + 2) == nomas.EINVAL
+    assert call(sm=0.0) == nomas.EINVAL and call(sm=float("nan")) == nomas.EINVAL
+    assert call(H=0) == nomas.EINVAL
+    assert call(wsb=need - 1) == nomas.EINVAL
+    assert call(n=nomas.MAX_SEGS + 1) == nomas.EUNSUPPORTED
+    empty, ne = segs((0, 0, 0, 0, 0))
+    assert call(segs=empty, n=ne, ws=None, wsb=0) == nomas.OK      # no tokens: nothing to do
