@@ -241,6 +241,9 @@ def workloads():
                   (63,360 x 2048 -> 6144 and -> 8192; median of 10), with the
                   dequantisation pass alone and torch's BF16 matmul on the
                   dequantised weights as context
+      train-fwd, train-bwd  segment-forcing training: 22 packed 3 s turns
+                  (354,112 tokens, block-causal) with 2 heads (one GPU's share
+                  of a head-sharded layer), forward and backward (median of 5)
     History caches are built on the GPU by rope3d + kv_quant_append (bit-exact
     to the oracle's quantiser)."""
     import numpy as np
@@ -436,6 +439,43 @@ def workloads():
     ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
                                       stream=stream), 5)
     attn_line("fullcache-h2", ms, H, cfg.Lq, cfg.Lc + cfg.Lq, dict(note="heads 0-1 of the full-cache inputs"))
+    del q, k, v, out, ws, cache
+
+    # ---- segment-forcing training: packed forward and backward
+    log("workload train-fwd / train-bwd: 22 packed 3 s turns, 2 heads")
+    segs = synth.train_segs()
+    H = 2
+    inp = synth.train_inputs(segs, H)
+    q, k, v, do = (d16(inp[x]) for x in ("q", "k", "v", "d_out"))
+    del inp
+    L = q.shape[0]
+    n_a = [s.ntok for s in segs]
+    pairs = H * sum(n_a[a] * sum(n_a[:a + 1]) for a in range(len(n_a)))
+    out = torch.empty_like(q)
+    lse = torch.empty((H, L), dtype=torch.float32, device=dev)
+    ws = torch.empty(nomas.seg_attn_workspace(segs, 0, H), dtype=torch.uint8, device=dev)
+    ms_f = timed(lambda: nomas.seg_attn(q, k, v, segs, cache_len=0, sm_scale=sm, out=out, lse=lse, workspace=ws,
+                                        stream=stream), 5)
+    fl_f = 4.0 * 128 * pairs
+    tf_f = fl_f / (ms_f * 1e-3) / 1e12
+    emit("train-fwd", metric="attention TFLOP/s", value=round(tf_f, 2), unit="TFLOP/s", ms=round(ms_f, 3),
+         pct_of_peak=round(100 * tf_f / PEAK_BF16_TFLOPS, 2), heads=H, tokens=L, segments=len(segs),
+         allowed_pairs=pairs, algorithmic_flop=fl_f)
+    del ws
+    wsb = torch.empty(nomas.seg_attn_bwd_workspace(segs, H), dtype=torch.uint8, device=dev)
+    g = [torch.empty((L, H, 128), dtype=torch.float32, device=dev) for _ in range(3)]
+    ms_b = timed(lambda: nomas.seg_attn_bwd(q, k, v, out, lse, do, segs, sm_scale=sm, dq=g[0], dk=g[1], dv=g[2],
+                                            workspace=wsb, stream=stream), 5)
+    # algorithmic: five products of 2 x 128 flops per allowed pair (S recomputed once);
+    # the kernels execute seven (S and dP in both the dK/dV and the dQ kernel)
+    fl_b = 10.0 * 128 * pairs
+    tf_b = fl_b / (ms_b * 1e-3) / 1e12
+    emit("train-bwd", metric="attention backward TFLOP/s", value=round(tf_b, 2), unit="TFLOP/s",
+         ms=round(ms_b, 3), pct_of_peak=round(100 * tf_b / PEAK_BF16_TFLOPS, 2), heads=H, tokens=L,
+         segments=len(segs), allowed_pairs=pairs, algorithmic_flop=fl_b,
+         executed_mfma_flop=14.0 * 128 * pairs,
+         executed_pct_of_peak=round(100 * 1.4 * tf_b / PEAK_BF16_TFLOPS, 2),
+         fwd_plus_bwd_ms=round(ms_f + ms_b, 3))
 
 
 def cpu_baseline(inp, cfg, sm):

@@ -25,7 +25,7 @@
 //   query tile (71,680 B): Q rows [64][136] and dO rows [64][136] bf16;
 //     Q^T and dO^T [128][72] bf16 with each 16-token chunk in the order
 //     [0-3, 8-11, 4-7, 12-15]; the row padding of Q^T rows 0-15 holds
-//     lse * log2(e) of the tile's tokens, that of dO^T rows 0-15 holds D.
+//     -lse / sm_scale of the tile's tokens, that of dO^T rows 0-15 holds -D.
 //   key tile (53,248 B): K rows, V rows [64][136], K^T [128][72] permuted.
 // Row strides are padded by 16 bytes against LDS bank conflicts.
 //
@@ -128,6 +128,7 @@ struct PackBwdArgs {
     const float* lse;
     uint8_t *qimg, *kimg;
     int32_t Ln, H;
+    float sm_scale;
     BwdPlan pl;
     SegTable segs;
     RopeTables rt;
@@ -176,8 +177,8 @@ __global__ __launch_bounds__(PACK_NT) void bwd_pack_kernel(const PackBwdArgs P) 
         dsum += __shfl_xor(dsum, 1);
         dsum += __shfl_xor(dsum, 2);
         if (qd == 0) {
-            pad[0][row] = valid ? P.lse[(size_t)h * P.Ln + tok] * 1.44269504088896341f : INFINITY;
-            pad[1][row] = valid ? dsum : 0.0f;
+            pad[0][row] = valid ? -P.lse[(size_t)h * P.Ln + tok] / P.sm_scale : -INFINITY;
+            pad[1][row] = valid ? -dsum : 0.0f;
         }
     } else {
 #pragma unroll
@@ -216,8 +217,9 @@ __global__ __launch_bounds__(PACK_NT) void bwd_pack_kernel(const PackBwdArgs P) 
         }
     }
     __syncthreads();
-    // padding of the transposed rows: rows 0-15 of Q^T carry lse*log2(e) of
-    // tokens 4i..4i+3, those of dO^T carry D; the rest zero
+    // padding of the transposed rows: rows 0-15 of Q^T carry -lse/sm_scale of
+    // tokens 4i..4i+3 (so that P = 2^(sm_scale log2(e) (s + pad))), those of
+    // dO^T carry -D; the rest zero
     if (tid < ncol * D) {
         const int m = tid / D, i = tid % D;
         uint4 pv = make_uint4(0, 0, 0, 0);
@@ -248,13 +250,15 @@ struct BwdArgs {
 };
 static_assert(sizeof(BwdArgs) <= 4000, "kernel arguments are passed by value");
 
-// Workgroup -> (segment, head, first tile).  Wave w takes tile tile0 + 4 wg +
-// w/2, tokens 32 (w%2) .. +32 of it; waves past the segment's last tile
-// repeat that tile and store nothing.
+// Workgroup -> (segment, head, first tile).  A workgroup of the dQ kernel
+// covers 4 tiles (8 waves), one of the dK/dV kernel 2 tiles (4 waves); wave w
+// takes tile tile0 + NTL wg + w/2, tokens 32 (w%2) .. +32 of it.  Waves past
+// the segment's last tile repeat that tile and store nothing.
 struct WgPos {
     int a, head, tile, row;
     bool live;
 };
+template <int NTL>
 __device__ __forceinline__ WgPos wg_pos(const BwdPlan& pl, int wave) {
     const int b = blockIdx.x;
     int i = 0;
@@ -262,11 +266,11 @@ __device__ __forceinline__ WgPos wg_pos(const BwdPlan& pl, int wave) {
     WgPos p;
     p.a = __builtin_amdgcn_readfirstlane(pl.order[i]);
     const int nt = pl.tile0[p.a + 1] - pl.tile0[p.a];
-    const int nwg = (nt + WG_TILES - 1) / WG_TILES;
+    const int nwg = (nt + NTL - 1) / NTL;
     const int local = b - pl.blk0[i];
     p.head = __builtin_amdgcn_readfirstlane(local / nwg);
     const int wg = local - p.head * nwg;
-    const int tl = WG_TILES * wg + (wave >> 1);
+    const int tl = NTL * wg + (wave >> 1);
     p.live = tl < nt;
     p.tile = pl.tile0[p.a] + min(tl, nt - 1);
     p.row = WT * (wave & 1);
@@ -293,13 +297,33 @@ __device__ __forceinline__ b8 rowfrag(const uint8_t* img, int r, int s, int g) {
     return ldfrag(img + r * RSTR * 2 + 32 * s + 16 * g);
 }
 
+// Nothing is scheduled across this point: it pins the order of the slots of
+// the pipelined loop bodies (one matrix instruction each, plus the LDS read
+// of a later operand and a few vector instructions).
+#define SLOT() __builtin_amdgcn_sched_barrier(0)
+constexpr int FD = 2;               // LDS operand reads issued this many products ahead (dQ)
+constexpr int KFD = 1;              // the same for dK/dV, whose registers are scarcer
+
+// dS of one score in three stages spread over consecutive slots, so that no
+// slot holds a chain of dependent vector instructions:
+//   0: x = s c - lse2, y = dP - D;  1: x = 2^x;  2: p = x, ds = p y
+// t holds the scores in flight (at most 6 consecutive ones: index e % 8).
+struct Stage3 {
+    float x[8], y[8];
+};
+
 // ---- dQ: lane = query --------------------------------------------------------
+//
+// Per key tile and wave (32 queries x 64 keys, 48 products): the products of
+// key block 0 (S^T and dP^T alternating), those of key block 1 with the dS of
+// block 0 in their slots, the dQ^T products of block 0 with the dS of block 1
+// (two scores per slot), then the dQ^T products of block 1.
 
 __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[KBUF * KIMG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
-    const WgPos wp = wg_pos(A.pl, wave);
+    const WgPos wp = wg_pos<WG_TILES>(A.pl, wave);
     const int qrow = wp.row + l32;
     const uint8_t* qi = A.qimg + ((size_t)wp.head * A.pl.T + wp.tile) * QIMG;
     b8 qf[8], df[8];
@@ -308,8 +332,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
         qf[s] = rowfrag(qi, qrow, s, g);
         df[s] = rowfrag(qi + QI_DO, qrow, s, g);
     }
-    const float lse2 = *reinterpret_cast<const float*>(qi + QI_QT + (qrow >> 2) * CSTR * 2 + PAD + 4 * (qrow & 3));
-    const float dd = *reinterpret_cast<const float*>(qi + QI_DOT + (qrow >> 2) * CSTR * 2 + PAD + 4 * (qrow & 3));
+    // lse2 = lse log2(e) and D of this lane's query, from the image padding
+    const float lse2 = -A.c * *reinterpret_cast<const float*>(qi + QI_QT + (qrow >> 2) * CSTR * 2 + PAD + 4 * (qrow & 3));
+    const float dd = -*reinterpret_cast<const float*>(qi + QI_DOT + (qrow >> 2) * CSTR * 2 + PAD + 4 * (qrow & 3));
     f16v acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -332,6 +357,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
         }
     };
     const float c = A.c;
+    const f16v zero = {};
     copy(0);
     copy(1);
     for (int j = 0; j < nk; ++j) {
@@ -341,32 +367,60 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
         lds_barrier();
         copy(j + 2);        // into the buffer of tile j-1, which every wave has finished
         const uint8_t* K = lds + (j % KBUF) * KIMG;
+        // operand of product n: 0-31 S^T / dP^T of key blocks 0 and 1
+        // (even n: K rows, odd n: V rows; channel step (n % 16) / 2), 32-47
+        // dQ^T: channel block (n - 32) % 4, 16-key chunk (n - 32) / 4
+        auto afrag = [&](int n) {
+            if (n < 32) return rowfrag(K + ((n & 1) ? KI_V : 0), 32 * (n >> 4) + l32, (n & 15) >> 1, g);
+            return colfrag(K + KI_KT, 32 * ((n - 32) & 3) + l32, (n - 32) >> 2, g);
+        };
         f16v s[2], dp[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.0f;
-        // S^T = K Q^T and dP^T = V dO^T: key blocks kb (keys 32 kb + l32 of the A rows)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i & 1] = mma(rowfrag(K, 32 * (i & 1) + l32, i >> 1, g), qf[i >> 1], s[i & 1]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            dp[i & 1] = mma(rowfrag(K + KI_V, 32 * (i & 1) + l32, i >> 1, g), df[i >> 1], dp[i & 1]);
-        // dS = P (dP - D), P = 2^(S c - lse2); register r of block kb holds key
-        // 32 kb + 8 (r/4) + 4 g + r%4, so 16-key chunk ch = 2 kb + r/8
         uint32_t pk[16];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -lse2));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -lse2));
-                pk[8 * kb + r / 2] = pack_bf16(p0 * (dp[kb][r] - dd), p1 * (dp[kb][r + 1] - dd));
+        Stage3 t;
+        float pe = 0.0f;
+        // score e (0..31; block e / 16, register e % 16) through stage st
+        auto stage = [&](int st, int e) {
+            const int kb = e >> 4, r = e & 15, i3 = e & 7;
+            if (st == 0) {
+                t.x[i3] = fmaf(s[kb][r], c, -lse2);
+                t.y[i3] = dp[kb][r] - dd;
+            } else if (st == 1) {
+                t.x[i3] = __builtin_amdgcn_exp2f(t.x[i3]);
+            } else {
+                const float v = t.x[i3] * t.y[i3];
+                if (r & 1) pk[e >> 1] = pack_bf16(pe, v);
+                else pe = v;
             }
-        // dQ^T += K^T dS^T: channel blocks db, 16-key chunks ch
+        };
+        b8 fr[48];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            acc[i & 3] = mma(colfrag(K + KI_KT, 32 * (i & 3) + l32, i >> 2, g), chunk4(pk + 4 * (i >> 2)), acc[i & 3]);
+        for (int n = 0; n < FD; ++n) fr[n] = afrag(n);
+        SLOT();
+#pragma unroll
+        for (int n = 0; n < 48; ++n) {
+            if (n + FD < 48) fr[n + FD] = afrag(n + FD);
+            if (n < 32) {
+                const int kb = n >> 4, m = n & 15;
+                if (m & 1) dp[kb] = mma(fr[n], df[m >> 1], m < 2 ? zero : dp[kb]);
+                else s[kb] = mma(fr[n], qf[m >> 1], m < 2 ? zero : s[kb]);
+            } else {
+                const int m = n - 32;
+                acc[m & 3] = mma(fr[n], chunk4(pk + 4 * (m >> 2)), acc[m & 3]);
+            }
+            // dS of block 0 in slots 16-33 (one score per slot), of block 1 in
+            // slots 32-41 (two per slot)
+#pragma unroll
+            for (int st = 0; st < 3; ++st) {
+                const int e0 = n - 16 - st;
+                if (e0 >= 0 && e0 < 16) stage(st, e0);
+                const int e1 = 2 * (n - 32 - st);
+                if (e1 >= 0 && e1 < 16) {
+                    stage(st, 16 + e1);
+                    stage(st, 17 + e1);
+                }
+            }
+            SLOT();
+        }
     }
     dma_wait<0>();
 
@@ -394,7 +448,7 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[QBUF * QIMG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
-    const WgPos wp = wg_pos(A.pl, wave);
+    const WgPos wp = wg_pos<WG_TILES>(A.pl, wave);
     const int krow = wp.row + l32;
     const uint8_t* ki = A.kimg + ((size_t)wp.head * A.pl.T + wp.tile) * KIMG;
     b8 kf[8], vf[8];
@@ -432,43 +486,62 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
         lds_barrier();
         if (j + 1 < nq) copy(j + 1);    // into the buffer of tile j-1, which every wave has finished
         const uint8_t* Q = lds + (j % QBUF) * QIMG;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            f16v s, dp;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
-            // S = Q K^T, dP = dO V^T for queries 32 u .. +32 of the tile
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s = mma(rowfrag(Q, 32 * u + l32, i, g), kf[i], s);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) dp = mma(rowfrag(Q + QI_DO, 32 * u + l32, i, g), vf[i], dp);
-            // register r holds query 32 u + 8 (r/4) + 4 g + r%4: its lse2 and D
-            // sit in the padding of transposed row 8 u + 2 (r/4) + g
-            uint32_t pp[8], ps[8];
+        // Per 32-query half u, 32 slots of one product each: S (slots 0-7),
+        // dP (8-15) with P formed in their slots, dV^T (16-23) with dS formed
+        // in theirs, dK^T (24-31).  Register r of S and dP holds query
+        // 32 u + 8 (r/4) + 4 g + r%4, whose -lse/sm_scale and -D sit in the
+        // padding of transposed row 8 u + 2 (r/4) + g: they are the initial
+        // accumulators, so S + pad gives P = 2^(c (S + pad)) and dP - D
+        // comes out of the products.
+        auto afrag = [&](int n) {
+            const int u = n >> 5, m = n & 31;
+            if (m < 16) return rowfrag(Q + (m < 8 ? 0 : QI_DO), 32 * u + l32, m & 7, g);
+            const int ch = (m >> 2) & 1, db = m & 3;
+            return colfrag(Q + (m < 24 ? QI_DOT : QI_QT), 32 * db + l32, 2 * u + ch, g);
+        };
+        auto pad16 = [&](int off, int u) {
+            f16v x;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int pr = 8 * u + 2 * r4 + g;
-                const float4 l4 = *reinterpret_cast<const float4*>(Q + QI_QT + pr * CSTR * 2 + PAD);
-                const float4 d4 = *reinterpret_cast<const float4*>(Q + QI_DOT + pr * CSTR * 2 + PAD);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int j2 = 0; j2 < 4; j2 += 2) {
-                    const int r = 4 * r4 + j2;
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[j2]));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -lv[j2 + 1]));
-                    pp[r / 2] = pack_bf16(p0, p1);
-                    ps[r / 2] = pack_bf16(p0 * (dp[r] - dvv[j2]), p1 * (dp[r + 1] - dvv[j2 + 1]));
-                }
+                const float4 v = *reinterpret_cast<const float4*>(Q + off + (8 * u + 2 * r4 + g) * CSTR * 2 + PAD);
+                x[4 * r4] = v.x; x[4 * r4 + 1] = v.y; x[4 * r4 + 2] = v.z; x[4 * r4 + 3] = v.w;
             }
-            // dV^T += dO^T P, dK^T += Q^T dS: channel blocks db, 16-query chunks 2 u + ch
+            return x;
+        };
+        f16v sc = pad16(QI_QT, 0), dp;
+        uint32_t pp[8], ps[8];
+        b8 fr[64];
 #pragma unroll
-            for (int ch = 0; ch < 2; ++ch)
+        for (int n = 0; n < KFD; ++n) fr[n] = afrag(n);
+        SLOT();
+        auto slot = [&](int n) {
+            const int u = n >> 5, m = n & 31;
+            if (n + KFD < 64) fr[n + KFD] = afrag(n + KFD);
+            if (m == 4) dp = pad16(QI_DOT, u);
+            if (m == 28 && u == 0) sc = pad16(QI_QT, 1);
+            if (m < 8) sc = mma(fr[n], kf[m], sc);
+            else if (m < 16) dp = mma(fr[n], vf[m - 8], dp);
+            else if (m < 24) dv[m & 3] = mma(fr[n], chunk4(pp + 4 * ((m >> 2) & 1)), dv[m & 3]);
+            else dk[m & 3] = mma(fr[n], chunk4(ps + 4 * ((m >> 2) & 1)), dk[m & 3]);
+            // P of scores 2 (m - 9), +1 in slots 9-16
+            if (m >= 9 && m < 17) {
+                const int r = 2 * (m - 9);
+                const float p0 = __builtin_amdgcn_exp2f(sc[r] * c), p1 = __builtin_amdgcn_exp2f(sc[r + 1] * c);
+                sc[r] = p0;
+                sc[r + 1] = p1;
+                pp[r >> 1] = pack_bf16(p0, p1);
+            }
+            // dS of scores 2 (m - 17), +1 in slots 17-24
+            if (m >= 17 && m < 25) {
+                const int r = 2 * (m - 17);
+                ps[r >> 1] = pack_bf16(sc[r] * dp[r], sc[r + 1] * dp[r + 1]);
+            }
+            SLOT();
+        };
 #pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    dv[db] = mma(colfrag(Q + QI_DOT, 32 * db + l32, 2 * u + ch, g), chunk4(pp + 4 * ch), dv[db]);
-                    dk[db] = mma(colfrag(Q + QI_QT, 32 * db + l32, 2 * u + ch, g), chunk4(ps + 4 * ch), dk[db]);
-                }
-        }
+        for (int n = 0; n < 32; ++n) slot(n);
+#pragma unroll
+        for (int n = 32; n < 64; ++n) slot(n);
     }
     dma_wait<0>();
 
@@ -510,14 +583,14 @@ int64_t plan_tiles(const SegTable& st, BwdPlan* pl) {
 }
 
 // block ranges in the given segment order; returns the block count
-int64_t plan_blocks(BwdPlan* pl, int H, bool late_first) {
+int64_t plan_blocks(BwdPlan* pl, int H, bool late_first, int tiles_per_wg) {
     int64_t b = 0;
     for (int i = 0; i < pl->nseg; ++i) {
         const int a = late_first ? pl->nseg - 1 - i : i;
         pl->order[i] = a;
         pl->blk0[i] = (int32_t)b;
         const int nt = pl->tile0[a + 1] - pl->tile0[a];
-        b += (int64_t)H * ((nt + WG_TILES - 1) / WG_TILES);
+        b += (int64_t)H * ((nt + tiles_per_wg - 1) / tiles_per_wg);
     }
     pl->blk0[pl->nseg] = (int32_t)b;
     return b;
@@ -537,14 +610,14 @@ int launch_seg_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     const int64_t T = plan_tiles(st, &pl);
     uint8_t* qimg = static_cast<uint8_t*>(workspace);
     uint8_t* kimg = qimg + (size_t)H * T * QIMG;
-    PackBwdArgs P{q, k, v, o, dout, lse, qimg, kimg, Ln, H, pl, st, rt};
+    PackBwdArgs P{q, k, v, o, dout, lse, qimg, kimg, Ln, H, sm_scale, pl, st, rt};
     hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)T, (unsigned)H, 2), dim3(PACK_NT), 0, stream, P);
     BwdArgs A{qimg, kimg, dq, dk, dv, Ln, H, sm_scale * 1.44269504088896341f, sm_scale, pl, st, rt};
     // dK/dV: early segments (the most query tiles) first
-    const int64_t nb_kv = plan_blocks(&A.pl, H, false);
+    const int64_t nb_kv = plan_blocks(&A.pl, H, false, WG_TILES);
     hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)nb_kv), dim3(NT), 0, stream, A);
     // dQ: late segments (the most key tiles) first
-    const int64_t nb_q = plan_blocks(&A.pl, H, true);
+    const int64_t nb_q = plan_blocks(&A.pl, H, true, WG_TILES);
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)nb_q), dim3(NT), 0, stream, A);
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
 }

@@ -6,7 +6,10 @@ the GPU; the expected gradients come from the oracle alone.
 Parity bar for the fp32 gradients: relative L2 error <= 5e-3 per tensor and
 max-abs error <= 2e-2 times the tensor's largest magnitude.  The kernels
 round P and dS to bf16 (relative 2^-9 per term) before their products and
-take D from the forward's bf16 output; sums are fp32."""
+take D from the forward's bf16 output; sums are fp32.  Where a gradient is
+exactly zero (a token alone in its segment has P = 1 and dS = 0), the
+relative error has no meaning; its max-abs error is then bounded by 2e-2
+times the largest magnitude among the case's three gradients."""
 import numpy as np
 import pytest
 import torch
@@ -32,14 +35,21 @@ def _grads_gpu(q, k, v, d_out, segs, H):
     return [t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
 
 
-def _close(got, ref, what):
+def _close(got, ref, what, case_scale=0.0):
     assert np.all(np.isfinite(got)), "%s: non-finite gradient" % what
     d = got - ref
     scale = float(np.abs(ref).max())
     mx = float(np.abs(d).max())
-    rl2 = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+    nref = float(np.linalg.norm(ref))
+    rl2 = float(np.linalg.norm(d) / nref) if nref > 0 else 0.0
     say("%s: max-abs %.3e (of max %.3e) rel-L2 %.3e" % (what, mx, scale, rl2))
-    assert rl2 <= GRAD_REL_L2 and mx <= GRAD_MAX_REL * scale, (what, mx, scale, rl2)
+    assert rl2 <= GRAD_REL_L2 and mx <= GRAD_MAX_REL * max(scale, case_scale), (what, mx, scale, rl2)
+
+
+def _close3(got, ref, name):
+    case_scale = max(float(np.abs(r).max()) for r in ref)
+    for g, r, w in zip(got, ref, ("dq", "dk", "dv")):
+        _close(g, r, "%s %s" % (name, w), case_scale)
 
 
 def _check(name, segs, H, seed):
@@ -48,8 +58,7 @@ def _check(name, segs, H, seed):
     say("seg_attn_bwd", name, "L", L, "H", H, "segs", segs)
     got = _grads_gpu(q, k, v, d_out, segs, H)
     ref = oracle.seg_attn_bwd(q, k, v, d_out, segs, SM)
-    for g, r, w in zip(got, ref, ("dq", "dk", "dv")):
-        _close(g, r, "%s %s" % (name, w))
+    _close3(got, ref, name)
 
 
 def test_bwd_tiny_three_segments():
@@ -59,8 +68,7 @@ def test_bwd_tiny_three_segments():
     say("seg_attn_bwd tiny (3 x 64 tokens, H 2)")
     got = _grads_gpu(inp["q"], inp["k"], inp["v"], d_out, segs, 2)
     ref = oracle.seg_attn_bwd(inp["q"], inp["k"], inp["v"], d_out, segs, SM)
-    for g, r, w in zip(got, ref, ("dq", "dk", "dv")):
-        _close(g, r, "tiny " + w)
+    _close3(got, ref, "tiny")
 
 
 CASES = [
@@ -131,11 +139,11 @@ def test_bwd_training_sequence_full_size():
     # sum_k dv_k = sum_q dO_q (rows of P sum to one)
     dof = oracle.bf16_bits_to_f64(d_out)
     lhs, rhs = dv.sum(axis=0), dof.sum(axis=0)
-    tol = 1e-3 * np.abs(dof).sum(axis=0)
+    tol = 1e-6 * np.abs(dof).sum(axis=0)
     say("full sum dv: max |diff| %.3e, max tol %.3e" % (np.abs(lhs - rhs).max(), tol.max()))
     assert np.all(np.abs(lhs - rhs) <= tol)
     # sum_k dKr_k = 0 (rows of dS sum to zero), against the size of the terms
     dkr = oracle.rope3d(dk, segs)
     s, a = np.abs(dkr.sum(axis=0)), np.abs(dkr).sum(axis=0)
     say("full sum dKr: max |sum| / sum |.| = %.3e" % (s / a).max())
-    assert np.all(s <= 1e-2 * a)
+    assert np.all(s <= 1e-3 * a)
