@@ -45,6 +45,7 @@
 // magnitude, so any per-pair or per-block-pair exchange would be bound by HBM.
 #include <algorithm>
 #include <cstring>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -302,15 +303,7 @@ __device__ __forceinline__ b8 rowfrag(const uint8_t* img, int r, int s, int g) {
 // of a later operand and a few vector instructions).
 #define SLOT() __builtin_amdgcn_sched_barrier(0)
 constexpr int FD = 2;               // LDS operand reads issued this many products ahead (dQ)
-constexpr int KFD = 1;              // the same for dK/dV, whose registers are scarcer
-
-// dS of one score in three stages spread over consecutive slots, so that no
-// slot holds a chain of dependent vector instructions:
-//   0: x = s c - lse2, y = dP - D;  1: x = 2^x;  2: p = x, ds = p y
-// t holds the scores in flight (at most 6 consecutive ones: index e % 8).
-struct Stage3 {
-    float x[8], y[8];
-};
+constexpr int KFD = 1;              // the same for dK/dV (its registers hold P in fp32 for dS)
 
 // ---- dQ: lane = query --------------------------------------------------------
 //
@@ -358,15 +351,21 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
     };
     const float c = A.c;
     const f16v zero = {};
+    f16v negd;              // -D: the initial dP^T accumulator, so that dP - D comes out of the products
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negd[r] = -dd;
     copy(0);
     copy(1);
-    for (int j = 0; j < nk; ++j) {
+    // tile j lives in buffer j % 3; the loop is unrolled by 3 so that every
+    // LDS operand address is the lane's base plus an immediate offset
+    auto tile_step = [&](int j, auto bufc) {
+        constexpr int bi = decltype(bufc)::value;
         // this wave's copies of tile j have landed once at most those of tile j+1 are in flight
         if (wv < KIMG_KB % NW) dma_wait<(KIMG_KB + NW - 1) / NW>();
         else dma_wait<KIMG_KB / NW>();
         lds_barrier();
         copy(j + 2);        // into the buffer of tile j-1, which every wave has finished
-        const uint8_t* K = lds + (j % KBUF) * KIMG;
+        const uint8_t* K = lds + bi * KIMG;
         // operand of product n: 0-31 S^T / dP^T of key blocks 0 and 1
         // (even n: K rows, odd n: V rows; channel step (n % 16) / 2), 32-47
         // dQ^T: channel block (n - 32) % 4, 16-key chunk (n - 32) / 4
@@ -376,18 +375,18 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
         };
         f16v s[2], dp[2];
         uint32_t pk[16];
-        Stage3 t;
+        float tx[8];
         float pe = 0.0f;
-        // score e (0..31; block e / 16, register e % 16) through stage st
+        // score e (0..31; block e / 16, register e % 16) through stage st:
+        // 0: x = S c - lse2;  1: x = 2^x;  2: dS = x (dP - D), packed in pairs
         auto stage = [&](int st, int e) {
-            const int kb = e >> 4, r = e & 15, i3 = e & 7;
+            const int kb = e >> 4, r = e & 15, i8 = e & 7;
             if (st == 0) {
-                t.x[i3] = fmaf(s[kb][r], c, -lse2);
-                t.y[i3] = dp[kb][r] - dd;
+                tx[i8] = fmaf(s[kb][r], c, -lse2);
             } else if (st == 1) {
-                t.x[i3] = __builtin_amdgcn_exp2f(t.x[i3]);
+                tx[i8] = __builtin_amdgcn_exp2f(tx[i8]);
             } else {
-                const float v = t.x[i3] * t.y[i3];
+                const float v = tx[i8] * dp[kb][r];
                 if (r & 1) pk[e >> 1] = pack_bf16(pe, v);
                 else pe = v;
             }
@@ -401,7 +400,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
             if (n + FD < 48) fr[n + FD] = afrag(n + FD);
             if (n < 32) {
                 const int kb = n >> 4, m = n & 15;
-                if (m & 1) dp[kb] = mma(fr[n], df[m >> 1], m < 2 ? zero : dp[kb]);
+                if (m & 1) dp[kb] = mma(fr[n], df[m >> 1], m < 2 ? negd : dp[kb]);
                 else s[kb] = mma(fr[n], qf[m >> 1], m < 2 ? zero : s[kb]);
             } else {
                 const int m = n - 32;
@@ -421,6 +420,11 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
             }
             SLOT();
         }
+    };
+    for (int j = 0; j < nk; j += KBUF) {
+        tile_step(j, std::integral_constant<int, 0>{});
+        if (j + 1 < nk) tile_step(j + 1, std::integral_constant<int, 1>{});
+        if (j + 2 < nk) tile_step(j + 2, std::integral_constant<int, 2>{});
     }
     dma_wait<0>();
 
@@ -481,11 +485,14 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
     };
     const float c = A.c;
     copy(0);
-    for (int j = 0; j < nq; ++j) {
+    // tile j lives in buffer j % 2; the loop is unrolled by 2 so that every
+    // LDS operand address is the lane's base plus an immediate offset
+    auto tile_step = [&](int j, auto bufc) {
+        constexpr int bi = decltype(bufc)::value;
         dma_wait<0>();
         lds_barrier();
         if (j + 1 < nq) copy(j + 1);    // into the buffer of tile j-1, which every wave has finished
-        const uint8_t* Q = lds + (j % QBUF) * QIMG;
+        const uint8_t* Q = lds + bi * QIMG;
         // Per 32-query half u, 32 slots of one product each: S (slots 0-7),
         // dP (8-15) with P formed in their slots, dV^T (16-23) with dS formed
         // in theirs, dK^T (24-31).  Register r of S and dP holds query
@@ -531,7 +538,7 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
                 sc[r + 1] = p1;
                 pp[r >> 1] = pack_bf16(p0, p1);
             }
-            // dS of scores 2 (m - 17), +1 in slots 17-24
+            // dS = P (dP - D) of scores 2 (m - 17), +1 in slots 17-24
             if (m >= 17 && m < 25) {
                 const int r = 2 * (m - 17);
                 ps[r >> 1] = pack_bf16(sc[r] * dp[r], sc[r + 1] * dp[r + 1]);
@@ -542,6 +549,10 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
         for (int n = 0; n < 32; ++n) slot(n);
 #pragma unroll
         for (int n = 32; n < 64; ++n) slot(n);
+    };
+    for (int j = 0; j < nq; j += QBUF) {
+        tile_step(j, std::integral_constant<int, 0>{});
+        if (j + 1 < nq) tile_step(j + 1, std::integral_constant<int, 1>{});
     }
     dma_wait<0>();
 
