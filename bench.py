@@ -21,6 +21,7 @@ The CPU baseline times the oracle on a bounded sample of the same workload.
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
        python bench.py --copy-calibration   (plain copy kernel for counter scaling)
        python bench.py --workloads          (the other workloads, one JSON line each; see workloads())
+       python bench.py --workloads --only train   (a subset of them, by group)
 """
 from __future__ import annotations
 
@@ -89,6 +90,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--workloads", action="store_true")
+    ap.add_argument("--only", default="", help="with --workloads: comma-separated groups (turn3s, seg4s, "
+                    "fiveturns, decoder, w8a16, fullcache, train)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -99,7 +102,7 @@ def main():
         copy_calibration()
         return
     if args.workloads:
-        workloads()
+        workloads([w for w in args.only.split(",") if w])
         return
 
     import numpy as np
@@ -219,7 +222,7 @@ def main():
     print(json.dumps(line))
 
 
-def workloads():
+def workloads(only=None):
     """Throughput of the path on the other workloads, one JSON line each, all
     inputs seeded synthetic and resident in HBM before timing, HIP events on
     the launch stream:
@@ -284,6 +287,9 @@ def workloads():
             ts.append(a.elapsed_time(b))
         return float(np.median(ts))
 
+    def want(group):
+        return not only or group in only
+
     def emit(name, **kw):
         line = dict(workload=name, **kw)
         print(json.dumps(line), flush=True)
@@ -295,187 +301,194 @@ def workloads():
              pct_of_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2), heads=H, queries=Lq, keys_per_query=keys,
              algorithmic_flop=fl, **(extra or {}))
 
-    # ---- turn3s
-    log("workload turn3s")
-    cfg = synth.CONFIGS[2]
-    inp = synth.layer_inputs(2)
-    (seg,) = cfg.new_segs
-    cache = build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs, cfg.H, cfg.Lc)
-    q, k, v = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])
-    out = torch.empty_like(q)
-    ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H), dtype=torch.uint8, device=dev)
-    ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
-                                      stream=stream), 10, 3)
-    attn_line("turn3s", ms, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq)
-    del q, k, v, out, ws, cache, inp
-
-    # ---- seg4s: 54 layers resident, 8 steps over all of them
-    log("workload seg4s: 54 layers resident, 8 steps over all of them")
-    cfg = synth.CONFIGS[3]
-    (seg,) = cfg.new_segs
-    layers = []
-    t0 = time.time()
-    for l in range(cfg.layers):
-        inp = synth.layer_inputs(3, l)
+    if want("turn3s"):
+        # ---- turn3s
+        log("workload turn3s")
+        cfg = synth.CONFIGS[2]
+        inp = synth.layer_inputs(2)
+        (seg,) = cfg.new_segs
         cache = build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs, cfg.H, cfg.Lc)
-        layers.append((d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])) + cache)
+        q, k, v = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])
+        out = torch.empty_like(q)
+        ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
+                                          stream=stream), 10, 3)
+        attn_line("turn3s", ms, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq)
+        del q, k, v, out, ws, cache, inp
+
+    if want("seg4s"):
+        # ---- seg4s: 54 layers resident, 8 steps over all of them
+        log("workload seg4s: 54 layers resident, 8 steps over all of them")
+        cfg = synth.CONFIGS[3]
+        (seg,) = cfg.new_segs
+        layers = []
+        t0 = time.time()
+        for l in range(cfg.layers):
+            inp = synth.layer_inputs(3, l)
+            cache = build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs, cfg.H, cfg.Lc)
+            layers.append((d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])) + cache)
+            del inp
+            if l % 6 == 5:
+                log("seg4s: %d of %d layers resident (%.0f s)" % (l + 1, cfg.layers, time.time() - t0))
+        out = torch.empty_like(layers[0][0])
+        ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H), dtype=torch.uint8, device=dev)
+
+        def sequence():
+            for _ in range(cfg.steps):
+                for (q, k, v, kc, vc, ks, vs) in layers:
+                    nomas.seg_attn(q, k, v, [seg], kc, vc, ks, vs, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
+                                   stream=stream)
+
+        ms = timed(sequence, 3, 1)
+        calls = cfg.layers * cfg.steps
+        attn_line("seg4s", ms / calls, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq,
+                  dict(calls=calls, sequence_ms=round(ms, 1), outlier_channels=cfg.outliers))
+        del layers, out, ws
+
+    if want("fiveturns"):
+        # ---- fiveturns
+        log("workload fiveturns")
+        cfg = synth.CONFIGS[5]
+        H = cfg.H
+        n = synth.turn_seg(0).ntok
+        cache = build_cache(None, None, None, H, 5 * n)
+        length = 0
+        for t in range(5):
+            inp = synth.turn_inputs(t)
+            seg = inp["seg"]
+            q, k, v, qc = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"]), d16(inp["q_cam"])
+            wk, wv = d16(inp["w_k"]), d16(inp["w_v"])
+            cam = torch.from_numpy(nomas.cam_tokens(inp["c2w"])).to(dev)
+            out, oc, kr = torch.empty_like(q), torch.empty_like(qc), torch.empty_like(k)
+            ws = torch.empty(nomas.seg_attn_workspace([seg], length, H), dtype=torch.uint8, device=dev)
+            ms_a = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=length, sm_scale=sm, out=out,
+                                                workspace=ws, stream=stream), 5)
+            ms_c = timed(lambda: nomas.cam_xattn(qc, cam, wk, wv, sm_scale=sm, out=oc, stream=stream), 5)
+            ms_r = timed(lambda: nomas.rope3d(k, [seg], out=kr, stream=stream), 5)
+            # appending the same rows at the same offset is idempotent
+            ms_q = timed(lambda: nomas.kv_quant_append(kr, v, *cache, length, stream=stream), 5)
+            elems = n * H * 128
+            gbs = lambda b, m: round(b / (m * 1e-3) / 1e9, 1)
+            attn_line("fiveturns-turn%d" % t, ms_a, H, n, length + n,
+                      dict(cache_tokens=length,
+                           cam_xattn=dict(ms=round(ms_c, 4), GBps=gbs(4 * elems, ms_c), camera_tokens=cam.shape[0]),
+                           rope3d=dict(ms=round(ms_r, 4), GBps=gbs(4 * elems, ms_r)),
+                           kv_quant_append=dict(ms=round(ms_q, 4), GBps=gbs(2 * 3 * elems + 2 * 4 * n * H, ms_q)),
+                           hbm_peak_GBps=PEAK_HBM_GBS))
+            length = nomas.kv_quant_append(kr, v, *cache, length, stream=stream)
+            torch.cuda.synchronize()
+            del q, k, v, qc, out, oc, kr, ws
+        del cache
+
+    if want("decoder"):
+        # ---- decoder window: 10 latent frames of 4x16x16 tubelets at 1280x704
+        log("workload decoder-window")
+        L, Hq, Hkv = 10 * 44 * 80, 32, 8
+        q = d16(synth.random_bf16(501, (L, Hq, 128)))
+        k = d16(synth.random_bf16(502, (L, Hkv, 128)))
+        v = d16(synth.random_bf16(503, (L, Hkv, 128)))
+        out = torch.empty_like(q)
+        ws = torch.empty(nomas.gqa_attn_workspace(L, Hq, Hkv), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: nomas.gqa_attn(q, k, v, sm_scale=sm, out=out, workspace=ws, stream=stream), 5)
+        attn_line("decoder-window", ms, Hq, L, L, dict(kv_heads=Hkv, entry="nomas_gqa_attn"))
+        del q, k, v, out, ws
+
+    if want("w8a16"):
+        # ---- INT8-weight linear layers of one 12 s segment (63,360 tokens, hidden 2048)
+        for name, N in (("w8a16-qkv", 6144), ("w8a16-ffn-up", 8192)):
+            log("workload " + name)
+            M, K = 63360, 2048
+            x = d16(synth.random_bf16(601, (M, K)))
+            g = np.random.default_rng(602)
+            codes = torch.from_numpy(g.integers(-127, 128, size=(N, K), dtype=np.int8)).to(dev)
+            scale = torch.from_numpy((1.0 / (73.0 * math.sqrt(K)) * (0.5 + g.random(N))).astype(np.float32)).to(dev)
+            y = torch.empty((M, N), dtype=torch.int16, device=dev)
+            ws = torch.empty(nomas.w8a16_linear_workspace(K, N), dtype=torch.uint8, device=dev)
+            ms = timed(lambda: nomas.w8a16_linear(x, codes, scale, out=y, workspace=ws, stream=stream), 10, 3)
+            # context: the dequantisation pass alone (M = 0), and torch's BF16 matmul on the dequantised weights
+            ms_dq = timed(lambda: nomas.w8a16_linear(x[:0], codes, scale, out=y[:0], workspace=ws, stream=stream), 10, 3)
+            wb = ws[:N * K * 2].view(torch.bfloat16).view(N, K)
+            xb = x.view(torch.bfloat16)
+            wt = wb.t().contiguous()
+            ms_t = timed(lambda: torch.matmul(xb, wt), 10, 3)
+            fl = 2.0 * M * N * K
+            tf = fl / (ms * 1e-3) / 1e12
+            emit(name, metric="linear TFLOP/s", value=round(tf, 2), unit="TFLOP/s", ms=round(ms, 4),
+                 pct_of_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2), M=M, K=K, N=N, algorithmic_flop=fl,
+                 dequant_ms=round(ms_dq, 4), context_torch_bf16_matmul_ms=round(ms_t, 4))
+            del x, codes, scale, y, ws, wt
+
+    if want("fullcache"):
+        # ---- fullcache-sel18 and fullcache-h2 share the full-cache inputs
+        log("workload fullcache-sel18 / fullcache-h2: generating the full-cache inputs")
+        cfg = synth.CONFIGS[4]
+        inp = synth.layer_inputs(4)
+        (seg,) = cfg.new_segs
+        (hseg,) = cfg.hist_segs
+        frame = hseg.Hg * hseg.Wg
+        # history selection: 18 of the 288 cached latent frames, the last of every 16
+        sel = [[(f * frame, (f + 1) * frame) for f in range(15, hseg.T, 16)]]
+        nsel = sum(hi - lo for lo, hi in sel[0])
+        cache = build_cache(inp["k_hist"], inp["v_hist"], [hseg], cfg.H, cfg.Lc)
+        q, k, v = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])
+        out = torch.empty_like(q)
+        ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H, sel=sel), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
+                                          stream=stream, sel=sel), 5)
+        attn_line("fullcache-sel18", ms, cfg.H, cfg.Lq, nsel + cfg.Lq,
+                  dict(cache_tokens=cfg.Lc, selected_frames=len(sel[0]), selected_tokens=nsel))
+        del q, k, v, out, ws, cache
+
+        # ---- fullcache-h2: one GPU's share of the full-cache shape
+        log("workload fullcache-h2: one GPU's share of the full-cache shape")
+        H = 2
+        sub = lambda a: np.ascontiguousarray(a[:, :H])
+        cache = build_cache(sub(inp["k_hist"]), sub(inp["v_hist"]), [hseg], H, cfg.Lc)
+        q, k, v = d16(sub(inp["q"])), d16(sub(inp["k_new"])), d16(sub(inp["v_new"]))
         del inp
-        if l % 6 == 5:
-            log("seg4s: %d of %d layers resident (%.0f s)" % (l + 1, cfg.layers, time.time() - t0))
-    out = torch.empty_like(layers[0][0])
-    ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, H), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
+                                          stream=stream), 5)
+        attn_line("fullcache-h2", ms, H, cfg.Lq, cfg.Lc + cfg.Lq, dict(note="heads 0-1 of the full-cache inputs"))
+        del q, k, v, out, ws, cache
 
-    def sequence():
-        for _ in range(cfg.steps):
-            for (q, k, v, kc, vc, ks, vs) in layers:
-                nomas.seg_attn(q, k, v, [seg], kc, vc, ks, vs, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
-                               stream=stream)
-
-    ms = timed(sequence, 3, 1)
-    calls = cfg.layers * cfg.steps
-    attn_line("seg4s", ms / calls, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq,
-              dict(calls=calls, sequence_ms=round(ms, 1), outlier_channels=cfg.outliers))
-    del layers, out, ws
-
-    # ---- fiveturns
-    log("workload fiveturns")
-    cfg = synth.CONFIGS[5]
-    H = cfg.H
-    n = synth.turn_seg(0).ntok
-    cache = build_cache(None, None, None, H, 5 * n)
-    length = 0
-    for t in range(5):
-        inp = synth.turn_inputs(t)
-        seg = inp["seg"]
-        q, k, v, qc = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"]), d16(inp["q_cam"])
-        wk, wv = d16(inp["w_k"]), d16(inp["w_v"])
-        cam = torch.from_numpy(nomas.cam_tokens(inp["c2w"])).to(dev)
-        out, oc, kr = torch.empty_like(q), torch.empty_like(qc), torch.empty_like(k)
-        ws = torch.empty(nomas.seg_attn_workspace([seg], length, H), dtype=torch.uint8, device=dev)
-        ms_a = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=length, sm_scale=sm, out=out,
-                                            workspace=ws, stream=stream), 5)
-        ms_c = timed(lambda: nomas.cam_xattn(qc, cam, wk, wv, sm_scale=sm, out=oc, stream=stream), 5)
-        ms_r = timed(lambda: nomas.rope3d(k, [seg], out=kr, stream=stream), 5)
-        # appending the same rows at the same offset is idempotent
-        ms_q = timed(lambda: nomas.kv_quant_append(kr, v, *cache, length, stream=stream), 5)
-        elems = n * H * 128
-        gbs = lambda b, m: round(b / (m * 1e-3) / 1e9, 1)
-        attn_line("fiveturns-turn%d" % t, ms_a, H, n, length + n,
-                  dict(cache_tokens=length,
-                       cam_xattn=dict(ms=round(ms_c, 4), GBps=gbs(4 * elems, ms_c), camera_tokens=cam.shape[0]),
-                       rope3d=dict(ms=round(ms_r, 4), GBps=gbs(4 * elems, ms_r)),
-                       kv_quant_append=dict(ms=round(ms_q, 4), GBps=gbs(2 * 3 * elems + 2 * 4 * n * H, ms_q)),
-                       hbm_peak_GBps=PEAK_HBM_GBS))
-        length = nomas.kv_quant_append(kr, v, *cache, length, stream=stream)
-        torch.cuda.synchronize()
-        del q, k, v, qc, out, oc, kr, ws
-    del cache
-
-    # ---- decoder window: 10 latent frames of 4x16x16 tubelets at 1280x704
-    log("workload decoder-window")
-    L, Hq, Hkv = 10 * 44 * 80, 32, 8
-    q = d16(synth.random_bf16(501, (L, Hq, 128)))
-    k = d16(synth.random_bf16(502, (L, Hkv, 128)))
-    v = d16(synth.random_bf16(503, (L, Hkv, 128)))
-    out = torch.empty_like(q)
-    ws = torch.empty(nomas.gqa_attn_workspace(L, Hq, Hkv), dtype=torch.uint8, device=dev)
-    ms = timed(lambda: nomas.gqa_attn(q, k, v, sm_scale=sm, out=out, workspace=ws, stream=stream), 5)
-    attn_line("decoder-window", ms, Hq, L, L, dict(kv_heads=Hkv, entry="nomas_gqa_attn"))
-    del q, k, v, out, ws
-
-    # ---- INT8-weight linear layers of one 12 s segment (63,360 tokens, hidden 2048)
-    for name, N in (("w8a16-qkv", 6144), ("w8a16-ffn-up", 8192)):
-        log("workload " + name)
-        M, K = 63360, 2048
-        x = d16(synth.random_bf16(601, (M, K)))
-        g = np.random.default_rng(602)
-        codes = torch.from_numpy(g.integers(-127, 128, size=(N, K), dtype=np.int8)).to(dev)
-        scale = torch.from_numpy((1.0 / (73.0 * math.sqrt(K)) * (0.5 + g.random(N))).astype(np.float32)).to(dev)
-        y = torch.empty((M, N), dtype=torch.int16, device=dev)
-        ws = torch.empty(nomas.w8a16_linear_workspace(K, N), dtype=torch.uint8, device=dev)
-        ms = timed(lambda: nomas.w8a16_linear(x, codes, scale, out=y, workspace=ws, stream=stream), 10, 3)
-        # context: the dequantisation pass alone (M = 0), and torch's BF16 matmul on the dequantised weights
-        ms_dq = timed(lambda: nomas.w8a16_linear(x[:0], codes, scale, out=y[:0], workspace=ws, stream=stream), 10, 3)
-        wb = ws[:N * K * 2].view(torch.bfloat16).view(N, K)
-        xb = x.view(torch.bfloat16)
-        wt = wb.t().contiguous()
-        ms_t = timed(lambda: torch.matmul(xb, wt), 10, 3)
-        fl = 2.0 * M * N * K
-        tf = fl / (ms * 1e-3) / 1e12
-        emit(name, metric="linear TFLOP/s", value=round(tf, 2), unit="TFLOP/s", ms=round(ms, 4),
-             pct_of_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2), M=M, K=K, N=N, algorithmic_flop=fl,
-             dequant_ms=round(ms_dq, 4), context_torch_bf16_matmul_ms=round(ms_t, 4))
-        del x, codes, scale, y, ws, wt
-
-    # ---- fullcache-sel18 and fullcache-h2 share the full-cache inputs
-    log("workload fullcache-sel18 / fullcache-h2: generating the full-cache inputs")
-    cfg = synth.CONFIGS[4]
-    inp = synth.layer_inputs(4)
-    (seg,) = cfg.new_segs
-    (hseg,) = cfg.hist_segs
-    frame = hseg.Hg * hseg.Wg
-    # history selection: 18 of the 288 cached latent frames, the last of every 16
-    sel = [[(f * frame, (f + 1) * frame) for f in range(15, hseg.T, 16)]]
-    nsel = sum(hi - lo for lo, hi in sel[0])
-    cache = build_cache(inp["k_hist"], inp["v_hist"], [hseg], cfg.H, cfg.Lc)
-    q, k, v = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])
-    out = torch.empty_like(q)
-    ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H, sel=sel), dtype=torch.uint8, device=dev)
-    ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
-                                      stream=stream, sel=sel), 5)
-    attn_line("fullcache-sel18", ms, cfg.H, cfg.Lq, nsel + cfg.Lq,
-              dict(cache_tokens=cfg.Lc, selected_frames=len(sel[0]), selected_tokens=nsel))
-    del q, k, v, out, ws, cache
-
-    # ---- fullcache-h2: one GPU's share of the full-cache shape
-    log("workload fullcache-h2: one GPU's share of the full-cache shape")
-    H = 2
-    sub = lambda a: np.ascontiguousarray(a[:, :H])
-    cache = build_cache(sub(inp["k_hist"]), sub(inp["v_hist"]), [hseg], H, cfg.Lc)
-    q, k, v = d16(sub(inp["q"])), d16(sub(inp["k_new"])), d16(sub(inp["v_new"]))
-    del inp
-    out = torch.empty_like(q)
-    ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, H), dtype=torch.uint8, device=dev)
-    ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
-                                      stream=stream), 5)
-    attn_line("fullcache-h2", ms, H, cfg.Lq, cfg.Lc + cfg.Lq, dict(note="heads 0-1 of the full-cache inputs"))
-    del q, k, v, out, ws, cache
-
-    # ---- segment-forcing training: packed forward and backward
-    log("workload train-fwd / train-bwd: 22 packed 3 s turns, 2 heads")
-    segs = synth.train_segs()
-    H = 2
-    inp = synth.train_inputs(segs, H)
-    q, k, v, do = (d16(inp[x]) for x in ("q", "k", "v", "d_out"))
-    del inp
-    L = q.shape[0]
-    n_a = [s.ntok for s in segs]
-    pairs = H * sum(n_a[a] * sum(n_a[:a + 1]) for a in range(len(n_a)))
-    out = torch.empty_like(q)
-    lse = torch.empty((H, L), dtype=torch.float32, device=dev)
-    ws = torch.empty(nomas.seg_attn_workspace(segs, 0, H), dtype=torch.uint8, device=dev)
-    ms_f = timed(lambda: nomas.seg_attn(q, k, v, segs, cache_len=0, sm_scale=sm, out=out, lse=lse, workspace=ws,
-                                        stream=stream), 5)
-    fl_f = 4.0 * 128 * pairs
-    tf_f = fl_f / (ms_f * 1e-3) / 1e12
-    emit("train-fwd", metric="attention TFLOP/s", value=round(tf_f, 2), unit="TFLOP/s", ms=round(ms_f, 3),
-         pct_of_peak=round(100 * tf_f / PEAK_BF16_TFLOPS, 2), heads=H, tokens=L, segments=len(segs),
-         allowed_pairs=pairs, algorithmic_flop=fl_f)
-    del ws
-    wsb = torch.empty(nomas.seg_attn_bwd_workspace(segs, H), dtype=torch.uint8, device=dev)
-    g = [torch.empty((L, H, 128), dtype=torch.float32, device=dev) for _ in range(3)]
-    ms_b = timed(lambda: nomas.seg_attn_bwd(q, k, v, out, lse, do, segs, sm_scale=sm, dq=g[0], dk=g[1], dv=g[2],
-                                            workspace=wsb, stream=stream), 5)
-    # algorithmic: five products of 2 x 128 flops per allowed pair (S recomputed once);
-    # the kernels execute seven (S and dP in both the dK/dV and the dQ kernel)
-    fl_b = 10.0 * 128 * pairs
-    tf_b = fl_b / (ms_b * 1e-3) / 1e12
-    emit("train-bwd", metric="attention backward TFLOP/s", value=round(tf_b, 2), unit="TFLOP/s",
-         ms=round(ms_b, 3), pct_of_peak=round(100 * tf_b / PEAK_BF16_TFLOPS, 2), heads=H, tokens=L,
-         segments=len(segs), allowed_pairs=pairs, algorithmic_flop=fl_b,
-         executed_mfma_flop=14.0 * 128 * pairs,
-         executed_pct_of_peak=round(100 * 1.4 * tf_b / PEAK_BF16_TFLOPS, 2),
-         fwd_plus_bwd_ms=round(ms_f + ms_b, 3))
+    if want("train"):
+        # ---- segment-forcing training: packed forward and backward
+        log("workload train-fwd / train-bwd: 22 packed 3 s turns, 2 heads")
+        segs = synth.train_segs()
+        H = 2
+        inp = synth.train_inputs(segs, H)
+        q, k, v, do = (d16(inp[x]) for x in ("q", "k", "v", "d_out"))
+        del inp
+        L = q.shape[0]
+        n_a = [s.ntok for s in segs]
+        pairs = H * sum(n_a[a] * sum(n_a[:a + 1]) for a in range(len(n_a)))
+        out = torch.empty_like(q)
+        lse = torch.empty((H, L), dtype=torch.float32, device=dev)
+        ws = torch.empty(nomas.seg_attn_workspace(segs, 0, H), dtype=torch.uint8, device=dev)
+        ms_f = timed(lambda: nomas.seg_attn(q, k, v, segs, cache_len=0, sm_scale=sm, out=out, lse=lse, workspace=ws,
+                                            stream=stream), 5)
+        fl_f = 4.0 * 128 * pairs
+        tf_f = fl_f / (ms_f * 1e-3) / 1e12
+        emit("train-fwd", metric="attention TFLOP/s", value=round(tf_f, 2), unit="TFLOP/s", ms=round(ms_f, 3),
+             pct_of_peak=round(100 * tf_f / PEAK_BF16_TFLOPS, 2), heads=H, tokens=L, segments=len(segs),
+             allowed_pairs=pairs, algorithmic_flop=fl_f)
+        del ws
+        wsb = torch.empty(nomas.seg_attn_bwd_workspace(segs, H), dtype=torch.uint8, device=dev)
+        g = [torch.empty((L, H, 128), dtype=torch.float32, device=dev) for _ in range(3)]
+        ms_b = timed(lambda: nomas.seg_attn_bwd(q, k, v, out, lse, do, segs, sm_scale=sm, dq=g[0], dk=g[1], dv=g[2],
+                                                workspace=wsb, stream=stream), 5)
+        # algorithmic: five products of 2 x 128 flops per allowed pair (S recomputed once);
+        # the kernels execute seven (S and dP in both the dK/dV and the dQ kernel)
+        fl_b = 10.0 * 128 * pairs
+        tf_b = fl_b / (ms_b * 1e-3) / 1e12
+        emit("train-bwd", metric="attention backward TFLOP/s", value=round(tf_b, 2), unit="TFLOP/s",
+             ms=round(ms_b, 3), pct_of_peak=round(100 * tf_b / PEAK_BF16_TFLOPS, 2), heads=H, tokens=L,
+             segments=len(segs), allowed_pairs=pairs, algorithmic_flop=fl_b,
+             executed_mfma_flop=14.0 * 128 * pairs,
+             executed_pct_of_peak=round(100 * 1.4 * tf_b / PEAK_BF16_TFLOPS, 2),
+             fwd_plus_bwd_ms=round(ms_f + ms_b, 3))
 
 
 def cpu_baseline(inp, cfg, sm):

@@ -41,8 +41,9 @@
 //     rows; B = the wave's Q, dO in registers), then dQ^T += K^T dS^T.  It
 //     walks the key tiles of segments 0..a.
 // S and dP are recomputed by both kernels instead of exchanging dQ partials
-// between workgroups; the pairs outnumber the tokens by four orders of
-// magnitude, so any per-pair or per-block-pair exchange would be bound by HBM.
+// between workgroups; at training lengths the pairs outnumber the tokens by
+// five orders of magnitude, so any per-pair or per-block-pair exchange would
+// be bound by HBM.
 #include <algorithm>
 #include <cstring>
 #include <type_traits>
