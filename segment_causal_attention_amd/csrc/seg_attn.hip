@@ -235,6 +235,8 @@ struct AttnArgs {
     int32_t nsplit;                 // key-range parts per query tile
     float scale_log2;               // sm_scale * log2(e)
     int32_t tile0[NOMAS_MAX_SEGS + 1];   // first query tile of each new segment
+    int32_t order[NOMAS_MAX_SEGS];       // segments in launch order (most keys first)
+    int32_t lt0[NOMAS_MAX_SEGS + 1];     // first launch-order tile of each of them
     int32_t ktile0[NOMAS_MAX_SEGS];      // first key tile (of a head's images) of each segment's region
     int32_t nsel[NOMAS_MAX_SEGS];        // cache tokens each segment sees (its region's first keys)
     SegTable segs;
@@ -406,15 +408,19 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
-    // block = (head * nsplit + split) * ntq + query tile: the workgroups that
-    // share a key range run side by side
+    // block = (head * nsplit + split) * ntq + launch-order query tile: the
+    // workgroups that share a key range run side by side, and the segments
+    // with the most keys go first (packed calls: the last segment), so that
+    // the grid does not end on a few long workgroups
     const int hs = __builtin_amdgcn_readfirstlane(blockIdx.x / A.ntq);
-    const int qt = __builtin_amdgcn_readfirstlane(blockIdx.x - hs * A.ntq);
+    const int li = __builtin_amdgcn_readfirstlane(blockIdx.x - hs * A.ntq);
     const int head = __builtin_amdgcn_readfirstlane(hs / A.nsplit);
     const int split = __builtin_amdgcn_readfirstlane(hs - head * A.nsplit);
 
-    int a = 0;
-    while (a + 1 < A.segs.n && A.tile0[a + 1] <= qt) ++a;
+    int oi = 0;
+    while (oi + 1 < A.segs.n && A.lt0[oi + 1] <= li) ++oi;
+    const int a = A.order[oi];
+    const int qt = A.tile0[a] + (li - A.lt0[oi]);
     const SegDev& sg = A.segs.s[a];
     // workgroup-uniform values, kept in scalar registers so that tile choices
     // are scalar branches and tile bases are scalar addresses
@@ -828,6 +834,22 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     }
     A.tile0[segs.n] = nt;
     A.ntq = nt;
+    // launch order: segments by descending key count (stable)
+    {
+        int nk[NOMAS_MAX_SEGS];
+        for (int i = 0; i < segs.n; ++i) {
+            const SegDev& s = segs.s[i];
+            nk[i] = A.nsel[i] + s.start + s.n_text + s.T * s.Hg * s.Wg;
+            A.order[i] = i;
+        }
+        std::stable_sort(A.order, A.order + segs.n, [&](int x, int y) { return nk[x] > nk[y]; });
+        int t = 0;
+        for (int i = 0; i < segs.n; ++i) {
+            A.lt0[i] = t;
+            t += A.tile0[A.order[i] + 1] - A.tile0[A.order[i]];
+        }
+        A.lt0[segs.n] = t;
+    }
     A.segs = segs;
     A.rt = rt;
     if (nt == 0) return NOMAS_OK;
