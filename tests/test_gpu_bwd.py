@@ -25,12 +25,12 @@ GRAD_REL_L2 = 5e-3
 GRAD_MAX_REL = 2e-2
 
 
-def _grads_gpu(q, k, v, d_out, segs, H):
+def _grads_gpu(q, k, v, d_out, segs, H, sm=SM):
     Ln = q.shape[0]
     qd, kd, vd, dd = dev16(q), dev16(k), dev16(v), dev16(d_out)
     lse = torch.empty((H, Ln), dtype=torch.float32, device="cuda:0")
-    out = nomas.seg_attn(qd, kd, vd, segs, cache_len=0, sm_scale=SM, lse=lse)
-    dq, dk, dv = nomas.seg_attn_bwd(qd, kd, vd, out, lse, dd, segs, sm_scale=SM)
+    out = nomas.seg_attn(qd, kd, vd, segs, cache_len=0, sm_scale=sm, lse=lse)
+    dq, dk, dv = nomas.seg_attn_bwd(qd, kd, vd, out, lse, dd, segs, sm_scale=sm)
     torch.cuda.synchronize()
     return [t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
 
@@ -52,12 +52,12 @@ def _close3(got, ref, name):
         _close(g, r, "%s %s" % (name, w), case_scale)
 
 
-def _check(name, segs, H, seed):
+def _check(name, segs, H, seed, sm=SM):
     L = sum(s[0] + s[2] * s[3] * s[4] for s in segs)
     q, k, v, d_out = (synth.random_bf16(seed + i, (L, H, 128)) for i in range(4))
-    say("seg_attn_bwd", name, "L", L, "H", H, "segs", segs)
-    got = _grads_gpu(q, k, v, d_out, segs, H)
-    ref = oracle.seg_attn_bwd(q, k, v, d_out, segs, SM)
+    say("seg_attn_bwd", name, "L", L, "H", H, "segs", segs[:4], "sm_scale", sm)
+    got = _grads_gpu(q, k, v, d_out, segs, H, sm)
+    ref = oracle.seg_attn_bwd(q, k, v, d_out, segs, sm)
     _close3(got, ref, name)
 
 
@@ -81,12 +81,24 @@ CASES = [
     # several workgroups per segment (1,472 tokens each) and late positions
     ("three-turns", [(64, 18 * i, 2, 22, 32) for i in range(3)], 2),
     ("late-t", [(3, 16000, 2, 7, 5), (0, 9, 1, 30, 33)], 2),
+    # 16 heads; segment lengths that are whole tiles (64 and 128 tokens)
+    ("heads16", [(10, 0, 1, 10, 20), (5, 1, 1, 10, 20)], 16),
+    ("tile-aligned", [(64, 0, 0, 1, 1), (0, 0, 2, 8, 8), (0, 2, 1, 8, 8)], 2),
+    # 40 small segments: long segment tables, one workgroup per segment
+    ("forty-segments", [(1 + (i % 3), i, 1, 2 + (i % 2), 3) for i in range(40)], 2),
 ]
 
 
 @pytest.mark.parametrize("name,segs,H", CASES, ids=[c[0] for c in CASES])
 def test_bwd_matches_oracle(name, segs, H):
     _check(name, segs, H, 500 + 7 * len(name))
+
+
+@pytest.mark.parametrize("sm", [0.3, 0.02])
+def test_bwd_softmax_scale(sm):
+    """A sharp softmax (0.3: scores spread over tens of log units, P close to
+    one-hot) and a flat one (0.02)."""
+    _check("scale-%g" % sm, [(9, 0, 2, 6, 7), (4, 2, 1, 6, 7)], 2, 700, sm)
 
 
 def test_bwd_mask_invariance_bitwise():
