@@ -756,20 +756,33 @@ int build_key_plan(const SegTable& segs, int Lc, int Ln, const int32_t* sel_off,
 int plan_splits(const SegTable& segs, const KeyPlan& kp, const int32_t* seg_reg, int H, int n_split) {
     if (n_split > 0) return n_split;
     int nq = 0, nt_min = 1 << 30;
+    double keys = 0.0;              // sum over query tiles of their key count
     for (int i = 0; i < segs.n; ++i) {
         const SegDev& s = segs.s[i];
         const int ntok = s.n_text + s.T * s.Hg * s.Wg;
         if (ntok == 0) continue;
-        nq += (ntok + BM - 1) / BM;
-        nt_min = std::min(nt_min, (kp.nsel[seg_reg[i]] + s.start + ntok + BN - 1) / BN);
+        const int tiles = (ntok + BM - 1) / BM;
+        const int nk = kp.nsel[seg_reg[i]] + s.start + ntok;
+        nq += tiles;
+        nt_min = std::min(nt_min, (nk + BN - 1) / BN);
+        keys += (double)tiles * nk;
     }
     const int cus = device_cu_count();
     if (nq == 0 || cus <= 0) return 1;
     const int64_t units = (int64_t)nq * H;
+    // Cost in units of one workgroup's whole key range: the rounds of
+    // workgroups the grid takes, plus for p > 1 parts the merge pass, which
+    // moves p * 516 + 260 bytes per (query, head) at HBM speed while the
+    // attention spends 512 FLOP per (query, key, head) on MFMA (about 250
+    // FLOP per byte apart, as measured), and 2% per extra part for the
+    // parts' own prologues and fp32 partial outputs.
+    const double keys_avg = keys / nq;
     int best = 1;
     double best_cost = (double)((units + cus - 1) / cus);
     for (int p = 2; p <= 4 && nt_min / p >= 16; ++p) {
-        const double cost = (double)((units * p + cus - 1) / cus) / p;
+        const double rounds = (double)((units * p + cus - 1) / cus) / p;
+        const double overhead = (p * 516.0 + 260.0) * 250.0 / (512.0 * keys_avg) + 0.02 * (p - 1);
+        const double cost = rounds * (1.0 + overhead);
         if (cost < best_cost - 1e-9) { best = p; best_cost = cost; }
     }
     return best;
