@@ -17,8 +17,11 @@
 // 2 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (A = x rows, B = W rows, both
 // k-contiguous).  K advances in steps of 64: the step's x tile (256 rows) and
 // W tile (256 rows), 128 bytes per row, are copied into LDS by buffer-to-LDS
-// DMA, 16-byte chunk c of row r landing at chunk c ^ (r % 8) of the row so
-// that the fragment reads are free of bank conflicts.  Two stages: step t+1
+// DMA, 16-byte chunk c of row r landing at chunk c ^ ((r / 2) % 8) of the
+// row.  A row is 128 bytes, half of the 64 four-byte banks, so rows 2i and
+// 2i+1 cover the two halves; the swizzle by r / 2 spreads the 16 rows that a
+// ds_read_b128 serves per cycle over all 16 groups of 4 banks, free of
+// conflicts.  Two stages: step t+1
 // is copied into the stage step t-1 left while step t computes.  Reads of
 // x past row M come back as zeros (buffer range checking); stores stop at M.
 #include "common.hpp"
@@ -83,7 +86,7 @@ __device__ __forceinline__ void g_wait() {
 
 // fragment of row `row` (tile-local), k chunk `ch` (8 bf16) from a swizzled tile
 __device__ __forceinline__ gbf16x8 g_frag(const uint8_t* tile, int row, int ch) {
-    return *reinterpret_cast<const gbf16x8*>(tile + row * (GK * 2) + 16 * (ch ^ (row & 7)));
+    return *reinterpret_cast<const gbf16x8*>(tile + row * (GK * 2) + 16 * (ch ^ ((row >> 1) & 7)));
 }
 
 __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
@@ -109,11 +112,13 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     const uint64_t xb = (uint64_t)(uintptr_t)G.x, wbp = (uint64_t)(uintptr_t)G.w;
     const gu32x4 rx = {(uint32_t)xb, (uint32_t)(xb >> 32) & 0xffffu, (uint32_t)G.M * rowb, 0x00020000u};
     const gu32x4 rw = {(uint32_t)wbp, (uint32_t)(wbp >> 32) & 0xffffu, (uint32_t)G.N * rowb, 0x00020000u};
-    // lane l of a 1 KB copy: row l/8 of an 8-row group, chunk (l%8) ^ (l/8) of the row's 128 bytes
-    const uint32_t voff = (uint32_t)(lane >> 3) * rowb + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     // wave w copies 8-row groups w, w+8, w+16, w+24 of the x tile and of the W tile
     const int wv = __builtin_amdgcn_readfirstlane(wave);       // wave-uniform, for scalar DMA operands
+    // lane l of a 1 KB copy lands at row 8 grp + l/8, position l%8 of the row,
+    // which holds chunk (l%8) ^ ((row / 2) % 8) = (l%8) ^ (l/16 + 4 (grp % 2));
+    // grp % 2 = w % 2 for every group the wave copies
+    const uint32_t voff = (uint32_t)(lane >> 3) * rowb + 16u * (uint32_t)((lane & 7) ^ ((lane >> 4) + 4 * (wv & 1)));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
     auto copy_step = [&](int t, int st) {
         const uint32_t kb = (uint32_t)t * (GK * 2);
 #pragma unroll
