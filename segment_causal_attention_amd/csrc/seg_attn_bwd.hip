@@ -399,6 +399,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
 #pragma unroll
         for (int n = 0; n < 48; ++n) {
             if (n + FD < 48) fr[n + FD] = afrag(n + FD);
+            // raised wave priority over the S^T / dP^T products (-1% measured)
+            if (n == 0) __builtin_amdgcn_s_setprio(2);
+            if (n == 32) __builtin_amdgcn_s_setprio(0);
             if (n < 32) {
                 const int kb = n >> 4, m = n & 15;
                 if (m & 1) dp[kb] = mma(fr[n], df[m >> 1], m < 2 ? negd : dp[kb]);
@@ -525,6 +528,9 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
         auto slot = [&](int n) {
             const int u = n >> 5, m = n & 31;
             if (n + KFD < 64) fr[n + KFD] = afrag(n + KFD);
+            // raised wave priority over the S and dP products of each half
+            if (m == 0) __builtin_amdgcn_s_setprio(2);
+            if (m == 16) __builtin_amdgcn_s_setprio(0);
             if (m == 4) dp = pad16(QI_DOT, u);
             if (m == 28 && u == 0) sc = pad16(QI_QT, 1);
             if (m < 8) sc = mma(fr[n], kf[m], sc);
