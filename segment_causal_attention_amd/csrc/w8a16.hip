@@ -149,6 +149,10 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
         const uint8_t* wt = xt + GTILE;
 #pragma unroll
         for (int kk = 0; kk < GK / 16; ++kk) {
+            // raised wave priority over the first half of the step's products
+            // (-1 to -3% on the model shapes)
+            if (kk == 0) __builtin_amdgcn_s_setprio(2);
+            if (kk == 2) __builtin_amdgcn_s_setprio(0);
             gbf16x8 a[2], b[4];
 #pragma unroll
             for (int i = 0; i < 2; ++i) a[i] = g_frag(xt, wm + 32 * i + l32, 2 * kk + g);
