@@ -386,10 +386,11 @@ __device__ __forceinline__ float pipelined_step(const uint16_t* Kn, const uint16
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         if (i + FD < 32) fr[i + FD] = frag(i + FD);
-        // the S^T half of the step issues at a raised wave priority: the
-        // SIMD's other wave then tends to be in its O^T half (measured -0.8%)
+        // the S^T products and the first O^T products of the step issue at a
+        // raised wave priority, so the SIMD's two waves drift apart in phase
+        // (measured -1.3% against no priority change; ending at slot 16: -0.8%)
         if (i == 0) __builtin_amdgcn_s_setprio(2);
-        if (i == 16) __builtin_amdgcn_s_setprio(0);
+        if (i == 20) __builtin_amdgcn_s_setprio(0);
         if (i < 16) sn[i & 1] = mfma(fr[i], w.qf[i >> 1], i < 2 ? zero : sn[i & 1]);
         else w.o[i & 3] = mfma(fr[i], pchunk(pk, (i - 16) >> 2), w.o[i & 3]);
         // rescale of tile j
