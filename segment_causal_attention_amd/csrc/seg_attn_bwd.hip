@@ -252,10 +252,10 @@ struct BwdArgs {
 };
 static_assert(sizeof(BwdArgs) <= 4000, "kernel arguments are passed by value");
 
-// Workgroup -> (segment, head, first tile).  A workgroup of the dQ kernel
-// covers 4 tiles (8 waves), one of the dK/dV kernel 2 tiles (4 waves); wave w
-// takes tile tile0 + NTL wg + w/2, tokens 32 (w%2) .. +32 of it.  Waves past
-// the segment's last tile repeat that tile and store nothing.
+// Workgroup -> (segment, head, first tile).  A workgroup (8 waves) covers
+// NTL = 4 tiles of one segment; wave w takes tile tile0 + NTL wg + w/2,
+// tokens 32 (w%2) .. +32 of it.  Waves past the segment's last tile repeat
+// that tile and store nothing.
 struct WgPos {
     int a, head, tile, row;
     bool live;
@@ -451,6 +451,10 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
 }
 
 // ---- dK, dV: lane = key ------------------------------------------------------
+//
+// Per query tile and wave (64 queries x 32 keys, 64 products) two halves of
+// 32 queries, each: the S products, the dP products with P formed in their
+// slots, the dV^T products with dS formed in theirs, the dK^T products.
 
 __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[QBUF * QIMG];
