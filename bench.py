@@ -112,7 +112,7 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS["fullcache"]
     H, Lq, Lc = cfg.H, cfg.Lq, cfg.Lc
     (seg,) = cfg.new_segs
     (hseg,) = cfg.hist_segs
@@ -121,7 +121,7 @@ def main():
     Nc = 72
 
     t0 = time.time()
-    inp = synth.layer_inputs(4)
+    inp = synth.layer_inputs("fullcache")
     cam_in = synth.turn_inputs(0, with_cam=True)
     log("inputs generated in %.1f s" % (time.time() - t0))
 
@@ -304,8 +304,8 @@ def workloads(only=None):
     if want("turn3s"):
         # ---- turn3s
         log("workload turn3s")
-        cfg = synth.CONFIGS[2]
-        inp = synth.layer_inputs(2)
+        cfg = synth.WORKLOADS["turn3s"]
+        inp = synth.layer_inputs("turn3s")
         (seg,) = cfg.new_segs
         cache = build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs, cfg.H, cfg.Lc)
         q, k, v = d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])
@@ -319,12 +319,12 @@ def workloads(only=None):
     if want("seg4s"):
         # ---- seg4s: 54 layers resident, 8 steps over all of them
         log("workload seg4s: 54 layers resident, 8 steps over all of them")
-        cfg = synth.CONFIGS[3]
+        cfg = synth.WORKLOADS["seg4s"]
         (seg,) = cfg.new_segs
         layers = []
         t0 = time.time()
         for l in range(cfg.layers):
-            inp = synth.layer_inputs(3, l)
+            inp = synth.layer_inputs("seg4s", l)
             cache = build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs, cfg.H, cfg.Lc)
             layers.append((d16(inp["q"]), d16(inp["k_new"]), d16(inp["v_new"])) + cache)
             del inp
@@ -348,7 +348,7 @@ def workloads(only=None):
     if want("fiveturns"):
         # ---- fiveturns
         log("workload fiveturns")
-        cfg = synth.CONFIGS[5]
+        cfg = synth.WORKLOADS["fiveturns"]
         H = cfg.H
         n = synth.turn_seg(0).ntok
         cache = build_cache(None, None, None, H, 5 * n)
@@ -421,8 +421,8 @@ def workloads(only=None):
     if want("fullcache"):
         # ---- fullcache-sel18 and fullcache-h2 share the full-cache inputs
         log("workload fullcache-sel18 / fullcache-h2: generating the full-cache inputs")
-        cfg = synth.CONFIGS[4]
-        inp = synth.layer_inputs(4)
+        cfg = synth.WORKLOADS["fullcache"]
+        inp = synth.layer_inputs("fullcache")
         (seg,) = cfg.new_segs
         (hseg,) = cfg.hist_segs
         frame = hseg.Hg * hseg.Wg

@@ -91,20 +91,21 @@ class Config:
 
 TINY_SEGS = (Seg(16, 0, 2, 4, 6), Seg(16, 2, 2, 4, 6), Seg(16, 4, 2, 4, 6))
 
-CONFIGS = {
-    1: Config(1, "tiny", 2, new_segs=(TINY_SEGS[1],), hist_segs=(TINY_SEGS[0],),
+# The workloads by name; cid seeds their random streams.
+WORKLOADS = {
+    "tiny": Config(1, "tiny", 2, new_segs=(TINY_SEGS[1],), hist_segs=(TINY_SEGS[0],),
               notes="2 segments of 16 text + 2x4x6 video tokens; packed and "
                     "3-segment variants drawn from the same streams"),
-    2: Config(2, "turn3s", 16, new_segs=(Seg(256, 18, 18, HG, WG),),
+    "turn3s": Config(2, "turn3s", 16, new_segs=(Seg(256, 18, 18, HG, WG),),
               hist_segs=(Seg(0, 0, 18, HG, WG),),
               notes="3 s turn: 18 latent frames + 256 text vs 18-frame INT8 history"),
-    3: Config(3, "seg4s", 16, new_segs=(Seg(256, 18, 24, HG, WG),),
+    "seg4s": Config(3, "seg4s", 16, new_segs=(Seg(256, 18, 24, HG, WG),),
               hist_segs=(Seg(0, 0, 18, HG, WG),), outliers=20, layers=54, steps=8,
               notes="4 s segment, 1% of the 2048 hidden channels x20 in Q/K, 54 layers x 8 steps"),
-    4: Config(4, "fullcache", 16, new_segs=(Seg(0, 288, 72, HG, WG),),
+    "fullcache": Config(4, "fullcache", 16, new_segs=(Seg(0, 288, 72, HG, WG),),
               hist_segs=(Seg(0, 0, 288, HG, WG),),
               notes="12 s segment vs 288 cached latent frames (~317K keys)"),
-    5: Config(5, "fiveturns", 16, new_segs=(Seg(0, 0, 72, HG, WG),), hist_segs=(),
+    "fiveturns": Config(5, "fiveturns", 16, new_segs=(Seg(0, 0, 72, HG, WG),), hist_segs=(),
               turns=5, cam_frames=288,
               notes="5 turns of 72 latent frames; cache grows by 63,360 tokens a turn"),
 }
@@ -225,7 +226,7 @@ def tiny_inputs():
     q/k/v are drawn for all 192 tokens; cache mode uses segment 0's k/v as the
     history and segment 1 as the new segment, the packed mode takes segments
     0 and 1 as new tokens, the 3-segment mode caches segment 0 and takes 1, 2."""
-    cfg = CONFIGS[1]
+    cfg = WORKLOADS["tiny"]
     L = seg_tokens(TINY_SEGS)
     shp = (L, cfg.H, D)
     return dict(cfg=cfg, segs=TINY_SEGS,
@@ -234,10 +235,12 @@ def tiny_inputs():
                 v=bf16_tensor(1, 0, "v_new", shp))
 
 
-def layer_inputs(cid: int, inst: int = 0, with_hist: bool = True):
+def layer_inputs(name: str, inst: int = 0, with_hist: bool = True):
     """q, k_new, v_new [Lq][H][128] and k_hist, v_hist [Lc][H][128] (pre-RoPE
-    history keys) as bf16 bits for configs 2, 3 (one layer) and 4."""
-    cfg = CONFIGS[cid]
+    history keys) as bf16 bits for the turn3s, seg4s (one layer) and
+    fullcache workloads."""
+    cfg = WORKLOADS[name]
+    cid = cfg.cid
     cols = outlier_columns(cfg, inst)
     shp = (cfg.Lq, cfg.H, D)
     out = dict(cfg=cfg, outlier_cols=cols,
@@ -254,7 +257,7 @@ def layer_inputs(cid: int, inst: int = 0, with_hist: bool = True):
 def turn_inputs(k: int, with_cam: bool = True):
     """Turn k of the five-turn workload: new-segment q/k/v, camera queries for
     the video tokens, a 288-frame c2w path and the camera K/V projections."""
-    cfg = CONFIGS[5]
+    cfg = WORKLOADS["fiveturns"]
     seg = turn_seg(k)
     shp = (seg.ntok, cfg.H, D)
     out = dict(cfg=cfg, seg=seg,

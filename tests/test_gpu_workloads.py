@@ -51,11 +51,12 @@ def check_rows(name, out, lse, inp_q, inp_k, inp_v, segs, ocache, Lc, rows, head
     np.testing.assert_allclose(gl, lref, rtol=0, atol=2.0 ** -8)
 
 
-@pytest.mark.parametrize("cid,layer", [(2, 0), (3, 0), (3, 53)], ids=["turn3s", "seg4s-layer0", "seg4s-layer53"])
-def test_attention_with_oracle_cache(cid, layer):
+@pytest.mark.parametrize("name,layer", [("turn3s", 0), ("seg4s", 0), ("seg4s", 53)],
+                         ids=["turn3s", "seg4s-layer0", "seg4s-layer53"])
+def test_attention_with_oracle_cache(name, layer):
     """3 s turn and 4 s segment (with outliers): the INT8 history comes from
     the oracle's quantiser, byte for byte."""
-    inp = synth.layer_inputs(cid, layer)
+    inp = synth.layer_inputs(name, layer)
     cfg = inp["cfg"]
     if cfg.outliers:
         assert len(inp["outlier_cols"]) == 20
@@ -63,7 +64,7 @@ def test_attention_with_oracle_cache(cid, layer):
     ocache = oracle.build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs)
     gcache = tuple(dev(a) for a in ocache)
     out, lse = run_attn(dev16(inp["q"]), dev16(inp["k_new"]), dev16(inp["v_new"]), cfg.new_segs, gcache, cfg.Lc, cfg.H)
-    rows = sample_rows(cfg.Lq, 16 if cid == 2 else 64, extra=range(250, 262))
+    rows = sample_rows(cfg.Lq, 16 if name == "turn3s" else 64, extra=range(250, 262))
     check_rows("%s layer %d" % (cfg.name, layer), out, lse, inp["q"], inp["k_new"], inp["v_new"], cfg.new_segs,
                ocache, cfg.Lc, rows)
 
@@ -104,7 +105,7 @@ def check_cache_rows(name, cache, start, k_rot_d, k_bits, v_bits, segs, heads):
 def test_full_cache_workload():
     """12 s segment over 288 cached latent frames (~317K keys), cache built on
     the GPU exactly as the benchmark builds it."""
-    inp = synth.layer_inputs(4)
+    inp = synth.layer_inputs("fullcache")
     cfg = inp["cfg"]
     H, Lq, Lc = cfg.H, cfg.Lq, cfg.Lc
     heads = [0, 9]
@@ -142,7 +143,7 @@ def test_five_turns_growing_cache():
     """Five 12 s turns: each turn attends over the cache of all earlier turns,
     runs camera cross-attention, then rotates and appends its keys/values.
     Quantisation is checked every turn, attention and camera on turns 0 and 4."""
-    cfg = synth.CONFIGS[5]
+    cfg = synth.WORKLOADS["fiveturns"]
     H = cfg.H
     cap = 5 * synth.turn_seg(0).ntok
     cache = cache_tensors(H, cap)

@@ -38,7 +38,7 @@ def test_latent_frames_per_second():
     assert val("fps") // val("vae_temporal") == 6
     # a 12 s turn is 72 latent frames = 288 video frames = 72 camera tokens
     assert 12 * val("fps") // val("vae_temporal") == 72
-    assert synth.turn_seg(0).T == 72 and synth.CONFIGS[5].cam_frames == 12 * val("fps")
+    assert synth.turn_seg(0).T == 72 and synth.WORKLOADS["fiveturns"].cam_frames == 12 * val("fps")
 
 
 def test_camera_token_width():
@@ -46,6 +46,6 @@ def test_camera_token_width():
 
 
 def test_history_window_in_workloads():
-    for cid in (2, 3):
-        (hseg,) = synth.CONFIGS[cid].hist_segs
+    for name in ("turn3s", "seg4s"):
+        (hseg,) = synth.WORKLOADS[name].hist_segs
         assert hseg.T == val("history_latent_frames")
