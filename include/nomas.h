@@ -218,7 +218,7 @@ int64_t nomas_seg_attn_workspace(const nomas_seg* new_segs, int n_new_segs, int6
  * segs: the packed segments (the forward's new_segs), L = their token count.
  * workspace: device scratch of at least nomas_seg_attn_bwd_workspace(...)
  *   bytes, 16-byte aligned, owned by the caller (each segment's tokens laid
- *   out as 64-token tiles: 124,928 bytes per tile and head); two calls in
+ *   out as 64-token tiles: 70,656 bytes per tile and head); two calls in
  *   flight must not share one.  Pointers 16-byte aligned (lse 4).
  * Errors as nomas_seg_attn; L * H <= NOMAS_MAX_TOKEN_HEADS.
  */
@@ -229,7 +229,7 @@ int nomas_seg_attn_bwd(const nomas_bf16* q, const nomas_bf16* k, const nomas_bf1
                        void* stream);
 
 /*
- * Workspace bytes nomas_seg_attn_bwd needs: H * 124,928 * (sum over the
+ * Workspace bytes nomas_seg_attn_bwd needs: H * 70,656 * (sum over the
  * segments of ceil(tokens / 64)); or a negative error code.  Host only.
  */
 int64_t nomas_seg_attn_bwd_workspace(const nomas_seg* segs, int n_segs, int H);

@@ -22,24 +22,25 @@
 // exactly zero to every gradient, so no kernel masks anything.  A pack kernel
 // writes two images per tile, each a byte image of what an attention kernel
 // wants in LDS:
-//   query tile (71,680 B): Q rows [64][136] and dO rows [64][136] bf16;
-//     Q^T and dO^T [128][72] bf16 with each 16-token chunk in the order
-//     [0-3, 8-11, 4-7, 12-15]; the row padding of Q^T rows 0-15 holds
-//     -lse / sm_scale of the tile's tokens, that of dO^T rows 0-15 holds -D.
-//   key tile (53,248 B): K rows, V rows [64][136], K^T [128][72] permuted.
-// Row strides are padded by 16 bytes against LDS bank conflicts.
+//   query tile (35,840 B): Q rows [64][136] and dO rows [64][136] bf16, then
+//     -lse / sm_scale and -D of the tile's tokens (fp32 [64] each).
+//   key tile (34,816 B): K rows and V rows [64][136] bf16.
+// Row strides are padded by 16 bytes, and within each 16-token block token
+// 4a + b sits at row 4b + a, so that the plain row reads and the transposing
+// reads below both hit distinct LDS banks.
 //
 // Two attention kernels, both on v_mfma_f32_32x32x16_bf16, 8 waves of 32
-// tokens per workgroup, tiles copied into LDS by buffer-to-LDS DMA:
+// tokens per workgroup, tiles copied into LDS by buffer-to-LDS DMA, four
+// buffers deep:
 //   dK/dV kernel, key on the MFMA's N side (one lane column = one key):
 //     S = Q K^T and dP = dO V^T (A = Q, dO rows from LDS; B = the wave's K, V
 //     held in registers), then dV^T += dO^T P and dK^T += Q^T dS (A = dO^T,
-//     Q^T from LDS; B = P, dS straight from the accumulators, which is why
-//     the transposed images carry the chunk permutation).  It walks the
-//     query tiles of its segment and every later one.
+//     Q^T read from the same rows by the LDS transpose read; B = P, dS
+//     straight from the accumulators).  It walks the query tiles of its
+//     segment and every later one.
 //   dQ kernel, query on the N side: S^T = K Q^T and dP^T = V dO^T (A = K, V
-//     rows; B = the wave's Q, dO in registers), then dQ^T += K^T dS^T.  It
-//     walks the key tiles of segments 0..a.
+//     rows; B = the wave's Q, dO in registers), then dQ^T += K^T dS^T (K^T
+//     by the transpose read).  It walks the key tiles of segments 0..a.
 // S and dP are recomputed by both kernels instead of exchanging dQ partials
 // between workgroups; at training lengths the pairs outnumber the tokens by
 // five orders of magnitude, so any per-pair or per-block-pair exchange would
@@ -56,38 +57,31 @@ namespace {
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef short s4v __attribute__((ext_vector_type(4)));
 
 constexpr int TB = 64;                          // tokens per image tile
 constexpr int RSTR = D + 8;                     // row stride (bf16) of [token][channel] images
-constexpr int CSTR = TB + 8;                    // row stride (bf16) of [channel][token] images
 constexpr int ROWIMG = TB * RSTR * 2;           // 17408
-constexpr int COLIMG = D * CSTR * 2;            // 18432
 constexpr int QI_DO = ROWIMG;                   // query image: dO rows
-constexpr int QI_QT = 2 * ROWIMG;               //              Q^T
-constexpr int QI_DOT = 2 * ROWIMG + COLIMG;     //              dO^T
-constexpr int QIMG = 2 * ROWIMG + 2 * COLIMG;   // 71680
+constexpr int QI_LSE = 2 * ROWIMG;              //              -lse / sm_scale, fp32 [64]
+constexpr int QI_D = 2 * ROWIMG + 4 * TB;       //              -D, fp32 [64]
+constexpr int QIMG = 35 * 1024;                 // 35840 (35,328 used)
 constexpr int KI_V = ROWIMG;                    // key image: V rows
-constexpr int KI_KT = 2 * ROWIMG;               //            K^T
-constexpr int KIMG = 2 * ROWIMG + COLIMG;       // 53248
-constexpr int QIMG_KB = QIMG / 1024;            // 70 one-kilobyte DMA copies
-constexpr int KIMG_KB = KIMG / 1024;            // 52
-constexpr int PAD = 2 * TB;                     // byte offset of the padding in a [channel][token] row
-static_assert(QIMG % 1024 == 0 && KIMG % 1024 == 0, "tile images are copied in 1 KB pieces");
+constexpr int KIMG = 2 * ROWIMG;                // 34816
+constexpr int QIMG_KB = QIMG / 1024;            // 35 one-kilobyte DMA copies
+constexpr int KIMG_KB = KIMG / 1024;            // 34
+static_assert(QIMG % 1024 == 0 && KIMG % 1024 == 0 && QI_D + 4 * TB <= QIMG, "tile images are copied in 1 KB pieces");
 
 constexpr int NW = 8;                           // waves per workgroup (2 per SIMD)
 constexpr int NT = NW * 64;
 constexpr int WT = 32;                          // tokens per wave
 constexpr int WG_TILES = NW * WT / TB;          // image tiles per workgroup (4)
-constexpr int KBUF = 3;                         // key-tile buffers of the dQ kernel
-constexpr int QBUF = 2;                         // query-tile buffers of the dK/dV kernel
+constexpr int KBUF = 4;                         // key-tile buffers of the dQ kernel
+constexpr int QBUF = 4;                         // query-tile buffers of the dK/dV kernel
 constexpr int PACK_NT = 256;
 
-// position of token k of a tile in a permuted [channel][token] row
-__device__ __forceinline__ int tperm(int k) {
-    const int w = k & 15;
-    const int p = w < 4 ? w : w < 8 ? w + 4 : w < 12 ? w - 4 : w;
-    return (k & ~15) + p;
-}
+// image row of token k of a tile: token 4a + b of each 16-token block at row 4b + a
+__device__ __forceinline__ int trow(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
 
 __device__ __forceinline__ f16v mma(b8 a, b8 b, f16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -138,8 +132,6 @@ struct PackBwdArgs {
 static_assert(sizeof(PackBwdArgs) <= 4000, "kernel arguments are passed by value");
 
 __global__ __launch_bounds__(PACK_NT) void bwd_pack_kernel(const PackBwdArgs P) {
-    __shared__ __attribute__((aligned(16))) uint16_t ct[2][D * CSTR];   // transposed images
-    __shared__ float pad[2][TB];
     const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const bool is_q = blockIdx.z == 0;
     int a = 0;
@@ -178,9 +170,10 @@ __global__ __launch_bounds__(PACK_NT) void bwd_pack_kernel(const PackBwdArgs P) 
         }
         dsum += __shfl_xor(dsum, 1);
         dsum += __shfl_xor(dsum, 2);
+        // -lse / sm_scale (so that P = 2^(sm_scale log2(e) (s + it))) and -D
         if (qd == 0) {
-            pad[0][row] = valid ? -P.lse[(size_t)h * P.Ln + tok] / P.sm_scale : -INFINITY;
-            pad[1][row] = valid ? -dsum : 0.0f;
+            reinterpret_cast<float*>(img + QI_LSE)[row] = valid ? -P.lse[(size_t)h * P.Ln + tok] / P.sm_scale : -INFINITY;
+            reinterpret_cast<float*>(img + QI_D)[row] = valid ? -dsum : 0.0f;
         }
     } else {
 #pragma unroll
@@ -193,8 +186,8 @@ __global__ __launch_bounds__(PACK_NT) void bwd_pack_kernel(const PackBwdArgs P) 
         }
     }
     // the two row images (Q, dO or K, V), padding zero
-    uint4* r0 = reinterpret_cast<uint4*>(img + row * RSTR * 2);
-    uint4* r1 = reinterpret_cast<uint4*>(img + ROWIMG + row * RSTR * 2);
+    uint4* r0 = reinterpret_cast<uint4*>(img + trow(row) * RSTR * 2);
+    uint4* r1 = reinterpret_cast<uint4*>(img + ROWIMG + trow(row) * RSTR * 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         r0[4 * qd + j] = a0[j];
@@ -204,36 +197,6 @@ __global__ __launch_bounds__(PACK_NT) void bwd_pack_kernel(const PackBwdArgs P) 
         r0[D / 8] = make_uint4(0, 0, 0, 0);
         r1[D / 8] = make_uint4(0, 0, 0, 0);
     }
-    // transposed images through LDS (Q^T, dO^T or K^T)
-    const int ncol = is_q ? 2 : 1;
-    const int pc = tperm(row);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t w0[4] = {a0[j].x, a0[j].y, a0[j].z, a0[j].w};
-        const uint32_t w1[4] = {a1[j].x, a1[j].y, a1[j].z, a1[j].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int ch = 8 * (4 * qd + j) + e;
-            ct[0][ch * CSTR + pc] = (uint16_t)(w0[e >> 1] >> (16 * (e & 1)));
-            if (is_q) ct[1][ch * CSTR + pc] = (uint16_t)(w1[e >> 1] >> (16 * (e & 1)));
-        }
-    }
-    __syncthreads();
-    // padding of the transposed rows: rows 0-15 of Q^T carry -lse/sm_scale of
-    // tokens 4i..4i+3 (so that P = 2^(sm_scale log2(e) (s + pad))), those of
-    // dO^T carry -D; the rest zero
-    if (tid < ncol * D) {
-        const int m = tid / D, i = tid % D;
-        uint4 pv = make_uint4(0, 0, 0, 0);
-        if (is_q && i < TB / 4)
-            pv = make_uint4(__float_as_uint(pad[m][4 * i]), __float_as_uint(pad[m][4 * i + 1]),
-                            __float_as_uint(pad[m][4 * i + 2]), __float_as_uint(pad[m][4 * i + 3]));
-        *reinterpret_cast<uint4*>(&ct[m][i * CSTR + TB]) = pv;
-    }
-    __syncthreads();
-    uint4* dst = reinterpret_cast<uint4*>(img + 2 * ROWIMG);
-    const uint4* srcl = reinterpret_cast<const uint4*>(&ct[0][0]);
-    for (int i = tid; i < ncol * COLIMG / 16; i += PACK_NT) dst[i] = srcl[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -290,13 +253,25 @@ __device__ __forceinline__ float4 unrotate4(float4 x, float s, bool vid, int grp
                        x.z * cs.z + x.w * cs.w, x.w * cs.z - x.z * cs.w);
 }
 
-// dO^T / Q^T / K^T fragment: channel row `ch`, 16-token chunk `k16`, lane half g
-__device__ __forceinline__ b8 colfrag(const uint8_t* img, int ch, int k16, int g) {
-    return ldfrag(img + ch * CSTR * 2 + 32 * k16 + 16 * g);
-}
-// Q / dO / K / V row fragment: token row `r`, channels 16 s + 8 g
+// Q / dO / K / V row fragment: token `r`, channels 16 s + 8 g
 __device__ __forceinline__ b8 rowfrag(const uint8_t* img, int r, int s, int g) {
-    return ldfrag(img + r * RSTR * 2 + 32 * s + 16 * g);
+    return ldfrag(img + trow(r) * RSTR * 2 + 32 * s + 16 * g);
+}
+// Transposed fragment (A operand of dO^T, Q^T or K^T) from a row image in
+// LDS: lane (channel ch0 + l32, half g) gets tokens 16 k16 + 4 g + 0..3 and
+// 16 k16 + 8 + 4 g + 0..3, the token order in which the B operand leaves the
+// accumulators.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane 4e + m
+// of a group names 4 consecutive elements of row e, and lane r of the group
+// receives element r of rows 0..3.  So lane 4e + m of group (g, h) names
+// token 16 k16 + 4 g + e (+8 for the second read), channels ch0 + 16 h + 4 m.
+__device__ __forceinline__ b8 trfrag(const uint8_t* img, int ch0, int k16, int lane) {
+    const int e = (lane >> 2) & 3, g = lane >> 5;
+    const int ch = ch0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // trow(16 k16 + 4 g + e) = 16 k16 + 4 e + g; the +8 token is two rows on
+    uint8_t* p = const_cast<uint8_t*>(img) + (16 * k16 + 4 * e + g) * RSTR * 2 + 2 * ch;
+    const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)p);
+    const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p + 2 * RSTR * 2));
+    return __builtin_bit_cast(b8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Nothing is scheduled across this point: it pins the order of the slots of
@@ -326,9 +301,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
         qf[s] = rowfrag(qi, qrow, s, g);
         df[s] = rowfrag(qi + QI_DO, qrow, s, g);
     }
-    // lse2 = lse log2(e) and D of this lane's query, from the image padding
-    const float lse2 = -A.c * *reinterpret_cast<const float*>(qi + QI_QT + (qrow >> 2) * CSTR * 2 + PAD + 4 * (qrow & 3));
-    const float dd = -*reinterpret_cast<const float*>(qi + QI_DOT + (qrow >> 2) * CSTR * 2 + PAD + 4 * (qrow & 3));
+    // lse2 = lse log2(e) and D of this lane's query
+    const float lse2 = -A.c * reinterpret_cast<const float*>(qi + QI_LSE)[qrow];
+    const float dd = -reinterpret_cast<const float*>(qi + QI_D)[qrow];
     f16v acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -357,22 +332,23 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
     for (int r = 0; r < 16; ++r) negd[r] = -dd;
     copy(0);
     copy(1);
-    // tile j lives in buffer j % 3; the loop is unrolled by 3 so that every
+    copy(2);
+    // tile j lives in buffer j % 4; the loop is unrolled by 4 so that every
     // LDS operand address is the lane's base plus an immediate offset
     auto tile_step = [&](int j, auto bufc) {
         constexpr int bi = decltype(bufc)::value;
-        // this wave's copies of tile j have landed once at most those of tile j+1 are in flight
-        if (wv < KIMG_KB % NW) dma_wait<(KIMG_KB + NW - 1) / NW>();
-        else dma_wait<KIMG_KB / NW>();
+        // this wave's copies of tile j have landed once at most those of tiles j+1, j+2 are in flight
+        if (wv < KIMG_KB % NW) dma_wait<2 * ((KIMG_KB + NW - 1) / NW)>();
+        else dma_wait<2 * (KIMG_KB / NW)>();
         lds_barrier();
-        copy(j + 2);        // into the buffer of tile j-1, which every wave has finished
+        copy(j + 3);        // into the buffer of tile j-1, which every wave has finished
         const uint8_t* K = lds + bi * KIMG;
         // operand of product n: 0-31 S^T / dP^T of key blocks 0 and 1
         // (even n: K rows, odd n: V rows; channel step (n % 16) / 2), 32-47
         // dQ^T: channel block (n - 32) % 4, 16-key chunk (n - 32) / 4
         auto afrag = [&](int n) {
             if (n < 32) return rowfrag(K + ((n & 1) ? KI_V : 0), 32 * (n >> 4) + l32, (n & 15) >> 1, g);
-            return colfrag(K + KI_KT, 32 * ((n - 32) & 3) + l32, (n - 32) >> 2, g);
+            return trfrag(K, 32 * ((n - 32) & 3), (n - 32) >> 2, lane);
         };
         f16v s[2], dp[2];
         uint32_t pk[16];
@@ -429,6 +405,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
         tile_step(j, std::integral_constant<int, 0>{});
         if (j + 1 < nk) tile_step(j + 1, std::integral_constant<int, 1>{});
         if (j + 2 < nk) tile_step(j + 2, std::integral_constant<int, 2>{});
+        if (j + 3 < nk) tile_step(j + 3, std::integral_constant<int, 3>{});
     }
     dma_wait<0>();
 
@@ -493,37 +470,38 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
     };
     const float c = A.c;
     copy(0);
-    // tile j lives in buffer j % 2; the loop is unrolled by 2 so that every
-    // LDS operand address is the lane's base plus an immediate offset
-    auto tile_step = [&](int j, auto bufc) {
-        constexpr int bi = decltype(bufc)::value;
-        dma_wait<0>();
+    copy(1);
+    copy(2);
+    // tile j lives in buffer j % 4 (the buffer's base is added once per tile)
+    auto tile_step = [&](int j, int bi) {
+        // this wave's copies of tile j have landed once at most those of tiles j+1, j+2 are in flight
+        if (wv < QIMG_KB % NW) dma_wait<2 * ((QIMG_KB + NW - 1) / NW)>();
+        else dma_wait<2 * (QIMG_KB / NW)>();
         lds_barrier();
-        if (j + 1 < nq) copy(j + 1);    // into the buffer of tile j-1, which every wave has finished
+        copy(j + 3);        // into the buffer of tile j-1, which every wave has finished
         const uint8_t* Q = lds + bi * QIMG;
         // Per 32-query half u, 32 slots of one product each: S (slots 0-7),
         // dP (8-15) with P formed in their slots, dV^T (16-23) with dS formed
         // in theirs, dK^T (24-31).  Register r of S and dP holds query
-        // 32 u + 8 (r/4) + 4 g + r%4, whose -lse/sm_scale and -D sit in the
-        // padding of transposed row 8 u + 2 (r/4) + g: they are the initial
-        // accumulators, so S + pad gives P = 2^(c (S + pad)) and dP - D
-        // comes out of the products.
+        // 32 u + 8 (r/4) + 4 g + r%4, whose -lse/sm_scale and -D are the
+        // initial accumulators, so S + pad gives P = 2^(c (S + pad)) and
+        // dP - D comes out of the products.
         auto afrag = [&](int n) {
             const int u = n >> 5, m = n & 31;
             if (m < 16) return rowfrag(Q + (m < 8 ? 0 : QI_DO), 32 * u + l32, m & 7, g);
             const int ch = (m >> 2) & 1, db = m & 3;
-            return colfrag(Q + (m < 24 ? QI_DOT : QI_QT), 32 * db + l32, 2 * u + ch, g);
+            return trfrag(Q + (m < 24 ? QI_DO : 0), 32 * db, 2 * u + ch, lane);
         };
         auto pad16 = [&](int off, int u) {
             f16v x;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 v = *reinterpret_cast<const float4*>(Q + off + (8 * u + 2 * r4 + g) * CSTR * 2 + PAD);
+                const float4 v = *reinterpret_cast<const float4*>(Q + off + 4 * (32 * u + 8 * r4 + 4 * g));
                 x[4 * r4] = v.x; x[4 * r4 + 1] = v.y; x[4 * r4 + 2] = v.z; x[4 * r4 + 3] = v.w;
             }
             return x;
         };
-        f16v sc = pad16(QI_QT, 0), dp;
+        f16v sc = pad16(QI_LSE, 0), dp;
         uint32_t pp[8], ps[8];
         b8 fr[64];
 #pragma unroll
@@ -535,8 +513,8 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
             // raised wave priority over the S and dP products of each half
             if (m == 0) __builtin_amdgcn_s_setprio(2);
             if (m == 16) __builtin_amdgcn_s_setprio(0);
-            if (m == 4) dp = pad16(QI_DOT, u);
-            if (m == 28 && u == 0) sc = pad16(QI_QT, 1);
+            if (m == 4) dp = pad16(QI_D, u);
+            if (m == 28 && u == 0) sc = pad16(QI_LSE, 1);
             if (m < 8) sc = mma(fr[n], kf[m], sc);
             else if (m < 16) dp = mma(fr[n], vf[m - 8], dp);
             else if (m < 24) dv[m & 3] = mma(fr[n], chunk4(pp + 4 * ((m >> 2) & 1)), dv[m & 3]);
@@ -561,10 +539,7 @@ __global__ __launch_bounds__(NT) void bwd_dkv_kernel(const BwdArgs A) {
 #pragma unroll
         for (int n = 32; n < 64; ++n) slot(n);
     };
-    for (int j = 0; j < nq; j += QBUF) {
-        tile_step(j, std::integral_constant<int, 0>{});
-        if (j + 1 < nq) tile_step(j + 1, std::integral_constant<int, 1>{});
-    }
+    for (int j = 0; j < nq; ++j) tile_step(j, j & 3);
     dma_wait<0>();
 
     // epilogue: dk = R^T (sm_scale dK^T), dv, fp32

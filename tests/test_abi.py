@@ -237,12 +237,12 @@ def test_w8a16_host_checks():
 
 
 def test_seg_attn_bwd_host_checks():
-    """Backward pass: workspace = H x (tiles) x 124,928 bytes, every segment
+    """Backward pass: workspace = H x (tiles) x 70,656 bytes, every segment
     starting a new 64-token tile; bad arguments are rejected on the host."""
     L = nomas.lib()
     P = ctypes.c_void_p
     sa, n = segs((16, 0, 2, 4, 6), (3, 2, 1, 2, 2), (0, 0, 0, 0, 0), (70, 0, 0, 1, 1))
-    assert L.nomas_seg_attn_bwd_workspace(sa, n, 2) == 2 * (1 + 1 + 0 + 2) * 124928
+    assert L.nomas_seg_attn_bwd_workspace(sa, n, 2) == 2 * (1 + 1 + 0 + 2) * 70656
     assert L.nomas_seg_attn_bwd_workspace(sa, n, 0) == nomas.EINVAL
     assert L.nomas_seg_attn_bwd_workspace(sa, 0, 2) == nomas.EINVAL
     assert L.nomas_seg_attn_bwd_workspace(sa, n, 300) == nomas.EUNSUPPORTED
