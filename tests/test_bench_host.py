@@ -1,0 +1,42 @@
+"""Host-side behaviour of bench.py that needs no GPU: the refusal of more
+than one GPU, and the rule that HBM traffic from the committed counter
+summary is reported only for the kernel source it was measured on."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=300)
+    assert r.returncode == 2
+    assert r.stdout == ""
+    assert "one MI355X" in r.stderr
+
+
+def test_traffic_only_for_the_measured_kernel_source(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    # no summary at all
+    assert bench.traffic_for_current_kernel() is None
+    # a summary taken on the current source
+    f.write_text(json.dumps({"kernel_digest": bench.kernel_digest(), "hbm_bytes_per_launch": 1234.0}))
+    assert bench.traffic_for_current_kernel() == 1234.0
+    # one taken on another source
+    f.write_text(json.dumps({"kernel_digest": "0" * 16, "hbm_bytes_per_launch": 1234.0}))
+    assert bench.traffic_for_current_kernel() is None
+    # an unreadable one
+    f.write_text("{not json")
+    assert bench.traffic_for_current_kernel() is None
+
+
+def test_committed_traffic_summary_is_well_formed():
+    with open(os.path.join(ROOT, "profiles", "seg_attn_fullcache_traffic.json")) as fh:
+        t = json.load(fh)
+    assert len(t["kernel_digest"]) == 16
+    assert t["hbm_bytes_per_launch"] > 0
