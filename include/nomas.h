@@ -126,10 +126,12 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
  *   then the cache pointers may be NULL).
  * sm_scale > 0 (1/sqrt(128) for the model).
  * out: device, [Ln][H][128] bf16.  lse: device [H][Ln] float32 or NULL.
- * n_split: 0 lets the library split each query tile's keys into 1..4
- *   contiguous parts so that the grid fills the GPU's last round of
- *   workgroups (partial results are merged by the log-sum-exp identity);
- *   1..NOMAS_MAX_SPLIT forces that many parts.  Results agree to rounding.
+ * n_split: 0 lets the library split query tiles' keys into contiguous
+ *   parts so that the grid fills the GPU's last round of workgroups: every
+ *   tile into 1..4 parts, or, with one new segment, only the tiles of the
+ *   last round into up to 8 (partial results are merged by the log-sum-exp
+ *   identity); 1..NOMAS_MAX_SPLIT forces that many parts for every tile.
+ *   Results agree to rounding.
  * workspace: device scratch of at least nomas_seg_attn_workspace(...)
  *   bytes (same segments, cache_len, H and n_split, on the current device),
  *   16-byte aligned, owned by the caller; the call overwrites it (the keys

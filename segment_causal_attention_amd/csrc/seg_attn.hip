@@ -232,7 +232,8 @@ struct AttnArgs {
     float* plse;                    //            partial log2-sum-exp [split][H][Ln]
     int32_t Ln, H, ntq, ntk;        // H: query heads; ntq: query tiles per head, ntk: key tiles per KV head
     int32_t grp;                    // query heads per key/value head (head h reads KV head h / grp)
-    int32_t nsplit;                 // key-range parts per query tile
+    int32_t nsplit;                 // key-range parts of a split query tile
+    int32_t nmain;                  // blocks [0, nmain): whole query tiles; the rest split into nsplit parts
     float scale_log2;               // sm_scale * log2(e)
     int32_t tile0[NOMAS_MAX_SEGS + 1];   // first query tile of each new segment
     int32_t order[NOMAS_MAX_SEGS];       // segments in launch order (most keys first)
@@ -413,14 +414,28 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
-    // block = (head * nsplit + split) * ntq + launch-order query tile: the
-    // workgroups that share a key range run side by side, and the segments
-    // with the most keys go first (packed calls: the last segment), so that
-    // the grid does not end on a few long workgroups
-    const int hs = __builtin_amdgcn_readfirstlane(blockIdx.x / A.ntq);
-    const int li = __builtin_amdgcn_readfirstlane(blockIdx.x - hs * A.ntq);
-    const int head = __builtin_amdgcn_readfirstlane(hs / A.nsplit);
-    const int split = __builtin_amdgcn_readfirstlane(hs - head * A.nsplit);
+    // Units u = head * ntq + launch-order query tile.  Blocks [0, nmain)
+    // are units 0 .. nmain-1 whole; the others are the remaining units split
+    // into nsplit key-range parts, part-major, so that the workgroups that
+    // share a key range run side by side.  The segments with the most keys
+    // go first (packed calls: the last segment), so that the grid does not
+    // end on a few long workgroups.
+    int unit, split, parts;
+    if ((int)blockIdx.x < A.nmain) {
+        unit = blockIdx.x;
+        split = 0;
+        parts = 1;
+    } else {
+        const int t = blockIdx.x - A.nmain, r = A.ntq * A.H - A.nmain;
+        split = t / r;
+        unit = A.nmain + (t - split * r);
+        parts = A.nsplit;
+    }
+    unit = __builtin_amdgcn_readfirstlane(unit);
+    split = __builtin_amdgcn_readfirstlane(split);
+    parts = __builtin_amdgcn_readfirstlane(parts);
+    const int head = __builtin_amdgcn_readfirstlane(unit / A.ntq);
+    const int li = __builtin_amdgcn_readfirstlane(unit - head * A.ntq);
 
     int oi = 0;
     while (oi + 1 < A.segs.n && A.lt0[oi + 1] <= li) ++oi;
@@ -475,8 +490,8 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const int64_t kbase = (int64_t)(head / A.grp) * A.ntk + A.ktile0[a];   // this segment's region of the images
     const int nt_all = (nkeys + BN - 1) / BN;
     // this workgroup's part of the key tiles: [t0, t0 + nt)
-    const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * nt_all / A.nsplit));
-    const int nt = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * nt_all / A.nsplit) - t0);
+    const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * nt_all / parts));
+    const int nt = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * nt_all / parts) - t0);
     const int krd = l32 * KSTR + 8 * g;             // this lane's K / V^T fragment offsets
     const int vrd = l32 * VSTR + 8 * g;
     {
@@ -607,7 +622,7 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const float lt = half_sum(ws.lsum);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int row = r0 + wave * QW + l32;
-    if (row < r1 && A.nsplit > 1) {
+    if (row < r1 && parts > 1) {
         // partial result of this key range: O/l in fp32 and log2-sum-exp
         float* dst = A.po + (((int64_t)split * A.Ln + row) * A.H + head) * D;
 #pragma unroll
@@ -633,19 +648,23 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
 
 // Merge of the key-range parts (log-sum-exp identity): for each (row, head)
 // lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) * (O/l)_s.
-// 32 threads per (row, head), 4 channels each.
+// 32 threads per (row, head), 4 channels each, over the pairs f = head * Ln
+// + row >= f0: the split query tiles are the last units in head-major order,
+// so their rows are a suffix of these pairs.
 struct MergeArgs {
     const float* po;
     const float* plse;
     uint16_t* out;
     float* lse;
+    int64_t f0;
     int32_t Ln, H, nsplit;
 };
 
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs M) {
-    const int64_t pair = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);   // row * H + head
-    if (pair >= (int64_t)M.Ln * M.H) return;
-    const int row = (int)(pair / M.H), head = (int)(pair - (int64_t)row * M.H);
+    const int64_t f = M.f0 + (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    if (f >= (int64_t)M.Ln * M.H) return;
+    const int head = (int)(f / M.Ln), row = (int)(f - (int64_t)head * M.Ln);
+    const int64_t pair = (int64_t)row * M.H + head;
     const int ch = 4 * (threadIdx.x & 31);
     float mx = -INFINITY;
     for (int s = 0; s < M.nsplit; ++s) mx = fmaxf(mx, M.plse[((int64_t)s * M.H + head) * M.Ln + row]);
@@ -754,13 +773,28 @@ int build_key_plan(const SegTable& segs, int Lc, int Ln, const int32_t* sel_off,
     return finish();
 }
 
-// Key-range parts per query tile.  Forced when n_split > 0; otherwise the
-// count (1..4) that fills the last round of workgroups best, keeping every
-// part at 16 tiles or more: one workgroup per CU, so a grid of u units takes
-// ceil(u / CUs) rounds, each 1/parts as long.
-int plan_splits(const SegTable& segs, const KeyPlan& kp, const int32_t* seg_reg, int H, int n_split) {
-    if (n_split > 0) return n_split;
-    int nq = 0, nt_min = 1 << 30;
+// How the query tiles are split into key-range parts: the first `main`
+// units (head-major, launch order) run whole, the others in `parts` parts.
+struct SplitPlan {
+    int parts;
+    int64_t main;
+};
+
+// Forced when n_split > 0: every unit in n_split parts.  Otherwise, with
+// one workgroup per CU, a grid of u equal units takes ceil(u / CUs) rounds
+// and its last round may run mostly empty.  Two remedies are priced, in
+// units of one workgroup's whole key range:
+//  - every unit in p = 2..4 parts: ceil(p u / CUs) / p rounds;
+//  - for one segment (units of equal work), only the r = u mod CUs units of
+//    the last round, in s = 2..8 parts: floor(u / CUs) + ceil(r s / CUs) / s.
+// Split units pay the merge pass, which moves s * 516 + 260 bytes per
+// (query, head) at HBM speed while the attention spends 512 FLOP per
+// (query, key, head) on MFMA (about 250 FLOP per byte apart, as measured),
+// and 2% per extra part for the parts' own prologues and fp32 partial
+// outputs.  Every part keeps 16 key tiles or more.
+SplitPlan plan_splits(const SegTable& segs, const KeyPlan& kp, const int32_t* seg_reg, int H, int n_split) {
+    if (n_split > 0) return {n_split, 0};
+    int nq = 0, nt_min = 1 << 30, nseg = 0;
     double keys = 0.0;              // sum over query tiles of their key count
     for (int i = 0; i < segs.n; ++i) {
         const SegDev& s = segs.s[i];
@@ -771,24 +805,28 @@ int plan_splits(const SegTable& segs, const KeyPlan& kp, const int32_t* seg_reg,
         nq += tiles;
         nt_min = std::min(nt_min, (nk + BN - 1) / BN);
         keys += (double)tiles * nk;
+        ++nseg;
     }
     const int cus = device_cu_count();
-    if (nq == 0 || cus <= 0) return 1;
+    if (nq == 0 || cus <= 0) return {1, 0};
     const int64_t units = (int64_t)nq * H;
-    // Cost in units of one workgroup's whole key range: the rounds of
-    // workgroups the grid takes, plus for p > 1 parts the merge pass, which
-    // moves p * 516 + 260 bytes per (query, head) at HBM speed while the
-    // attention spends 512 FLOP per (query, key, head) on MFMA (about 250
-    // FLOP per byte apart, as measured), and 2% per extra part for the
-    // parts' own prologues and fp32 partial outputs.
     const double keys_avg = keys / nq;
-    int best = 1;
+    auto overhead = [&](int p) { return (p * 516.0 + 260.0) * 250.0 / (512.0 * keys_avg) + 0.02 * (p - 1); };
+    SplitPlan best{1, 0};
     double best_cost = (double)((units + cus - 1) / cus);
     for (int p = 2; p <= 4 && nt_min / p >= 16; ++p) {
-        const double rounds = (double)((units * p + cus - 1) / cus) / p;
-        const double overhead = (p * 516.0 + 260.0) * 250.0 / (512.0 * keys_avg) + 0.02 * (p - 1);
-        const double cost = rounds * (1.0 + overhead);
-        if (cost < best_cost - 1e-9) { best = p; best_cost = cost; }
+        const double cost = (double)((units * p + cus - 1) / cus) / p * (1.0 + overhead(p));
+        if (cost < best_cost - 1e-9) { best = {p, 0}; best_cost = cost; }
+    }
+    const int64_t r = units % cus;
+    // one segment: its tiles all see the same keys, and the units past
+    // `main` are the last rows of the last heads (the merge relies on it)
+    if (segs.n == 1 && nseg == 1 && r > 0 && segs.s[0].start == 0) {
+        for (int p = 2; p <= 8 && nt_min / p >= 16; ++p) {
+            const double cost = (double)(units / cus) + (double)((r * p + cus - 1) / cus) / p +
+                                (double)r / cus * overhead(p);
+            if (cost < best_cost - 1e-9) { best = {p, units - r}; best_cost = cost; }
+        }
     }
     return best;
 }
@@ -804,7 +842,7 @@ int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, in
     int32_t seg_reg[NOMAS_MAX_SEGS];
     const int rc = build_key_plan(segs, Lc, Ln, sel_off, sel_ranges, &kp, seg_reg);
     if (rc != NOMAS_OK) return rc;
-    const int p = plan_splits(segs, kp, seg_reg, H, n_split);
+    const int p = plan_splits(segs, kp, seg_reg, H, n_split).parts;
     const int64_t tiles = (int64_t)Hkv * kp.tile0[kp.nreg];
     int64_t b = tiles * TILE_BYTES + knorm_bytes(tiles);
     if (p > 1) b += (int64_t)p * Ln * H * (D + 1) * 4;
@@ -820,7 +858,8 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     int32_t seg_reg[NOMAS_MAX_SEGS];
     const int rc = build_key_plan(segs, Lc, Ln, sel_off, sel_ranges, &P.kp, seg_reg);
     if (rc != NOMAS_OK) return rc;
-    const int nsplit = plan_splits(segs, P.kp, seg_reg, H, n_split);
+    const SplitPlan sp = plan_splits(segs, P.kp, seg_reg, H, n_split);
+    const int nsplit = sp.parts;
     const int ntk = P.kp.tile0[P.kp.nreg];
     P.kc = kc; P.vc = vc; P.ks = ks; P.vs = vs;
     P.k = k; P.v = v;
@@ -836,6 +875,7 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.Ln = Ln; A.H = H; A.ntk = ntk;
     A.grp = H / Hkv;
     A.nsplit = nsplit;
+    A.nmain = (int32_t)sp.main;
     if (nsplit > 1) {
         A.po = reinterpret_cast<float*>(P.img + (int64_t)Hkv * ntk * TILE_BYTES + knorm_bytes((int64_t)Hkv * ntk));
         A.plse = A.po + (int64_t)nsplit * Ln * H * D;
@@ -872,11 +912,15 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.rt = rt;
     if (nt == 0) return NOMAS_OK;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)ntk, (unsigned)Hkv), dim3(PACK_NT), 0, stream, P);
-    const int64_t blocks = (int64_t)nt * H * nsplit;
+    const int64_t units = (int64_t)nt * H;
+    const int64_t blocks = sp.main + (units - sp.main) * nsplit;
     hipLaunchKernelGGL(seg_attn_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, A);
     if (nsplit > 1) {
-        const MergeArgs M{A.po, A.plse, out, lse, Ln, H, nsplit};
-        const int64_t mb = ((int64_t)Ln * H + 7) / 8;
+        // rows of the split units: from query tile main % nt of head main / nt
+        // on (one segment, starting at row 0), or every row
+        const int64_t f0 = sp.main > 0 ? sp.main / nt * Ln + sp.main % nt * BM : 0;
+        const MergeArgs M{A.po, A.plse, out, lse, f0, Ln, H, nsplit};
+        const int64_t mb = ((int64_t)Ln * H - f0 + 7) / 8;
         hipLaunchKernelGGL(merge_kernel, dim3((unsigned)mb), dim3(256), 0, stream, M);
     }
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
