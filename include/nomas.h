@@ -192,7 +192,8 @@ int64_t nomas_seg_attn_sel_workspace(const nomas_seg* new_segs, int n_new_segs, 
  * Workspace bytes nomas_seg_attn needs for these new segments, cache length,
  * head count and n_split on the current device: with T = H * ceil((cache_len
  * + Ln) / 64) tiles, T * 35840 + (4T rounded up to a multiple of 256), plus
- * parts * Ln * H * 516 when the keys are split into parts > 1; or a negative
+ * parts * 516 per (query, head) of the split query tiles when keys are
+ * split into parts > 1 (all Ln * H pairs when every tile is split); or a negative
  * error code (NOMAS_EINVAL / NOMAS_EUNSUPPORTED as for nomas_seg_attn).
  * Host only.
  */

@@ -228,8 +228,9 @@ struct AttnArgs {
     const float* knorm;             // [H][ntk] largest squared key norm per tile
     uint16_t* out;
     float* lse;
-    float* po;                      // split > 1: partial outputs O/l [split][Ln][H][128] fp32
-    float* plse;                    //            partial log2-sum-exp [split][H][Ln]
+    float* po;                      // split tiles: partial outputs O/l [split][nf][128] fp32 and
+    float* plse;                    //   partial log2-sum-exp [split][nf], for the (head, row)
+    int64_t f0, nf;                 //   pairs f = head * Ln + row in [f0, f0 + nf)
     int32_t Ln, H, ntq, ntk;        // H: query heads; ntq: query tiles per head, ntk: key tiles per KV head
     int32_t grp;                    // query heads per key/value head (head h reads KV head h / grp)
     int32_t nsplit;                 // key-range parts of a split query tile
@@ -624,7 +625,8 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     const int row = r0 + wave * QW + l32;
     if (row < r1 && parts > 1) {
         // partial result of this key range: O/l in fp32 and log2-sum-exp
-        float* dst = A.po + (((int64_t)split * A.Ln + row) * A.H + head) * D;
+        const int64_t f = (int64_t)head * A.Ln + row - A.f0;
+        float* dst = A.po + ((int64_t)split * A.nf + f) * D;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
                 *reinterpret_cast<float4*>(dst + 32 * db + 8 * i + 4 * g) =
                     make_float4(ws.o[db][4 * i] * inv, ws.o[db][4 * i + 1] * inv, ws.o[db][4 * i + 2] * inv,
                                 ws.o[db][4 * i + 3] * inv);
-        if (g == 0) A.plse[((int64_t)split * A.H + head) * A.Ln + row] = lt > 0.0f ? ws.m + __log2f(lt) : -INFINITY;
+        if (g == 0) A.plse[(int64_t)split * A.nf + f] = lt > 0.0f ? ws.m + __log2f(lt) : -INFINITY;
     } else if (row < r1) {
         uint16_t* dst = A.out + ((int64_t)row * A.H + head) * D;
 #pragma unroll
@@ -667,13 +669,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs M) {
     const int64_t pair = (int64_t)row * M.H + head;
     const int ch = 4 * (threadIdx.x & 31);
     float mx = -INFINITY;
-    for (int s = 0; s < M.nsplit; ++s) mx = fmaxf(mx, M.plse[((int64_t)s * M.H + head) * M.Ln + row]);
+    const int64_t nf = (int64_t)M.Ln * M.H - M.f0, fl = f - M.f0;
+    for (int s = 0; s < M.nsplit; ++s) mx = fmaxf(mx, M.plse[(int64_t)s * nf + fl]);
     float wsum = 0.0f;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int s = 0; s < M.nsplit; ++s) {
-        const float ls = M.plse[((int64_t)s * M.H + head) * M.Ln + row];
+        const float ls = M.plse[(int64_t)s * nf + fl];
         const float w = ls == -INFINITY ? 0.0f : exp2f(ls - mx);
-        const float4 o = *reinterpret_cast<const float4*>(M.po + ((int64_t)s * M.Ln + row) * M.H * D + head * D + ch);
+        const float4 o = *reinterpret_cast<const float4*>(M.po + ((int64_t)s * nf + fl) * D + ch);
         wsum += w;
         acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
     }
@@ -780,6 +783,22 @@ struct SplitPlan {
     int64_t main;
 };
 
+// First (head, row) pair f = head * Ln + row of the split units: with
+// main > 0 there is one segment (starting at row 0) and the split units are
+// its last query tiles in head-major order, so their rows are the suffix
+// from query tile main % ntq of head main / ntq on.
+static int64_t split_f0(const SplitPlan& sp, int ntq, int Ln) {
+    return sp.main > 0 ? sp.main / ntq * Ln + sp.main % ntq * BM : 0;
+}
+static int query_tiles(const SegTable& segs) {
+    int nt = 0;
+    for (int i = 0; i < segs.n; ++i) {
+        const SegDev& s = segs.s[i];
+        nt += (s.n_text + s.T * s.Hg * s.Wg + BM - 1) / BM;
+    }
+    return nt;
+}
+
 // Forced when n_split > 0: every unit in n_split parts.  Otherwise, with
 // one workgroup per CU, a grid of u equal units takes ceil(u / CUs) rounds
 // and its last round may run mostly empty.  Two remedies are priced, in
@@ -842,10 +861,10 @@ int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, in
     int32_t seg_reg[NOMAS_MAX_SEGS];
     const int rc = build_key_plan(segs, Lc, Ln, sel_off, sel_ranges, &kp, seg_reg);
     if (rc != NOMAS_OK) return rc;
-    const int p = plan_splits(segs, kp, seg_reg, H, n_split).parts;
+    const SplitPlan sp = plan_splits(segs, kp, seg_reg, H, n_split);
     const int64_t tiles = (int64_t)Hkv * kp.tile0[kp.nreg];
     int64_t b = tiles * TILE_BYTES + knorm_bytes(tiles);
-    if (p > 1) b += (int64_t)p * Ln * H * (D + 1) * 4;
+    if (sp.parts > 1) b += (int64_t)sp.parts * ((int64_t)Ln * H - split_f0(sp, query_tiles(segs), Ln)) * (D + 1) * 4;
     return b;
 }
 
@@ -876,9 +895,11 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.grp = H / Hkv;
     A.nsplit = nsplit;
     A.nmain = (int32_t)sp.main;
+    A.f0 = split_f0(sp, query_tiles(segs), Ln);
+    A.nf = (int64_t)Ln * H - A.f0;
     if (nsplit > 1) {
         A.po = reinterpret_cast<float*>(P.img + (int64_t)Hkv * ntk * TILE_BYTES + knorm_bytes((int64_t)Hkv * ntk));
-        A.plse = A.po + (int64_t)nsplit * Ln * H * D;
+        A.plse = A.po + (int64_t)nsplit * A.nf * D;
     }
     A.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
     int nt = 0;
@@ -916,11 +937,8 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     const int64_t blocks = sp.main + (units - sp.main) * nsplit;
     hipLaunchKernelGGL(seg_attn_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, A);
     if (nsplit > 1) {
-        // rows of the split units: from query tile main % nt of head main / nt
-        // on (one segment, starting at row 0), or every row
-        const int64_t f0 = sp.main > 0 ? sp.main / nt * Ln + sp.main % nt * BM : 0;
-        const MergeArgs M{A.po, A.plse, out, lse, f0, Ln, H, nsplit};
-        const int64_t mb = ((int64_t)Ln * H - f0 + 7) / 8;
+        const MergeArgs M{A.po, A.plse, out, lse, A.f0, Ln, H, nsplit};
+        const int64_t mb = (A.nf + 7) / 8;
         hipLaunchKernelGGL(merge_kernel, dim3((unsigned)mb), dim3(256), 0, stream, M);
     }
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;

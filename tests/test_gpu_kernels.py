@@ -181,6 +181,29 @@ def test_seg_attn_split_keys(name, n_split):
     np.testing.assert_allclose(lsen, lse1, rtol=0, atol=2.0 ** -8)
 
 
+def test_seg_attn_last_round_split():
+    """One segment whose query tiles leave the last round of workgroups
+    nearly empty on a 256-CU device: 17 tiles x 16 heads = 272 units, 16 in
+    the last round.  The library then splits only those 16 (head 15, tiles
+    1..16) into key-range parts; the workspace holds the partial buffers.
+    Rows of whole and split tiles against the oracle, with the library's
+    plan and with one part forced."""
+    segs, Lc, H = [(4352, 0, 0, 0, 0)], 8192, 16
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    plain = nomas.seg_attn_workspace(segs, Lc, H, n_split=1)
+    auto = nomas.seg_attn_workspace(segs, Lc, H, n_split=0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say("last-round split: CUs", cus, "workspace", plain, "->", auto)
+    if cus == 256:
+        assert auto > plain
+    rows = np.array([0, 1, 255, 256, 257, 2047, 2048, 4095, 4096, 4350, 4351])
+    ref, lref = oracle.seg_attn(q, k, v, segs, *cache, Lc, SM, rows=rows)
+    for n_split in (0, 1):
+        got, lse, _ = _run_gpu(q, k, v, segs, cache, Lc, H, n_split=n_split)
+        assert_close(got[rows], ref, "last-round split n_split=%d" % n_split)
+        np.testing.assert_allclose(lse[:, rows], lref, rtol=0, atol=2.0 ** -8)
+
+
 @pytest.mark.parametrize("name,segs,Lc,H", EDGE, ids=[c[0] for c in EDGE])
 def test_seg_attn_edge_shapes(name, segs, Lc, H):
     Ln = sum(s[0] + s[2] * s[3] * s[4] for s in segs)
