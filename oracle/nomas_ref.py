@@ -448,20 +448,37 @@ def w8a16_linear(x_bits, w_codes, w_scale, rows=None):
 #                       and injected by cross-attention in the dual-stream blocks)
 
 
+HALF_TURN_SKEW = 1e-12
+
+
 def _log_rotation(R):
-    """Axis (unit) and angle in [0, pi] of a rotation matrix."""
+    """Axis (unit) and angle in [0, pi] of a rotation matrix.
+
+    For R = exp(ang [a]x) = cos(ang) I + sin(ang) [a]x + (1 - cos(ang)) a a^T
+    the skew part is v = sin(ang) a and the symmetric part minus cos(ang) I
+    is (1 - cos(ang)) a a^T.  Up to a right angle the axis is v / |v|.  Past
+    it, sin(ang) shrinks towards zero at pi, so the axis magnitudes come from
+    the symmetric part (accurate there, 1 - cos(ang) >= 1) and only the sign
+    from v, whose largest-axis component keeps its sign until v vanishes.
+    At a half turn a and -a give the same rotation (but not once the angle is
+    scaled), and v is zero up to rounding; where that component of v is no
+    larger than HALF_TURN_SKEW (1e-12, far above the rounding of products of
+    orthonormal double matrices) the axis is taken with its largest component
+    positive."""
+    R = np.asarray(R, dtype=np.float64)
     v = 0.5 * np.array([R[2, 1] - R[1, 2], R[0, 2] - R[2, 0], R[1, 0] - R[0, 1]])
-    s = np.linalg.norm(v)
-    c = 0.5 * (np.trace(R) - 1.0)
+    s = float(np.linalg.norm(v))
+    c = 0.5 * (float(np.trace(R)) - 1.0)
     ang = math.atan2(s, c)
-    if s > 1e-6:
+    if c >= 0.0:
+        if s == 0.0:                # the identity: angle 0, any axis
+            return np.array([1.0, 0.0, 0.0]), 0.0
         return v / s, ang
-    if c > 0:                       # angle ~ 0: any axis
-        return np.array([1.0, 0.0, 0.0]), ang
-    # angle ~ pi: axis from the symmetric part, R = 2 a a^T - I
-    B = 0.5 * (R + np.eye(3))
-    j = int(np.argmax(np.diag(B)))
-    a = B[:, j] / math.sqrt(max(B[j, j], 1e-300))
+    A = (0.5 * (R + R.T) - c * np.eye(3)) / (1.0 - c)      # = a a^T
+    j = int(np.argmax(np.diag(A)))
+    a = A[:, j] / math.sqrt(A[j, j])                        # component j positive
+    if v[j] < -HALF_TURN_SKEW:
+        a = -a
     return a / np.linalg.norm(a), ang
 
 

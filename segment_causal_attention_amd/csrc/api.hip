@@ -81,28 +81,44 @@ void mat3_mul(const double A[9], const double B[9], double C[9]) {
         for (int j = 0; j < 3; ++j) C[3 * i + j] = A[3 * i] * B[j] + A[3 * i + 1] * B[3 + j] + A[3 * i + 2] * B[6 + j];
 }
 
-// axis (unit) and angle in [0, pi] of a rotation matrix
+// Axis (unit) and angle in [0, pi] of a rotation matrix R = exp(ang [a]x).
+// The skew part of R is sin(ang) a; its symmetric part minus cos(ang) I is
+// (1 - cos(ang)) a a^T.  Up to a right angle the axis is the normalised skew
+// part.  Beyond it the skew part shrinks towards zero at pi, so the axis is
+// read from the symmetric part (column of its largest diagonal entry) and
+// only its sign from the skew part.  At a half turn +a and -a are the same
+// rotation and the skew part is zero up to rounding: where its component
+// along the chosen column is no larger than 1e-12 (far above the rounding of
+// products of orthonormal double matrices) the largest axis component is
+// taken positive.
 void rot_log(const double R[9], double axis[3], double* ang) {
-    double v[3] = {0.5 * (R[7] - R[5]), 0.5 * (R[2] - R[6]), 0.5 * (R[3] - R[1])};
-    double s = std::sqrt(v[0] * v[0] + v[1] * v[1] + v[2] * v[2]);
-    double c = 0.5 * (R[0] + R[4] + R[8] - 1.0);
+    const double v[3] = {0.5 * (R[7] - R[5]), 0.5 * (R[2] - R[6]), 0.5 * (R[3] - R[1])};
+    const double s = std::sqrt(v[0] * v[0] + v[1] * v[1] + v[2] * v[2]);
+    const double c = 0.5 * (R[0] + R[4] + R[8] - 1.0);
     *ang = std::atan2(s, c);
-    if (s > 1e-6) {
-        for (int i = 0; i < 3; ++i) axis[i] = v[i] / s;
-    } else if (c > 0) {
-        axis[0] = 1.0; axis[1] = 0.0; axis[2] = 0.0;
-    } else {
-        // angle near pi: R = 2 a a^T - I, take the largest column of (R + I)/2
-        double B[9];
-        for (int i = 0; i < 9; ++i) B[i] = 0.5 * (R[i] + ((i % 4) == 0 ? 1.0 : 0.0));
-        int j = 0;
-        if (B[4] > B[0]) j = 1;
-        if (B[8] > B[4 * j]) j = 2;
-        double d = std::sqrt(B[4 * j] > 1e-300 ? B[4 * j] : 1e-300);
-        double a[3] = {B[j] / d, B[3 + j] / d, B[6 + j] / d};
-        double n = std::sqrt(a[0] * a[0] + a[1] * a[1] + a[2] * a[2]);
-        for (int i = 0; i < 3; ++i) axis[i] = a[i] / n;
+    if (c >= 0.0) {
+        if (s == 0.0) {
+            axis[0] = 1.0; axis[1] = 0.0; axis[2] = 0.0;
+            *ang = 0.0;
+        } else {
+            for (int i = 0; i < 3; ++i) axis[i] = v[i] / s;
+        }
+        return;
     }
+    // A = (sym(R) - c I) / (1 - c) = a a^T
+    double A[9];
+    for (int r = 0; r < 3; ++r)
+        for (int k = 0; k < 3; ++k)
+            A[3 * r + k] = (0.5 * (R[3 * r + k] + R[3 * k + r]) - (r == k ? c : 0.0)) / (1.0 - c);
+    int j = 0;
+    if (A[4] > A[0]) j = 1;
+    if (A[8] > A[4 * j]) j = 2;
+    const double d = std::sqrt(A[4 * j]);           // >= 1/sqrt(3) for a unit axis
+    double a[3] = {A[j] / d, A[3 + j] / d, A[6 + j] / d};
+    if (v[j] < -1e-12)
+        for (int i = 0; i < 3; ++i) a[i] = -a[i];
+    const double n = std::sqrt(a[0] * a[0] + a[1] * a[1] + a[2] * a[2]);
+    for (int i = 0; i < 3; ++i) axis[i] = a[i] / n;
 }
 
 void rot_exp(const double axis[3], double ang, double R[9]) {

@@ -150,6 +150,18 @@ def test_cam_tokens_match_oracle():
         nomas.cam_tokens(c2w[:6])
 
 
+def test_cam_tokens_near_pi():
+    """The library's host normalisation keeps the axis of rotations just short
+    of a half turn and uses the positive-largest-component axis at exactly pi,
+    as the oracle does (comfyui-wiki news page, 相机控制作为一等输入:
+    rotation scale 2.5); expected values are scipy matrix exponentials."""
+    from test_oracle_cam import near_pi_cases
+    for path, want, case in near_pi_cases():
+        got = nomas.cam_tokens(path).reshape(4, 4, 4)
+        np.testing.assert_allclose(got[1, :3, :3], want, rtol=0, atol=2e-6, err_msg=str(case))
+        np.testing.assert_allclose(got, oracle.cam_tokens(path).reshape(4, 4, 4), rtol=0, atol=2e-6)
+
+
 def test_seg_attn_sel_host_checks():
     """History selection: workspace sizes of shared and per-segment key
     regions, and the errors of an invalid selection (host only)."""

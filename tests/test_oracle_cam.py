@@ -83,3 +83,65 @@ def test_matches_brute_force():
     cam1[:, 0] = 1.0
     out1 = oracle.cam_xattn(q, cam1, wk, wv1, sm)
     np.testing.assert_allclose(out1, 0.75, rtol=0, atol=1e-15)
+
+
+def _skew(a):
+    x, y, z = a
+    return np.array([[0, -z, y], [z, 0, -x], [-y, x, 0.0]])
+
+
+NEAR_PI_AXES = [np.array([0.3, -0.8, 0.5]), np.array([-0.6, 0.0, 0.8]), np.array([0.0, 0.0, -1.0]),
+                np.array([0.2, 0.9, -0.1])]
+
+
+def near_pi_cases():
+    """(c2w path of 4 frames, expected relative rotation of frame 1 after the
+    x2.5 angle scale) for rotations of pi - 1e-3, pi - 1e-7 and exactly pi.
+    Expected values are matrix exponentials of the scaled skew matrix (scipy),
+    not the oracle's own exp; at exactly pi the axis is the one whose largest
+    component is positive (the sign convention for a half turn)."""
+    import scipy.linalg as sl
+
+    out = []
+    R0 = rotz(0.4)
+    for a in NEAR_PI_AXES:
+        a = a / np.linalg.norm(a)
+        for sgn in (1.0, -1.0):
+            ax = sgn * a
+            for eps in (1e-3, 1e-7, 0.0):
+                if eps == 0.0:
+                    Rrel = 2.0 * np.outer(ax, ax) - np.eye(3)          # exactly a half turn
+                    conv = ax if ax[np.argmax(np.abs(ax))] > 0 else -ax
+                    want = sl.expm(2.5 * math.pi * _skew(conv))
+                else:
+                    Rrel = sl.expm((math.pi - eps) * _skew(ax))
+                    want = sl.expm(2.5 * (math.pi - eps) * _skew(ax))
+                path = make_path([R0, R0 @ Rrel, R0, R0], [np.zeros(3)] * 4)
+                out.append((path, want, (tuple(ax), eps)))
+    return out
+
+
+def test_rotation_near_pi_keeps_its_axis():
+    """A relative rotation just short of a half turn keeps its axis sign, so
+    the x2.5 scaled rotation is R(a, 2.5 theta) (comfyui-wiki news page,
+    相机控制作为一等输入: rotation scale 2.5) all the way to pi; exactly at pi
+    the axis with a positive largest component is used."""
+    for path, want, case in near_pi_cases():
+        tok = oracle.cam_tokens(path).reshape(4, 4, 4)
+        np.testing.assert_allclose(tok[1, :3, :3], want, atol=1e-12, err_msg=str(case))
+        np.testing.assert_allclose(tok[0, :3, :3], np.eye(3), atol=1e-14)
+
+
+def test_rotation_scale_continuous_up_to_pi():
+    """Tokens of rotations pi - eps about a fixed axis converge to the
+    half-turn token R(a, 2.5 pi) as eps -> 0, down to eps = 1e-10 (no jump
+    where sin(theta) gets small; the sign convention of a half turn applies
+    only within 1e-12 of pi, where rounding decides the sign)."""
+    a = np.array([0.3, -0.8, 0.5])
+    a /= np.linalg.norm(a)
+    import scipy.linalg as sl
+    for eps in (1e-2, 1e-4, 1e-6, 1e-8, 1e-10):
+        path = make_path([np.eye(3), sl.expm((math.pi - eps) * _skew(a))] + [np.eye(3)] * 2, [np.zeros(3)] * 4)
+        tok = oracle.cam_tokens(path).reshape(4, 4, 4)[1, :3, :3]
+        lim = sl.expm(2.5 * math.pi * _skew(a))
+        assert np.abs(tok - lim).max() <= 2.5 * eps * 1.01 + 1e-12, eps
