@@ -319,7 +319,7 @@ def seg_attn(q_bits, k_new_bits, v_new_bits, new_segs, k_codes, v_codes, k_scale
 
 
 def seg_attn_bwd(q_bits, k_bits, v_bits, do_bits, segs, sm_scale, rows=None, heads=None,
-                 bf16_operands=True, want_kv=True, block=None):
+                 bf16_operands=True, want_kv=True, block=None, keys=None):
     """Gradients of packed segment-causal attention (training direction).
 
     The packed training sequence of the segment-forcing LoRA recipe
@@ -339,6 +339,13 @@ def seg_attn_bwd(q_bits, k_bits, v_bits, do_bits, segs, sm_scale, rows=None, hea
     q, k, v, dO: [Ln][H][128], bf16 bits (uint16) or float64 values; q and k
     before RoPE.  Returns (dq, dk, dv): dq [len(rows)][len(heads)][128] and,
     with want_kv, dk and dv [Ln][len(heads)][128] (else None), float64.
+
+    keys (key-subset mode, for long sequences): token indices whose dk and dv
+    are wanted.  The gradient of key j sums over the queries that see it
+    (segments at or after j's), and each of those needs its whole softmax row
+    (P over all its keys, O for D), so those rows are formed in full; only
+    the columns of the chosen keys are kept for dP, dS, dk and dv.  Returns
+    (None, dk, dv) with dk, dv [len(keys)][len(heads)][128]; dq is not formed.
     """
     q = np.asarray(q_bits)
     Ln, H, _ = q.shape
@@ -349,12 +356,20 @@ def seg_attn_bwd(q_bits, k_bits, v_bits, do_bits, segs, sm_scale, rows=None, hea
     pos = token_positions(segs)
     rnd = bf16_round if bf16_operands else (lambda a: a)
     sc = float(sm_scale)
-    # query rows whose softmax rows are needed: all of them for dk and dv
-    need = np.arange(Ln) if want_kv else rows
+    if keys is not None:
+        kidx = np.asarray(keys, dtype=np.int64)
+        assert len(kidx) and kidx.min() >= 0 and kidx.max() < Ln, "keys outside the sequence"
+        want_kv = True
+        first = int(np.searchsorted(ends, kidx.min(), side="right"))
+        need = np.arange(0 if first == 0 else int(ends[first - 1]), Ln)   # queries that see a chosen key
+    else:
+        kidx = np.arange(Ln)
+        # query rows whose softmax rows are needed: all of them for dk and dv
+        need = np.arange(Ln) if want_kv else rows
     seg_of = np.searchsorted(ends, need, side="right")
-    dq_r = np.zeros((Ln, len(heads), D))
-    dk_r = np.zeros((Ln, len(heads), D)) if want_kv else None
-    dv = np.zeros((Ln, len(heads), D)) if want_kv else None
+    dq_r = np.zeros((Ln, len(heads), D)) if keys is None else None
+    dk_r = np.zeros((len(kidx), len(heads), D)) if want_kv else None
+    dv = np.zeros((len(kidx), len(heads), D)) if want_kv else None
     for hi, h in enumerate(heads):
         Qr = rnd(rope3d_pos(values(q[:, h:h + 1, :]), *pos))[:, 0, :]
         Kr = rnd(rope3d_pos(values(np.asarray(k_bits)[:, h:h + 1, :]), *pos))[:, 0, :]
@@ -364,6 +379,8 @@ def seg_attn_bwd(q_bits, k_bits, v_bits, do_bits, segs, sm_scale, rows=None, hea
             mine = need[seg_of == a]
             e = int(ends[a])
             K, Va = Kr[:e], V[:e]
+            vis = np.nonzero(kidx < e)[0]         # chosen keys this segment's queries see
+            cols = kidx[vis] if keys is not None else slice(None)
             blk = block or int(max(8, min(256, (1 << 23) // max(1, e))))
             for lo in range(0, len(mine), blk):
                 r = mine[lo:lo + blk]
@@ -371,18 +388,19 @@ def seg_attn_bwd(q_bits, k_bits, v_bits, do_bits, segs, sm_scale, rows=None, hea
                 E = np.exp(S - S.max(axis=1, keepdims=True))
                 P = E / E.sum(axis=1, keepdims=True)
                 O = P @ Va
-                dP = dO[r] @ Va.T
                 Dr = np.sum(dO[r] * O, axis=1)
-                dS = P * (dP - Dr[:, None])
-                dq_r[r, hi] = sc * (dS @ K)
+                dP = dO[r] @ Va[cols].T
+                dS = P[:, cols] * (dP - Dr[:, None])
+                if keys is None:
+                    dq_r[r, hi] = sc * (dS @ K)
                 if want_kv:
-                    dk_r[:e, hi] += sc * (dS.T @ Qr[r])
-                    dv[:e, hi] += P.T @ dO[r]
+                    dk_r[vis, hi] += sc * (dS.T @ Qr[r])
+                    dv[vis, hi] += P[:, cols].T @ dO[r]
         del Qr, Kr, V, dO
-    dq = rope3d_pos(dq_r[rows], *(p[rows] for p in pos), inverse=True)
+    dq = None if keys is not None else rope3d_pos(dq_r[rows], *(p[rows] for p in pos), inverse=True)
     if not want_kv:
         return dq, None, None
-    dk = rope3d_pos(dk_r, *pos, inverse=True)
+    dk = rope3d_pos(dk_r, *(p[kidx] for p in pos), inverse=True)
     return dq, dk, dv
 
 

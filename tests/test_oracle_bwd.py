@@ -194,3 +194,22 @@ def test_rows_subset_matches_full():
     dqs, dks, dvs = oracle.seg_attn_bwd(q, k, v, dO, segs, SM, rows=rows, want_kv=False)
     assert dks is None and dvs is None
     np.testing.assert_allclose(dqs, dq[rows], rtol=0, atol=1e-13)
+
+
+def test_key_subset_matches_full():
+    """The key-subset mode (dk, dv of chosen keys only, for sequences too long
+    for the full gradient) equals the full gradients at those keys: keys of
+    every segment, segment boundaries and a text-only segment."""
+    segs = [(5, 0, 2, 3, 4), (0, 2, 1, 5, 3), (7, 0, 0, 1, 1), (2, 3, 1, 4, 4)]
+    L = sum(s[0] + s[2] * s[3] * s[4] for s in segs)
+    H = 2
+    q, k, v, d = (synth.random_bf16(1300 + i, (L, H, 128)) for i in range(4))
+    sm = 1 / math.sqrt(128)
+    _, dk, dv = oracle.seg_attn_bwd(q, k, v, d, segs, sm)
+    ends = np.cumsum([s[0] + s[2] * s[3] * s[4] for s in segs])
+    for keys in ([0, 1, 28], [29, 43, 44, 50, 51, L - 1], [L - 1], list(range(L))):
+        dq_s, dk_s, dv_s = oracle.seg_attn_bwd(q, k, v, d, segs, sm, keys=keys)
+        assert dq_s is None and dk_s.shape == (len(keys), H, 128)
+        np.testing.assert_allclose(dk_s, dk[keys], rtol=0, atol=1e-13 * np.abs(dk).max())
+        np.testing.assert_allclose(dv_s, dv[keys], rtol=0, atol=1e-13 * np.abs(dv).max())
+    assert ends[-1] == L
