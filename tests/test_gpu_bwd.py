@@ -132,7 +132,8 @@ def test_bwd_training_sequence_full_size():
     354,112 tokens, one GPU's 2 heads of a head-sharded layer): dq on rows
     sampled in every segment against the oracle row by row, and identities
     of softmax attention that hold at any size for dk and dv:
-    sum_k dv_k = sum_q dO_q and sum_k R dk_k = 0."""
+    sum_k dv_k = sum_q dO_q and sum_k R dk_k = 0, and dk, dv element by
+    element on sampled keys of the last segment."""
     segs = [s.astuple() for s in synth.train_segs()]
     H = 2
     inp = synth.train_inputs(synth.train_segs(), H)
@@ -159,3 +160,43 @@ def test_bwd_training_sequence_full_size():
     s, a = np.abs(dkr.sum(axis=0)), np.abs(dkr).sum(axis=0)
     say("full sum dKr: max |sum| / sum |.| = %.3e" % (s / a).max())
     assert np.all(s <= 1e-3 * a)
+    # dk and dv element by element on keys of the last segment (the oracle
+    # forms the whole softmax rows of the 16,096 queries that see them)
+    keys = np.unique(np.concatenate([[starts[-1], starts[-1] + 63, starts[-1] + 64, starts[-1] + 255,
+                                      starts[-1] + 256, ends[-1] - 1], rng.integers(starts[-1], L, 26)]))
+    _key_grads("full", q, k, v, d_out, segs, H, keys, dk, dv)
+
+
+def _key_grads(name, q, k, v, d_out, segs, H, keys, dk, dv):
+    """dk, dv of the GPU at `keys` against the oracle's key-subset mode, one
+    head per thread (the heads are independent)."""
+    from concurrent.futures import ThreadPoolExecutor
+    say("%s: oracle dk, dv on %d keys x %d heads" % (name, len(keys), H))
+    one = lambda h: oracle.seg_attn_bwd(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], d_out[:, h:h + 1], segs,
+                                        SM, keys=keys)
+    with ThreadPoolExecutor(H) as ex:
+        res = list(ex.map(one, range(H)))
+    rdk = np.concatenate([r[1] for r in res], axis=1)
+    rdv = np.concatenate([r[2] for r in res], axis=1)
+    _close(dk[keys], rdk, "%s dk (%d keys)" % (name, len(keys)))
+    _close(dv[keys], rdv, "%s dv (%d keys)" % (name, len(keys)))
+
+
+def test_bwd_six_turns_first_segment_keys():
+    """Six packed turns of 1 s (6 latent frames + 256 text tokens: 5,536
+    tokens each, 33,216 in all, 2 heads): dk and dv of keys in the first
+    segment, which every later query tile of the sequence sees (the longest
+    walk of the dK/dV kernel), element by element."""
+    tsegs = synth.train_segs(6, T=6)
+    segs = [s.astuple() for s in tsegs]
+    H = 2
+    inp = synth.train_inputs(tsegs, H, inst=1)
+    q, k, v, d_out = inp["q"], inp["k"], inp["v"], inp["d_out"]
+    L = q.shape[0]
+    say("seg_attn_bwd six turns L", L, "H", H)
+    dq, dk, dv = _grads_gpu(q, k, v, d_out, segs, H)
+    assert all(np.all(np.isfinite(g)) for g in (dq, dk, dv))
+    n0 = segs[0][0] + segs[0][2] * segs[0][3] * segs[0][4]
+    rng = np.random.Generator(np.random.PCG64(6))
+    keys = np.unique(np.concatenate([[0, 1, 255, 256, segs[0][0], n0 - 64, n0 - 1], rng.integers(0, n0, 25)]))
+    _key_grads("six turns", q, k, v, d_out, segs, H, keys, dk, dv)

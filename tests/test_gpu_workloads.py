@@ -10,6 +10,8 @@ are independent.
   five turns   cache grown turn by turn to 253,440 tokens, camera cross-attention
   decoder      one 10-latent-frame window: 35,200 tokens, 32 query / 8 KV heads
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -102,26 +104,77 @@ def check_cache_rows(name, cache, start, k_rot_d, k_bits, v_bits, segs, heads):
         assert np.array_equal(vs[h, start:start + L].cpu().numpy().view(np.uint32), vscale.view(np.uint32))
 
 
+def rows_per_tile(Lq, per_tile, seed, tile=256, extra=()):
+    """`per_tile` seeded rows from every `tile`-row query tile (all rows of a
+    shorter last tile), plus `extra`."""
+    rng = np.random.default_rng(seed)
+    rows = set(int(r) for r in extra if 0 <= r < Lq)
+    for t0 in range(0, Lq, tile):
+        n = min(tile, Lq - t0)
+        rows.update(int(t0 + r) for r in rng.choice(n, size=min(per_tile, n), replace=False))
+    return np.array(sorted(rows))
+
+
+def split_plan_rows(segs, Lc, H, Lq, cus):
+    """Query rows of the last head whose tiles the library splits into key-range
+    parts at this shape (one segment, the last-round units of the grid), and
+    the part count, read back from the workspace sizes: the split adds
+    parts x 516 bytes per (query, head) of the split tiles."""
+    ntq = (Lq + 255) // 256
+    units = ntq * H
+    r = units % cus
+    extra = nomas.seg_attn_workspace(segs, Lc, H, 0) - nomas.seg_attn_workspace(segs, Lc, H, 1)
+    f0 = (units - r) // ntq * Lq + (units - r) % ntq * 256
+    pairs = Lq * H - f0
+    assert r > 0 and extra % (516 * pairs) == 0, (r, extra, pairs)
+    return extra // (516 * pairs), f0
+
+
 def test_full_cache_workload():
     """12 s segment over 288 cached latent frames (~317K keys), cache built on
-    the GPU exactly as the benchmark builds it."""
+    the GPU exactly as the benchmark builds it.  All 16 heads are compared on
+    a seeded subset of 16 rows from every 256-row query tile (4,000 rows),
+    which includes every query tile whose keys the launch plan splits into
+    parts merged by the log-sum-exp identity."""
     inp = synth.layer_inputs("fullcache")
     cfg = inp["cfg"]
     H, Lq, Lc = cfg.H, cfg.Lq, cfg.Lc
-    heads = [0, 9]
     say("config", cfg.name, "Lq", Lq, "Lc", Lc)
+    # the launch plan at this shape: with 256 CUs, 3,968 query-tile units leave
+    # 128 for a last round; those (head 15, query tiles 120..247) run in 2 key parts
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    parts, f0 = split_plan_rows(cfg.new_segs, Lc, H, Lq, cus)
+    say("launch plan: %d CUs, last-round tiles in %d key parts from (head, row) %d" % (cus, parts, f0))
+    if cus == 256:
+        assert parts == 2 and f0 == 15 * Lq + 120 * 256
     cache = cache_tensors(H, Lc + Lq)
     k_rot, n = gpu_append(dev16(inp["k_hist"]), dev16(inp["v_hist"]), cfg.hist_segs, cache, 0)
     assert n == Lc
-    check_cache_rows("full-cache history", cache, 0, k_rot, inp["k_hist"], inp["v_hist"], cfg.hist_segs, heads)
+    check_cache_rows("full-cache history", cache, 0, k_rot, inp["k_hist"], inp["v_hist"], cfg.hist_segs, [0, 9, 15])
     del k_rot
     out, lse = run_attn(dev16(inp["q"]), dev16(inp["k_new"]), dev16(inp["v_new"]), cfg.new_segs, cache, Lc, H)
-    # the oracle's own cache for the sampled heads (bit-identical to the GPU's, checked above)
+    # the oracle's own cache for every head, bit-identical to the GPU's
+    say("full cache: oracle quantises the history of all %d heads" % H)
+    ocache = oracle.build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs)
+    for g, o, what in zip(cache, ocache, ("k codes", "v codes", "k scales", "v scales")):
+        got = g[:, :Lc].cpu().numpy()
+        assert np.array_equal(got.view(np.uint8 if got.itemsize == 1 else np.uint32),
+                              o.view(np.uint8 if o.itemsize == 1 else np.uint32)), what
+    rows = rows_per_tile(Lq, 16, 20261025, extra=list(range(880, 890)) + list(range(Lq - 16, Lq)))
+    split_rows = rows[rows >= f0 - (H - 1) * Lq] if parts > 1 else rows[:0]
+    say("full cache: %d rows x %d heads (%d rows in head %d's split tiles)" % (len(rows), H, len(split_rows), H - 1))
+    assert parts == 1 or len(split_rows) >= 16 * ((Lq - (f0 - (H - 1) * Lq)) // 256)
+    got = f64(out[torch.from_numpy(rows).to(out.device)])
+    gl = lse.cpu().numpy()[:, rows]
+    one = lambda h: oracle.seg_attn(inp["q"][:, h:h + 1], inp["k_new"][:, h:h + 1], inp["v_new"][:, h:h + 1],
+                                    cfg.new_segs, *(a[h:h + 1] for a in ocache), Lc, SM, rows=rows)
+    with ThreadPoolExecutor(4) as ex:          # heads are independent; numpy's exp is single-threaded
+        for h, (ref, lref) in enumerate(ex.map(one, range(H))):
+            assert_close(got[:, h], ref[:, 0], "full cache head %d (%d rows)" % (h, len(rows)))
+            np.testing.assert_allclose(gl[h], lref[0], rtol=0, atol=2.0 ** -8)
+    heads = [0, 9]
     sub = lambda a: np.ascontiguousarray(a[:, heads])
-    ocache = oracle.build_cache(sub(inp["k_hist"]), sub(inp["v_hist"]), cfg.hist_segs)
-    rows = sample_rows(Lq, 1024, tail=16, extra=range(880, 890))
-    check_rows("full cache", out, lse, sub(inp["q"]), sub(inp["k_new"]), sub(inp["v_new"]),
-               cfg.new_segs, ocache, Lc, rows, heads=list(range(len(heads))), gpu_heads=heads)
+    ocache = tuple(np.ascontiguousarray(a[heads]) for a in ocache)
     # history selection at this shape: 18 of the 288 cached latent frames (the
     # last of every 16), as the benchmark's selection workload runs it
     (hseg,) = cfg.hist_segs
@@ -142,12 +195,13 @@ def test_full_cache_workload():
 def test_five_turns_growing_cache():
     """Five 12 s turns: each turn attends over the cache of all earlier turns,
     runs camera cross-attention, then rotates and appends its keys/values.
-    Quantisation is checked every turn, attention and camera on turns 0 and 4."""
+    Quantisation is checked every turn, attention and camera on turns 0 and 4
+    (heads 3, 12 and 15, with a row in each of head 15's split query tiles)."""
     cfg = synth.WORKLOADS["fiveturns"]
     H = cfg.H
     cap = 5 * synth.turn_seg(0).ntok
     cache = cache_tensors(H, cap)
-    heads = [3, 12]
+    heads = [3, 12, 15]     # head 15 holds the query tiles the launch plan splits into key parts
     length = 0
     okc = {h: [] for h in heads}
     for k in range(5):
@@ -169,7 +223,9 @@ def test_five_turns_growing_cache():
                     vcs[h, :length] = np.concatenate([r[2] for r in okc[h]])
                     kss[h, :length] = np.concatenate([r[1] for r in okc[h]])
                     vss[h, :length] = np.concatenate([r[3] for r in okc[h]])
-            rows = sample_rows(seg.ntok, 2048, tail=16)
+            # one seeded row in each query tile from 120 on (head 15's split tiles at 256 CUs)
+            split_tiles = rows_per_tile(seg.ntok, 1, 20261030 + k)
+            rows = sample_rows(seg.ntok, 2048, tail=16, extra=split_tiles[split_tiles >= 120 * 256])
             check_rows("turn %d" % k, out, lse, inp["q"], inp["k_new"], inp["v_new"], [seg],
                        (kcs, vcs, kss, vss), length, rows, heads=heads)
             # camera cross-attention of the turn's video queries
