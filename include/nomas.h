@@ -134,11 +134,13 @@ int nomas_kv_quant_append(const nomas_bf16* k_rot, const nomas_bf16* v, int64_t 
  *   Results agree to rounding.
  * workspace: device scratch of at least nomas_seg_attn_workspace(...)
  *   bytes (same segments, cache_len, H and n_split, on the current device),
- *   16-byte aligned, owned by the caller; the call overwrites it (the keys
- *   laid out as 64-key tiles, about 140 bytes per cached or new token and
- *   head, each tile's largest squared key norm, plus fp32 partial results
- *   when the keys are split), so two calls
- *   in flight must not share one.  Too small or NULL: NOMAS_EINVAL.
+ *   16-byte aligned, owned by the caller; the call overwrites it, so two
+ *   calls in flight must not share one.  It holds the keys the call may see
+ *   laid out as bf16 64-key tile images, 35,840 bytes per tile and head
+ *   (560 bytes per cached or new token and head: 2.84 GB for 253,440 cached
+ *   + 63,360 new tokens at 16 heads), each tile's largest squared key norm,
+ *   and fp32 partial results when the keys are split.  Too small or NULL:
+ *   NOMAS_EINVAL.
  * n_new_segs in [1, NOMAS_MAX_SEGS]; cap <= NOMAS_MAX_CACHE and
  * Ln * H <= NOMAS_MAX_TOKEN_HEADS, else NOMAS_EUNSUPPORTED.
  */

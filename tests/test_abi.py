@@ -86,6 +86,11 @@ def test_seg_attn_host_checks():
     assert L.nomas_seg_attn_workspace(sa, n, 4000, 4, 1) == 4 * 64 * 35840 + 1024
     # split keys: fp32 partial outputs and log-sum-exps of every part on top
     assert L.nomas_seg_attn_workspace(sa, n, 1000, 3, 2) == 3 * 17 * 35840 + 256 + 2 * 64 * 3 * 129 * 4
+    # 560 bytes per (token, head): the full-cache shape (253,440 cached + 63,360 new tokens, 16 heads)
+    full, nf = segs((0, 288, 72, 22, 40))
+    ws_full = L.nomas_seg_attn_workspace(full, nf, 253440, 16, 1)
+    assert ws_full == 16 * 4950 * 35840 + (16 * 4950 * 4 + 255) // 256 * 256
+    assert 35840 // 64 == 560 and abs(ws_full / (16 * 316800) - 560) < 0.1 and 2.83e9 < ws_full < 2.85e9
     assert L.nomas_seg_attn_workspace(sa, n, -1, 3, 1) == nomas.EINVAL
     assert L.nomas_seg_attn_workspace(sa, n, 0, 0, 1) == nomas.EINVAL
     assert L.nomas_seg_attn_workspace(sa, n, 0, 2, -1) == nomas.EINVAL
