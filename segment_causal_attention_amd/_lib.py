@@ -137,6 +137,44 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _torch_stream(stream):
+    """The torch stream object for `stream` (None: the current stream; an
+    int: a raw hipStream_t handle, wrapped without taking ownership)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
+def _alloc_on(stream):
+    """Context for the tensors a call allocates (outputs, workspace).
+
+    PyTorch's caching allocator hands a freed block to the next allocation on
+    the stream the block was allocated on, ordered by that stream alone.  A
+    workspace allocated on the current stream but written by kernels queued
+    on another stream could therefore be reused while those kernels still
+    run.  Allocating under the call's own stream makes the reuse wait behind
+    the call's kernels."""
+    import contextlib
+    import torch
+    if stream is None:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(_torch_stream(stream))
+
+
+def _workspace(need, device, workspace, stream):
+    """The caller's workspace (checked), or a new one on the call's stream."""
+    import torch
+    if workspace is None:
+        with _alloc_on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device uint8 tensor")
+    return workspace
+
+
 def _dev(t, name, shape=None, elem=2):
     if t is None:
         raise ValueError("%s is required" % name)
@@ -160,7 +198,8 @@ def rope3d(x, segs, out=None, stream=None):
     L, H = x.shape[0], x.shape[1]
     _dev(x, "x", (seg_tokens(segs), H, HEAD_DIM))
     if out is None:
-        out = torch.empty_like(x)
+        with _alloc_on(stream):
+            out = torch.empty_like(x)
     _dev(out, "out", x.shape)
     arr, n = seg_array(segs)
     _check(lib().nomas_rope3d(_ptr(x), _ptr(out), arr, n, H, _stream(stream)), "nomas_rope3d")
@@ -237,15 +276,13 @@ def seg_attn(q, k_new, v_new, new_segs, k_codes=None, v_codes=None, k_scale=None
     elif k_codes is not None:
         cap = k_codes.shape[1]
     if out is None:
-        out = torch.empty_like(q)
+        with _alloc_on(stream):
+            out = torch.empty_like(q)
     _dev(out, "out", shp)
     if lse is not None:
         _dev(lse, "lse", (H, Ln), 4)
     need = seg_attn_workspace(new_segs, cache_len, H, n_split, sel)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device uint8 tensor")
+    workspace = _workspace(need, q.device, workspace, stream)
     arr, n = seg_array(new_segs)
     if sel is None:
         _check(lib().nomas_seg_attn(_ptr(q), _ptr(k_new), _ptr(v_new), arr, n, _ptr(k_codes), _ptr(v_codes),
@@ -286,14 +323,12 @@ def seg_attn_bwd(q, k, v, out, lse, d_out, segs, sm_scale: float = SM_SCALE, dq=
     grads = []
     for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if g is None:
-            g = torch.empty(shp, dtype=torch.float32, device=q.device)
+            with _alloc_on(stream):
+                g = torch.empty(shp, dtype=torch.float32, device=q.device)
         _dev(g, name, shp, 4)
         grads.append(g)
     need = seg_attn_bwd_workspace(segs, H)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device uint8 tensor")
+    workspace = _workspace(need, q.device, workspace, stream)
     arr, n = seg_array(segs)
     _check(lib().nomas_seg_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), arr, n, H,
                                     float(sm_scale), _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]),
@@ -319,15 +354,13 @@ def gqa_attn(q, k, v, sm_scale: float = SM_SCALE, out=None, lse=None, workspace=
     _dev(k, "k", (L, Hkv, HEAD_DIM))
     _dev(v, "v", (L, Hkv, HEAD_DIM))
     if out is None:
-        out = torch.empty_like(q)
+        with _alloc_on(stream):
+            out = torch.empty_like(q)
     _dev(out, "out", q.shape)
     if lse is not None:
         _dev(lse, "lse", (Hq, L), 4)
     need = gqa_attn_workspace(L, Hq, Hkv)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device uint8 tensor")
+    workspace = _workspace(need, q.device, workspace, stream)
     _check(lib().nomas_gqa_attn(_ptr(q), _ptr(k), _ptr(v), L, Hq, Hkv, float(sm_scale), _ptr(out), _ptr(lse),
                                 _ptr(workspace), workspace.numel(), _stream(stream)), "nomas_gqa_attn")
     return out
@@ -351,13 +384,11 @@ def w8a16_linear(x, w_codes, w_scale, out=None, workspace=None, stream=None):
     _dev(w_codes, "w_codes", (N, K), 1)
     _dev(w_scale, "w_scale", (N,), 4)
     if out is None:
-        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+        with _alloc_on(stream):
+            out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _dev(out, "out", (M, N))
     need = w8a16_linear_workspace(K, N)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device uint8 tensor")
+    workspace = _workspace(need, x.device, workspace, stream)
     _check(lib().nomas_w8a16_linear(_ptr(x), M, K, _ptr(w_codes), _ptr(w_scale), N, _ptr(out), _ptr(workspace),
                                     workspace.numel(), _stream(stream)), "nomas_w8a16_linear")
     return out
@@ -383,7 +414,8 @@ def cam_xattn(q, cam, w_k, w_v, sm_scale: float = SM_SCALE, out=None, stream=Non
     _dev(w_k, "w_k", (64, H * HEAD_DIM))
     _dev(w_v, "w_v", (64, H * HEAD_DIM))
     if out is None:
-        out = torch.empty_like(q)
+        with _alloc_on(stream):
+            out = torch.empty_like(q)
     _dev(out, "out", q.shape)
     _check(lib().nomas_cam_xattn(_ptr(q), Lq, H, _ptr(cam), Nc, _ptr(w_k), _ptr(w_v), float(sm_scale),
                                  _ptr(out), _stream(stream)), "nomas_cam_xattn")

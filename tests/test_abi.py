@@ -286,3 +286,49 @@ def test_seg_attn_bwd_host_checks():
     assert call(n=nomas.MAX_SEGS + 1) == nomas.EUNSUPPORTED
     empty, ne = segs((0, 0, 0, 0, 0))
     assert call(segs=empty, n=ne, ws=None, wsb=0) == nomas.OK      # no tokens: nothing to do
+
+
+def test_binding_allocates_on_the_call_stream(monkeypatch):
+    """Workspace and outputs the binding allocates for a call queued on a
+    given stream come from that stream's pool (torch.cuda.stream context), so
+    the caching allocator cannot reuse them behind kernels still running on
+    it; with no stream given the current stream is used as is.  CPU-only:
+    torch's stream context and allocator are replaced by recorders."""
+    import contextlib
+    import torch
+    from segment_causal_attention_amd import _lib
+    events = []
+
+    class Ext:
+        def __init__(self, handle):
+            self.handle = handle
+
+    @contextlib.contextmanager
+    def stream_ctx(s):
+        events.append(("enter", s))
+        yield
+        events.append(("exit", s))
+
+    real_empty = torch.empty
+
+    def empty(*a, **k):
+        events.append(("alloc",))
+        k.pop("device", None)
+        return real_empty(*a, **k)
+
+    monkeypatch.setattr(torch.cuda, "ExternalStream", Ext)
+    monkeypatch.setattr(torch.cuda, "stream", stream_ctx)
+    monkeypatch.setattr(torch, "empty", empty)
+    with pytest.raises(ValueError):             # a host tensor is no device workspace
+        _lib._workspace(100, "cpu", None, 0x1234)
+    assert [e[0] for e in events] == ["enter", "alloc", "exit"]
+    assert isinstance(events[0][1], Ext) and events[0][1].handle == 0x1234
+    events.clear()
+    obj = object()
+    with pytest.raises(ValueError):
+        _lib._workspace(100, "cpu", None, obj)
+    assert [e[0] for e in events] == ["enter", "alloc", "exit"] and events[0][1] is obj
+    events.clear()
+    with pytest.raises(ValueError):
+        _lib._workspace(100, "cpu", None, None)
+    assert events == [("alloc",)]

@@ -368,6 +368,32 @@ def test_seg_attn_deterministic_and_cache_copy():
     assert torch.equal(o1, o3)
 
 
+def test_seg_attn_on_a_side_stream_without_workspace():
+    """A call queued on a stream other than the current one, with the
+    workspace and output allocated by the binding, gives the same bits as on
+    the current stream; the next allocations on the current stream run while
+    the side stream may still be busy."""
+    segs, Lc, H = [(256, 18, 2, 22, 40)], 1760, 2
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    kc, vc, ks, vs = (dev(a) for a in cache)
+    ref = nomas.seg_attn(qd, kd, vd, segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for i in range(3):
+        outs.append(nomas.seg_attn(qd, kd, vd, segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, stream=side))
+        junk = torch.empty(nomas.seg_attn_workspace(segs, Lc, H), dtype=torch.uint8, device="cuda:0")
+        junk.fill_(0xFF)                      # would corrupt a workspace reused across streams
+        del junk
+    raw = nomas.seg_attn(qd, kd, vd, segs, kc, vc, ks, vs, cache_len=Lc, sm_scale=SM, stream=side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for o in outs + [raw]:
+        assert torch.equal(o, ref)
+
+
 # ----------------------------------------------------------------------------
 # decoder window attention with grouped KV heads (nomas_gqa_attn)
 

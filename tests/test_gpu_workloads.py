@@ -10,10 +10,12 @@ are independent.
   five turns   cache grown turn by turn to 253,440 tokens, camera cross-attention
   decoder      one 10-latent-frame window: 35,200 tokens, 32 query / 8 KV heads
 """
+import os
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
+import threadpoolctl
 import torch
 
 import oracle
@@ -168,7 +170,10 @@ def test_full_cache_workload():
     gl = lse.cpu().numpy()[:, rows]
     one = lambda h: oracle.seg_attn(inp["q"][:, h:h + 1], inp["k_new"][:, h:h + 1], inp["v_new"][:, h:h + 1],
                                     cfg.new_segs, *(a[h:h + 1] for a in ocache), Lc, SM, rows=rows)
-    with ThreadPoolExecutor(4) as ex:          # heads are independent; numpy's exp is single-threaded
+    # heads are independent and numpy's exp is single-threaded: 4 heads at a
+    # time, each with a quarter of the host's BLAS threads (more would oversubscribe)
+    blas = max(1, int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 4) // 4)
+    with threadpoolctl.threadpool_limits(blas, user_api="blas"), ThreadPoolExecutor(4) as ex:
         for h, (ref, lref) in enumerate(ex.map(one, range(H))):
             assert_close(got[:, h], ref[:, 0], "full cache head %d (%d rows)" % (h, len(rows)))
             np.testing.assert_allclose(gl[h], lref[0], rtol=0, atol=2.0 ** -8)
