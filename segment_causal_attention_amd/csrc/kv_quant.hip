@@ -33,17 +33,20 @@ constexpr int QT_PASSES = 4;        // 16-token passes per block
 
 // Block = 64 consecutive tokens of one head of K or of V, in passes of 16
 // whose loads are all issued first: each pass's codes land as 2 KB of
-// contiguous cache rows and its scales as 64 contiguous bytes.
+// contiguous cache rows and its scales as 64 contiguous bytes.  Blocks are
+// ordered token range first, then head, then K / V, so the blocks in flight
+// together read whole 4 KB token rows ([L][H][128] bf16: every head's 256 B
+// slice of a token) rather than one head's slices 4 KB apart.
 __global__ __launch_bounds__(256) void kv_quant_append_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, int64_t L, int H, int64_t ntb,
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
     int64_t cap, int64_t len) {
-    const int64_t per_tensor = (int64_t)H * ntb;
-    const bool is_v = blockIdx.x >= per_tensor;
-    const int64_t b = is_v ? blockIdx.x - per_tensor : blockIdx.x;
-    const int head = (int)(b / ntb);
+    const bool is_v = (blockIdx.x & 1) != 0;
+    const int64_t b = blockIdx.x >> 1;
+    const int64_t tb = b / H;                  // token range
+    const int head = (int)(b - tb * H);
     const int lane = threadIdx.x & 15;
-    const int64_t tok0 = (b - head * ntb) * QT_PASSES * 16 + (threadIdx.x >> 4);
+    const int64_t tok0 = tb * QT_PASSES * 16 + (threadIdx.x >> 4);
     const uint4* src = is_v ? v : k;
     uint4 w[QT_PASSES];
 #pragma unroll

@@ -6,8 +6,9 @@
 // group, head block), so the token's position and each group's float64
 // cos/sin entries are looked up once and applied to every head (lanes
 // 16b .. 16b+15 take heads b, b+4, ...); each head pass moves 1 KB of
-// contiguous rows.  The rotation is rope_chunk_f64's (float64, rounded once
-// to bf16).
+// contiguous rows, and the loads of four passes (16 heads, the whole 4 KB
+// token) are issued before any of them is rotated, so a wave keeps 4 KB in
+// flight.  The rotation is rope_chunk_f64's (float64, rounded once to bf16).
 #include "common.hpp"
 
 namespace nomas {
@@ -27,16 +28,25 @@ __global__ __launch_bounds__(ROPE_NT) void rope3d_kernel(const uint4* __restrict
 #pragma unroll
         for (int i = 0; i < 4; ++i) cs[i] = tab[i];
     }
-    for (int hd = lane >> 4; hd < H; hd += 4) {
-        const int64_t idx = (tok * H + hd) * 16 + grp;
-        uint4 v = x[idx];
-        if (video) {
-            v.x = rot_pair_f64(v.x, cs[0]);
-            v.y = rot_pair_f64(v.y, cs[1]);
-            v.z = rot_pair_f64(v.z, cs[2]);
-            v.w = rot_pair_f64(v.w, cs[3]);
+    for (int hd0 = lane >> 4; hd0 < H; hd0 += 16) {
+        uint4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int hd = hd0 + 4 * j;
+            if (hd < H) v[j] = x[(tok * H + hd) * 16 + grp];
         }
-        y[idx] = v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int hd = hd0 + 4 * j;
+            if (hd >= H) break;
+            if (video) {
+                v[j].x = rot_pair_f64(v[j].x, cs[0]);
+                v[j].y = rot_pair_f64(v[j].y, cs[1]);
+                v[j].z = rot_pair_f64(v[j].z, cs[2]);
+                v[j].w = rot_pair_f64(v[j].w, cs[3]);
+            }
+            y[(tok * H + hd) * 16 + grp] = v[j];
+        }
     }
 }
 
