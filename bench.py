@@ -68,6 +68,71 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class ClockSampler:
+    """Shader-clock samples of GPU 0 while the timed steps run: the SMU's
+    per-XCD current graphics clock (amdsmi gpu metrics), read every ~10 ms on
+    a host thread.  The peak of 2516.6 TFLOP/s assumes 2.4 GHz; a kernel held
+    below that clock by the power limit cannot reach it, so the bench line
+    also states the fraction of the peak at the measured clock.  Everything
+    degrades to None when the metrics cannot be read."""
+
+    def __init__(self, period_s=0.01):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self._h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            self._smi = amdsmi
+            self._h = hs[0] if hs else None
+        except Exception as e:          # no GPU metrics here: report no clock
+            log("clock sampler unavailable: %s" % e)
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        xs = m.get("current_gfxclks")
+        vals = [float(x) for x in xs if isinstance(x, (int, float)) and 0 < x < 10000] if isinstance(xs, list) else []
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [float(m["current_gfxclk"])]
+        return sum(vals) / len(vals) if vals else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v:
+                    self.samples.append(v)
+            except Exception:
+                pass
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self._h is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        try:
+            if self._h is not None:
+                self._smi.amdsmi_shut_down()
+        except Exception:
+            pass
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": xs[0], "max_mhz": xs[-1], "samples": len(xs),
+                "source": "amdsmi gpu metrics current_gfxclks (mean over XCDs), sampled every 10 ms during the "
+                          "timed steps"}
+
+
 def copy_calibration():
     """A plain device copy of a known size, for scaling FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -90,7 +155,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--workloads", action="store_true")
-    ap.add_argument("--only", default="", help="with --workloads: comma-separated groups (turn3s, seg4s, "
+    ap.add_argument("--only", default="", help="with --workloads: comma-separated groups (tiny, turn3s, seg4s, "
                     "fiveturns, decoder, w8a16, fullcache, train)")
     args = ap.parse_args()
 
@@ -102,7 +167,7 @@ def main():
         copy_calibration()
         return
     if args.workloads:
-        workloads([w for w in args.only.split(",") if w])
+        workloads([w for w in args.only.split(",") if w], cpu=not args.no_cpu_baseline)
         return
 
     import numpy as np
@@ -167,11 +232,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    clock = ClockSampler()
+    clock.start()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    clk = clock.stop()
 
     pairs = Lq * (Lc + Lq)
     flops = 4.0 * 128 * H * pairs
@@ -181,6 +249,12 @@ def main():
     achieved = flops / (attn_ms * 1e-3) / 1e12
     log("step %.3f ms, nomas_seg_attn %.3f ms (%.1f TFLOP/s, %.1f%% of peak)"
         % (ms_step, attn_ms, achieved, 100 * achieved / PEAK_BF16_TFLOPS))
+    if clk:
+        # dense BF16 MFMA: 256 CUs x 4096 FLOP per clock at the measured clock
+        clk["peak_at_clock_tflops"] = round(256 * 4096 * clk["mean_mhz"] * 1e6 / 1e12, 1)
+        clk["frac_at_clock"] = round(achieved / clk["peak_at_clock_tflops"], 4)
+        log("shader clock %.0f MHz (%d samples): %.1f%% of the peak at that clock"
+            % (clk["mean_mhz"], clk["samples"], 100 * clk["frac_at_clock"]))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -216,16 +290,19 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": round(attn_ms, 3),
             "traffic": traffic_for_current_kernel(),
+            "clock": clk,
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
 
 
-def workloads(only=None):
+def workloads(only=None, cpu=True):
     """Throughput of the path on the other workloads, one JSON line each, all
     inputs seeded synthetic and resident in HBM before timing, HIP events on
     the launch stream:
+      tiny        2 segments of 64 tokens (16 text + 2 x 4 x 6 video), 2 heads:
+                  the second over the first as a 64-token INT8 cache (median of 20)
       turn3s      16,096 queries over 15,840 cached + 16,096 own keys (median of 10 calls)
       seg4s       54 distinct layers (outlier channels x20) x 8 steps = 432 calls
                   timed end to end (median of 3 sequences)
@@ -248,7 +325,10 @@ def workloads(only=None):
                   (354,112 tokens, block-causal) with 2 heads (one GPU's share
                   of a head-sharded layer), forward and backward (median of 5)
     History caches are built on the GPU by rope3d + kv_quant_append (bit-exact
-    to the oracle's quantiser)."""
+    to the oracle's quantiser).  With cpu, the attention lines also carry the
+    oracle (numpy float64, as it stands) timed on the host: tiny, turn3s and
+    one seg4s call (layer 0) in full, and 4,096 query rows of head 0 on turns 0
+    and 4 of fiveturns; the oracle quantises its own caches, untimed."""
     import numpy as np
     import torch
 
@@ -294,12 +374,39 @@ def workloads(only=None):
         line = dict(workload=name, **kw)
         print(json.dumps(line), flush=True)
 
-    def attn_line(name, ms, H, Lq, keys, extra=None):
+    def attn_line(name, ms, H, Lq, keys, extra=None, cpu_b=None):
         fl = 4.0 * 128 * H * Lq * keys
         tf = fl / (ms * 1e-3) / 1e12
-        emit(name, metric="attention TFLOP/s", value=round(tf, 2), unit="TFLOP/s", ms=round(ms, 3),
-             pct_of_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2), heads=H, queries=Lq, keys_per_query=keys,
-             algorithmic_flop=fl, **(extra or {}))
+        more = dict(extra or {})
+        if cpu_b is not None:
+            more["cpu_baseline"] = dict(cpu_b, gpu_over_cpu=round(tf / cpu_b["value"], 1))
+        emit(name, metric="attention TFLOP/s", value=round(tf, 3 if tf < 1 else 2), unit="TFLOP/s", ms=round(ms, 4),
+             pct_of_peak=round(100 * tf / PEAK_BF16_TFLOPS, 3), heads=H, queries=Lq, keys_per_query=keys,
+             algorithmic_flop=fl, **more)
+
+    if cpu:
+        import oracle
+
+    if want("tiny"):
+        # ---- tiny: segment 1 over segment 0 as a 64-token INT8 cache
+        log("workload tiny")
+        inp = synth.tiny_inputs()
+        segs = [s.astuple() for s in inp["segs"]]
+        n = 64
+        cache = build_cache(inp["k"][:n], inp["v"][:n], segs[:1], 2, n)
+        q, k, v = (d16(inp[x][n:2 * n]) for x in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        ws = torch.empty(nomas.seg_attn_workspace(segs[1:2], n, 2), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: nomas.seg_attn(q, k, v, segs[1:2], *cache, cache_len=n, sm_scale=sm, out=out, workspace=ws,
+                                          stream=stream), 20, 3)
+        cpu_b = None
+        if cpu:
+            oc = oracle.build_cache(inp["k"][:n], inp["v"][:n], segs[:1])
+            qn, kn, vn = (np.ascontiguousarray(inp[x][n:2 * n]) for x in ("q", "k", "v"))
+            cpu_b = oracle_timing(lambda: oracle.seg_attn(qn, kn, vn, segs[1:2], *oc, n, sm), 4.0 * 128 * 2 * n * 2 * n,
+                                  "numpy float64 oracle, the whole call (64 queries x 128 keys x 2 heads)")
+        attn_line("tiny", ms, 2, n, 2 * n, dict(cache_tokens=n), cpu_b)
+        del q, k, v, out, ws, cache
 
     if want("turn3s"):
         # ---- turn3s
@@ -313,7 +420,15 @@ def workloads(only=None):
         ws = torch.empty(nomas.seg_attn_workspace([seg], cfg.Lc, cfg.H), dtype=torch.uint8, device=dev)
         ms = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=cfg.Lc, sm_scale=sm, out=out, workspace=ws,
                                           stream=stream), 10, 3)
-        attn_line("turn3s", ms, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq)
+        cpu_b = None
+        if cpu:
+            oc = oracle.build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs)
+            cpu_b = oracle_timing(
+                lambda: oracle.seg_attn(inp["q"], inp["k_new"], inp["v_new"], cfg.new_segs, *oc, cfg.Lc, sm),
+                4.0 * 128 * cfg.H * cfg.Lq * (cfg.Lc + cfg.Lq),
+                "numpy float64 oracle, the whole call (16,096 queries x 31,936 keys x 16 heads)")
+            del oc
+        attn_line("turn3s", ms, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq, cpu_b=cpu_b)
         del q, k, v, out, ws, cache, inp
 
     if want("seg4s"):
@@ -341,9 +456,19 @@ def workloads(only=None):
 
         ms = timed(sequence, 3, 1)
         calls = cfg.layers * cfg.steps
+        del layers
+        cpu_b = None
+        if cpu:
+            inp = synth.layer_inputs("seg4s", 0)
+            oc = oracle.build_cache(inp["k_hist"], inp["v_hist"], cfg.hist_segs)
+            cpu_b = oracle_timing(
+                lambda: oracle.seg_attn(inp["q"], inp["k_new"], inp["v_new"], cfg.new_segs, *oc, cfg.Lc, sm),
+                4.0 * 128 * cfg.H * cfg.Lq * (cfg.Lc + cfg.Lq),
+                "numpy float64 oracle, one whole call (layer 0: 21,376 queries x 37,216 keys x 16 heads)")
+            del inp, oc
         attn_line("seg4s", ms / calls, cfg.H, cfg.Lq, cfg.Lc + cfg.Lq,
-                  dict(calls=calls, sequence_ms=round(ms, 1), outlier_channels=cfg.outliers))
-        del layers, out, ws
+                  dict(calls=calls, sequence_ms=round(ms, 1), outlier_channels=cfg.outliers), cpu_b)
+        del out, ws
 
     if want("fiveturns"):
         # ---- fiveturns
@@ -353,6 +478,7 @@ def workloads(only=None):
         n = synth.turn_seg(0).ntok
         cache = build_cache(None, None, None, H, 5 * n)
         length = 0
+        ohead = []              # the oracle's own INT8 rows of head 0, turn by turn
         for t in range(5):
             inp = synth.turn_inputs(t)
             seg = inp["seg"]
@@ -369,12 +495,31 @@ def workloads(only=None):
             ms_q = timed(lambda: nomas.kv_quant_append(kr, v, *cache, length, stream=stream), 5)
             elems = n * H * 128
             gbs = lambda b, m: round(b / (m * 1e-3) / 1e9, 1)
+            cpu_b = None
+            if cpu and t in (0, 4):
+                rows = np.arange(4096)
+                oc = [np.zeros((1, max(1, length), 128), np.int8), np.zeros((1, max(1, length), 128), np.int8),
+                      np.zeros((1, max(1, length)), np.float32), np.zeros((1, max(1, length)), np.float32)]
+                if length:
+                    for i in range(4):
+                        oc[i][0, :length] = np.concatenate([r[i] for r in ohead])
+                q1, k1, v1 = (np.ascontiguousarray(inp[x][:, :1]) for x in ("q", "k_new", "v_new"))
+                cpu_b = oracle_timing(
+                    lambda: oracle.seg_attn(q1, k1, v1, [seg], *oc, length, sm, rows=rows),
+                    4.0 * 128 * len(rows) * (length + n),
+                    "numpy float64 oracle, head 0, query rows 0..4095 of %d, each over all %d keys"
+                    % (n, length + n))
             attn_line("fiveturns-turn%d" % t, ms_a, H, n, length + n,
                       dict(cache_tokens=length,
                            cam_xattn=dict(ms=round(ms_c, 4), GBps=gbs(4 * elems, ms_c), camera_tokens=cam.shape[0]),
                            rope3d=dict(ms=round(ms_r, 4), GBps=gbs(4 * elems, ms_r)),
                            kv_quant_append=dict(ms=round(ms_q, 4), GBps=gbs(2 * 3 * elems + 2 * 4 * n * H, ms_q)),
-                           hbm_peak_GBps=PEAK_HBM_GBS))
+                           hbm_peak_GBps=PEAK_HBM_GBS), cpu_b)
+            if cpu and t < 4:
+                kr = oracle.bf16_round(oracle.rope3d(oracle.bf16_bits_to_f64(inp["k_new"][:, :1]), [seg]))[:, 0]
+                kq, ksc = oracle.quantise(kr)
+                vq, vsc = oracle.quantise(oracle.bf16_bits_to_f64(inp["v_new"][:, 0]))
+                ohead.append((kq, vq, ksc, vsc))
             length = nomas.kv_quant_append(kr, v, *cache, length, stream=stream)
             torch.cuda.synchronize()
             del q, k, v, qc, out, oc, kr, ws
@@ -491,6 +636,36 @@ def workloads(only=None):
              fwd_plus_bwd_ms=round(ms_f + ms_b, 3))
 
 
+def _cpu_info():
+    """Threads the oracle's BLAS uses and the host CPU model."""
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((i.get("num_threads") or 1) for i in info) if info else int(threads)
+    except Exception:
+        cores = int(threads)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return int(cores), model
+
+
+def oracle_timing(run, flops, sample):
+    """Time one oracle call (numpy float64, as it stands) and report it as a
+    cpu_baseline object in TFLOP/s of algorithmic attention FLOPs."""
+    t0 = time.perf_counter()
+    run()
+    dt = time.perf_counter() - t0
+    cores, model = _cpu_info()
+    log("cpu baseline: %.2f s for %.3e FLOP (%s)" % (dt, flops, sample))
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 4), "cpu_model": model, "sample": sample}
+
+
 def cpu_baseline(inp, cfg, sm):
     """The oracle (numpy float64) on a bounded sample: head 0, the first 8192
     of the 63,360 query rows, all 316,800 allowed keys."""
@@ -504,35 +679,12 @@ def cpu_baseline(inp, cfg, sm):
     q1 = np.ascontiguousarray(inp["q"][:, :1])
     k1 = np.ascontiguousarray(inp["k_new"][:, :1])
     v1 = np.ascontiguousarray(inp["v_new"][:, :1])
-    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
-    t0 = time.perf_counter()
-    oracle.seg_attn(q1, k1, v1, cfg.new_segs, kc, vc, ks, vs, Lc, sm, rows=rows)
-    dt = time.perf_counter() - t0
     flops = 4.0 * 128 * len(rows) * (Lc + Lq)
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max((i.get("num_threads") or 1) for i in info) if info else int(threads)
-    except Exception:
-        cores = int(threads)
-    log("cpu baseline: %.2f s for %.3e FLOP" % (dt, flops))
-    model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
-    except OSError:
-        pass
-    return {
-        "value": round(flops / dt / 1e12, 5),
-        "unit": "TFLOP/s",
-        "cores": int(cores),
-        "kind": "oracle",
-        "seconds": round(dt, 2),
-        "cpu_model": model,
-        "sample": "numpy float64 oracle, head 0 of 16, query rows 0..8191 of 63,360, each over all 316,800 "
-                  "allowed keys (%.2e algorithmic FLOP), timed including its per-head key dequantisation "
-                  "and rotation" % flops,
-    }
+    return oracle_timing(
+        lambda: oracle.seg_attn(q1, k1, v1, cfg.new_segs, kc, vc, ks, vs, Lc, sm, rows=rows), flops,
+        "numpy float64 oracle, head 0 of 16, query rows 0..8191 of 63,360, each over all 316,800 "
+        "allowed keys (%.2e algorithmic FLOP), timed including its per-head key dequantisation "
+        "and rotation" % flops)
 
 
 if __name__ == "__main__":
