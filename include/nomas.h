@@ -281,6 +281,29 @@ int nomas_w8a16_linear(const nomas_bf16* x, int64_t M, int64_t K, const int8_t* 
 /* Workspace bytes nomas_w8a16_linear needs (N * K * 2), or a negative error code.  Host only. */
 int64_t nomas_w8a16_linear_workspace(int64_t K, int64_t N);
 
+/* Largest N * K * 2 (dequantised weight bytes) nomas_w8a16_linear_noalloc
+ * takes: 32 MiB, every linear shape of the DiT (2048 -> 6144 / 8192,
+ * 8192 -> 2048). */
+#define NOMAS_W8A16_NOALLOC_MAX_BYTES ((int64_t)32 << 20)
+
+/*
+ * nomas_w8a16_linear for callers that cannot allocate device memory: code
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, result and kernels as nomas_w8a16_linear,
+ * without the workspace: the dequantised weights go into a static scratch
+ * array of the library (NOMAS_W8A16_NOALLOC_MAX_BYTES per device, held from
+ * the library's load until the process ends).  No memory is allocated or
+ * freed and no allocating routine is called.  The first call on a device
+ * looks up the scratch array's device address (hipGetSymbolAddress) and
+ * keeps it.  N * K * 2 > NOMAS_W8A16_NOALLOC_MAX_BYTES: NOMAS_EUNSUPPORTED,
+ * checked before anything touches the device.  Every call on one device
+ * shares that device's array, and each call overwrites the part it uses
+ * before reading it (nothing needs clearing), so calls that overlap in time
+ * on one device (other streams, other threads) race: serialise them.
+ */
+int nomas_w8a16_linear_noalloc(const nomas_bf16* x, int64_t M, int64_t K, const int8_t* w_codes,
+                               const float* w_scale, int64_t N, nomas_bf16* y, void* stream);
+
 /*
  * Camera tokens of one turn (comfyui-wiki news, 相机控制作为一等输入).
  * Poses are made relative to the first frame (R0^T R_k, R0^T (t_k - t0)),

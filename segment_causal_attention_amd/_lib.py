@@ -27,7 +27,7 @@ SM_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_workspace",
            "nomas_seg_attn_sel", "nomas_seg_attn_sel_workspace", "nomas_gqa_attn", "nomas_gqa_attn_workspace",
            "nomas_seg_attn_bwd", "nomas_seg_attn_bwd_workspace",
-           "nomas_w8a16_linear", "nomas_w8a16_linear_workspace",
+           "nomas_w8a16_linear", "nomas_w8a16_linear_workspace", "nomas_w8a16_linear_noalloc",
            "nomas_cam_tokens", "nomas_cam_xattn", "nomas_rope_table", "nomas_strerror", "nomas_version")
 
 
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.nomas_w8a16_linear.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _P]
         L.nomas_w8a16_linear_workspace.argtypes = [_I64, _I64]
         L.nomas_w8a16_linear_workspace.restype = _I64
+        L.nomas_w8a16_linear_noalloc.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P]
         L.nomas_cam_tokens.argtypes = [_P, _I, _D, _D, _P]
         L.nomas_cam_xattn.argtypes = [_P, _I64, _I, _P, _I, _P, _P, _F, _P, _P]
         L.nomas_rope_table.argtypes = [_I, _I, _P, _P]
@@ -86,7 +87,7 @@ def lib() -> ctypes.CDLL:
         L.nomas_version.restype = ctypes.c_char_p
         for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_sel", "nomas_gqa_attn",
                      "nomas_seg_attn_bwd",
-                     "nomas_w8a16_linear",
+                     "nomas_w8a16_linear", "nomas_w8a16_linear_noalloc",
                      "nomas_cam_tokens",
                      "nomas_cam_xattn", "nomas_rope_table"):
             getattr(L, name).restype = _I
@@ -391,6 +392,25 @@ def w8a16_linear(x, w_codes, w_scale, out=None, workspace=None, stream=None):
     workspace = _workspace(need, x.device, workspace, stream)
     _check(lib().nomas_w8a16_linear(_ptr(x), M, K, _ptr(w_codes), _ptr(w_scale), N, _ptr(out), _ptr(workspace),
                                     workspace.numel(), _stream(stream)), "nomas_w8a16_linear")
+    return out
+
+
+W8A16_NOALLOC_MAX_BYTES = 32 << 20
+
+
+def w8a16_linear_noalloc(x, w_codes, w_scale, out, stream=None):
+    """w8a16_linear without a workspace (nomas_w8a16_linear_noalloc): the
+    library's static per-device scratch holds the dequantised weights, so the
+    call allocates nothing; `out` [M][N] must be given.  Calls that overlap
+    in time on one device share that scratch and race."""
+    M, K = x.shape
+    N = w_codes.shape[0]
+    _dev(x, "x", (M, K))
+    _dev(w_codes, "w_codes", (N, K), 1)
+    _dev(w_scale, "w_scale", (N,), 4)
+    _dev(out, "out", (M, N))
+    _check(lib().nomas_w8a16_linear_noalloc(_ptr(x), M, K, _ptr(w_codes), _ptr(w_scale), N, _ptr(out),
+                                            _stream(stream)), "nomas_w8a16_linear_noalloc")
     return out
 
 

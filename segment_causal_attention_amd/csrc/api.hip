@@ -23,6 +23,7 @@ int64_t seg_attn_workspace_bytes(const SegTable& segs, int Lc, int Ln, int H, in
 int launch_w8a16(const uint16_t* x, int64_t M, int64_t K, const int8_t* codes, const float* scale, int64_t N,
                  uint16_t* y, void* workspace, hipStream_t stream);
 int64_t w8a16_workspace_bytes(int64_t N, int64_t K);
+int w8a16_scratch(void** out);
 int launch_seg_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                         const float* lse, const uint16_t* dout, const SegTable& st, int Ln, int H, float sm_scale,
                         float* dq, float* dk, float* dv, void* workspace, const RopeTables& rt, hipStream_t stream);
@@ -341,6 +342,19 @@ int nomas_w8a16_linear(const nomas_bf16* x, int64_t M, int64_t K, const int8_t* 
         return NOMAS_EINVAL;
     if (workspace_bytes < w8a16_workspace_bytes(N, K)) return NOMAS_EINVAL;
     return launch_w8a16(x, M, K, w_codes, w_scale, N, y, workspace, (hipStream_t)stream);
+}
+
+int nomas_w8a16_linear_noalloc(const nomas_bf16* x, int64_t M, int64_t K, const int8_t* w_codes,
+                               const float* w_scale, int64_t N, nomas_bf16* y, void* stream) {
+    int rc = w8a16_shape(M, K, N);
+    if (rc != NOMAS_OK) return rc;
+    if (!w_codes || !w_scale) return NOMAS_EINVAL;
+    if (M > 0 && (!x || !y)) return NOMAS_EINVAL;
+    if ((x && !al16(x)) || (y && !al16(y)) || !al16(w_codes) || !al4(w_scale)) return NOMAS_EINVAL;
+    if (w8a16_workspace_bytes(N, K) > NOMAS_W8A16_NOALLOC_MAX_BYTES) return NOMAS_EUNSUPPORTED;
+    void* ws = nullptr;
+    if ((rc = w8a16_scratch(&ws)) != NOMAS_OK) return rc;
+    return launch_w8a16(x, M, K, w_codes, w_scale, N, y, ws, (hipStream_t)stream);
 }
 
 int nomas_cam_tokens(const double* c2w, int n_frames, double translation_scale, double rotation_scale,

@@ -24,6 +24,8 @@
 // conflicts.  Two stages: step t+1
 // is copied into the stage step t-1 left while step t computes.  Reads of
 // x past row M come back as zeros (buffer range checking); stores stop at M.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace nomas {
@@ -181,6 +183,35 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
 }
 
 int64_t w8a16_workspace_bytes(int64_t N, int64_t K) { return N * K * 2; }
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the dequantised weights of one
+// call go into this static array of the code object instead of a caller
+// workspace.  Each device that loads the library holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, so kernels
+// are given the device address that hipGetSymbolAddress returns, looked up
+// once per device with that device current.
+
+static __device__ __align__(256) uint8_t scratch[NOMAS_W8A16_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+int w8a16_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return NOMAS_EHIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NOMAS_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return NOMAS_OK;
+}
 
 int launch_w8a16(const uint16_t* x, int64_t M, int64_t K, const int8_t* codes, const float* scale, int64_t N,
                  uint16_t* y, void* workspace, hipStream_t stream) {

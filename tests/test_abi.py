@@ -253,6 +253,31 @@ def test_w8a16_host_checks():
     assert call(M=1 << 20, K=2048) == nomas.EUNSUPPORTED     # x beyond 2 GiB
 
 
+def test_w8a16_noalloc_host_checks():
+    """The allocation-free W8A16 entry point: the same argument checks, and
+    weights whose dequantised copy exceeds the static scratch (32 MiB) are
+    refused before anything touches the device."""
+    L = nomas.lib()
+    P = ctypes.c_void_p
+
+    def call(x=FAKE, M=100, K=128, w=FAKE, s=FAKE, N=256, y=FAKE):
+        return L.nomas_w8a16_linear_noalloc(P(x), M, K, P(w), P(s), N, P(y), None)
+
+    assert nomas.W8A16_NOALLOC_MAX_BYTES == 32 << 20
+    assert call(K=2048, N=8192 + 256) == nomas.EUNSUPPORTED      # 2048 x 8448 x 2 > 32 MiB
+    assert call(K=8192 + 64, N=2048) == nomas.EUNSUPPORTED
+    assert call(K=4096, N=4352) == nomas.EUNSUPPORTED
+    assert call(M=-1) == nomas.EINVAL
+    assert call(x=None) == nomas.EINVAL
+    assert call(y=None) == nomas.EINVAL
+    assert call(w=None) == nomas.EINVAL
+    assert call(s=None) == nomas.EINVAL
+    assert call(x=FAKE + 2) == nomas.EINVAL
+    assert call(s=FAKE + 2) == nomas.EINVAL
+    assert call(K=96) == nomas.EUNSUPPORTED
+    assert call(N=300) == nomas.EUNSUPPORTED
+
+
 def test_seg_attn_bwd_host_checks():
     """Backward pass: workspace = H x (tiles) x 70,656 bytes, every segment
     starting a new 64-token tile; bad arguments are rejected on the host."""
