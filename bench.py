@@ -80,6 +80,7 @@ class ClockSampler:
         import threading
         self.period = period_s
         self.samples = []
+        self.avg_samples = []
         self._stop = threading.Event()
         self._thread = None
         self._h = None
@@ -98,14 +99,17 @@ class ClockSampler:
         vals = [float(x) for x in xs if isinstance(x, (int, float)) and 0 < x < 10000] if isinstance(xs, list) else []
         if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
             vals = [float(m["current_gfxclk"])]
-        return sum(vals) / len(vals) if vals else None
+        avg = m.get("average_gfxclk_frequency")
+        return (sum(vals) / len(vals) if vals else None), (float(avg) if isinstance(avg, (int, float)) else None)
 
     def _run(self):
         while not self._stop.is_set():
             try:
-                v = self._read()
-                if v:
-                    self.samples.append(v)
+                cur, avg = self._read()
+                if cur:
+                    self.samples.append(cur)
+                if avg:
+                    self.avg_samples.append(avg)
             except Exception:
                 pass
             self._stop.wait(self.period)
@@ -128,7 +132,12 @@ class ClockSampler:
         if not self.samples:
             return None
         xs = sorted(self.samples)
-        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": xs[0], "max_mhz": xs[-1], "samples": len(xs),
+        av = sorted(self.avg_samples)
+        pick = lambda f: xs[min(len(xs) - 1, int(f * len(xs)))]
+        # the median: single readings dip far below the clock the kernel runs
+        # at (down to ~160 MHz), which drags a mean down by up to 25%
+        return {"median_mhz": pick(0.5), "p10_mhz": pick(0.1), "p90_mhz": pick(0.9), "samples": len(xs),
+                "smu_average_mhz": round(sum(av) / len(av), 1) if av else None,
                 "source": "amdsmi gpu metrics current_gfxclks (mean over XCDs), sampled every 10 ms during the "
                           "timed steps"}
 
@@ -212,6 +221,7 @@ def main():
     out_cam = torch.empty_like(q_cam)
     k_rot = torch.empty_like(k_new)
     ws = torch.empty(nomas.seg_attn_workspace([seg], Lc, H), dtype=torch.uint8, device=dev)
+    ws_cam = torch.empty(nomas.cam_xattn_workspace(H, Nc), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -225,7 +235,7 @@ def main():
                        stream=stream)
         if i is not None:
             ev[i][1].record(stream)
-        nomas.cam_xattn(q_cam, cam, w_k, w_v, sm_scale=sm, out=out_cam, stream=stream)
+        nomas.cam_xattn(q_cam, cam, w_k, w_v, sm_scale=sm, out=out_cam, workspace=ws_cam, stream=stream)
         nomas.rope3d(k_new, [seg], out=k_rot, stream=stream)
         nomas.kv_quant_append(k_rot, v_new, kc, vc, ks, vs, Lc, stream=stream)
 
@@ -251,10 +261,10 @@ def main():
         % (ms_step, attn_ms, achieved, 100 * achieved / PEAK_BF16_TFLOPS))
     if clk:
         # dense BF16 MFMA: 256 CUs x 4096 FLOP per clock at the measured clock
-        clk["peak_at_clock_tflops"] = round(256 * 4096 * clk["mean_mhz"] * 1e6 / 1e12, 1)
+        clk["peak_at_clock_tflops"] = round(256 * 4096 * clk["median_mhz"] * 1e6 / 1e12, 1)
         clk["frac_at_clock"] = round(achieved / clk["peak_at_clock_tflops"], 4)
-        log("shader clock %.0f MHz (%d samples): %.1f%% of the peak at that clock"
-            % (clk["mean_mhz"], clk["samples"], 100 * clk["frac_at_clock"]))
+        log("shader clock %.0f MHz (median of %d samples, p10 %.0f, p90 %.0f): %.1f%% of the peak at that clock"
+            % (clk["median_mhz"], clk["samples"], clk["p10_mhz"], clk["p90_mhz"], 100 * clk["frac_at_clock"]))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -489,7 +499,8 @@ def workloads(only=None, cpu=True):
             ws = torch.empty(nomas.seg_attn_workspace([seg], length, H), dtype=torch.uint8, device=dev)
             ms_a = timed(lambda: nomas.seg_attn(q, k, v, [seg], *cache, cache_len=length, sm_scale=sm, out=out,
                                                 workspace=ws, stream=stream), 5)
-            ms_c = timed(lambda: nomas.cam_xattn(qc, cam, wk, wv, sm_scale=sm, out=oc, stream=stream), 5)
+            wsc = torch.empty(nomas.cam_xattn_workspace(H, cam.shape[0]), dtype=torch.uint8, device=dev)
+            ms_c = timed(lambda: nomas.cam_xattn(qc, cam, wk, wv, sm_scale=sm, out=oc, workspace=wsc, stream=stream), 5)
             ms_r = timed(lambda: nomas.rope3d(k, [seg], out=kr, stream=stream), 5)
             # appending the same rows at the same offset is idempotent
             ms_q = timed(lambda: nomas.kv_quant_append(kr, v, *cache, length, stream=stream), 5)

@@ -323,10 +323,20 @@ int nomas_cam_tokens(const double* c2w, int n_frames, double translation_scale,
  * q: device [Lq][H][128] bf16 (video-token queries).  cam: device [Nc][64]
  * float32.  w_k, w_v: device [64][H*128] bf16.  out: device [Lq][H][128]
  * bf16.  1 <= Nc <= NOMAS_MAX_CAM.
+ * workspace: device scratch of at least nomas_cam_xattn_workspace(H, Nc)
+ * bytes, 16-byte aligned, owned by the caller: each head's projected camera
+ * keys and values (Kc, then Vc transposed) as the query stream keeps them
+ * in LDS, written by the call and read by its second kernel (52,736 bytes
+ * per head for 65..96 camera tokens); two calls in flight must not share one.
+ * Too small or NULL: NOMAS_EINVAL (Lq = 0 needs none).
  */
 int nomas_cam_xattn(const nomas_bf16* q, int64_t Lq, int H, const float* cam, int Nc,
                     const nomas_bf16* w_k, const nomas_bf16* w_v, float sm_scale,
-                    nomas_bf16* out, void* stream);
+                    nomas_bf16* out, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes nomas_cam_xattn needs for H heads and Nc camera tokens, or
+ * a negative error code.  Host only. */
+int64_t nomas_cam_xattn_workspace(int H, int Nc);
 
 /*
  * Host copy of the library's float32 RoPE table for one axis (0 = t, 1 = h,

@@ -28,7 +28,8 @@ SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg
            "nomas_seg_attn_sel", "nomas_seg_attn_sel_workspace", "nomas_gqa_attn", "nomas_gqa_attn_workspace",
            "nomas_seg_attn_bwd", "nomas_seg_attn_bwd_workspace",
            "nomas_w8a16_linear", "nomas_w8a16_linear_workspace", "nomas_w8a16_linear_noalloc",
-           "nomas_cam_tokens", "nomas_cam_xattn", "nomas_rope_table", "nomas_strerror", "nomas_version")
+           "nomas_cam_tokens", "nomas_cam_xattn", "nomas_cam_xattn_workspace", "nomas_rope_table", "nomas_strerror",
+           "nomas_version")
 
 
 class NomasError(RuntimeError):
@@ -79,7 +80,9 @@ def lib() -> ctypes.CDLL:
         L.nomas_w8a16_linear_workspace.restype = _I64
         L.nomas_w8a16_linear_noalloc.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P]
         L.nomas_cam_tokens.argtypes = [_P, _I, _D, _D, _P]
-        L.nomas_cam_xattn.argtypes = [_P, _I64, _I, _P, _I, _P, _P, _F, _P, _P]
+        L.nomas_cam_xattn.argtypes = [_P, _I64, _I, _P, _I, _P, _P, _F, _P, _P, _I64, _P]
+        L.nomas_cam_xattn_workspace.argtypes = [_I, _I]
+        L.nomas_cam_xattn_workspace.restype = _I64
         L.nomas_rope_table.argtypes = [_I, _I, _P, _P]
         L.nomas_strerror.argtypes = [_I]
         L.nomas_strerror.restype = ctypes.c_char_p
@@ -424,8 +427,18 @@ def cam_tokens(c2w, translation_scale: float = 1.0, rotation_scale: float = 2.5)
     return out
 
 
-def cam_xattn(q, cam, w_k, w_v, sm_scale: float = SM_SCALE, out=None, stream=None):
-    """Camera cross-attention of q [Lq][H][128] over cam [Nc][64] (float32, device)."""
+def cam_xattn_workspace(H: int, Nc: int) -> int:
+    """Bytes of device workspace cam_xattn needs (host only)."""
+    nbytes = lib().nomas_cam_xattn_workspace(int(H), int(Nc))
+    if nbytes < 0:
+        raise NomasError(int(nbytes), "nomas_cam_xattn_workspace")
+    return int(nbytes)
+
+
+def cam_xattn(q, cam, w_k, w_v, sm_scale: float = SM_SCALE, out=None, workspace=None, stream=None):
+    """Camera cross-attention of q [Lq][H][128] over cam [Nc][64] (float32,
+    device).  workspace: a device uint8 tensor of at least
+    cam_xattn_workspace(H, Nc) bytes, allocated here when not given."""
     import torch
     Lq, H = q.shape[0], q.shape[1]
     _dev(q, "q", (Lq, H, HEAD_DIM))
@@ -437,8 +450,9 @@ def cam_xattn(q, cam, w_k, w_v, sm_scale: float = SM_SCALE, out=None, stream=Non
         with _alloc_on(stream):
             out = torch.empty_like(q)
     _dev(out, "out", q.shape)
+    workspace = _workspace(cam_xattn_workspace(H, Nc), q.device, workspace, stream)
     _check(lib().nomas_cam_xattn(_ptr(q), Lq, H, _ptr(cam), Nc, _ptr(w_k), _ptr(w_v), float(sm_scale),
-                                 _ptr(out), _stream(stream)), "nomas_cam_xattn")
+                                 _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)), "nomas_cam_xattn")
     return out
 
 

@@ -29,7 +29,8 @@ int launch_seg_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         float* dq, float* dk, float* dv, void* workspace, const RopeTables& rt, hipStream_t stream);
 int64_t seg_attn_bwd_workspace_bytes(const SegTable& st, int H);
 int launch_cam_xattn(const uint16_t* q, int64_t Lq, int H, const float* cam, int Nc, const uint16_t* wk,
-                     const uint16_t* wv, float sm_scale, uint16_t* out, hipStream_t stream);
+                     const uint16_t* wv, float sm_scale, uint16_t* out, void* workspace, hipStream_t stream);
+int64_t cam_xattn_workspace_bytes(int H, int Nc);
 }  // namespace nomas
 
 using namespace nomas;
@@ -388,14 +389,22 @@ int nomas_cam_tokens(const double* c2w, int n_frames, double translation_scale, 
     return NOMAS_OK;
 }
 
+int64_t nomas_cam_xattn_workspace(int H, int Nc) {
+    if (H < 1 || Nc < 1) return NOMAS_EINVAL;
+    if (H > kMaxHeads || Nc > NOMAS_MAX_CAM) return NOMAS_EUNSUPPORTED;
+    return cam_xattn_workspace_bytes(H, Nc);
+}
+
 int nomas_cam_xattn(const nomas_bf16* q, int64_t Lq, int H, const float* cam, int Nc, const nomas_bf16* w_k,
-                    const nomas_bf16* w_v, float sm_scale, nomas_bf16* out, void* stream) {
+                    const nomas_bf16* w_v, float sm_scale, nomas_bf16* out, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
     if (Lq < 0 || H < 1 || Nc < 1 || !finite_pos(sm_scale)) return NOMAS_EINVAL;
     if (H > kMaxHeads || Lq > kMaxTokens || Nc > NOMAS_MAX_CAM) return NOMAS_EUNSUPPORTED;
     if (Lq == 0) return NOMAS_OK;
     if (!q || !cam || !w_k || !w_v || !out) return NOMAS_EINVAL;
     if (!al16(q) || !al16(cam) || !al16(w_k) || !al16(w_v) || !al16(out)) return NOMAS_EINVAL;
-    return launch_cam_xattn(q, Lq, H, cam, Nc, w_k, w_v, sm_scale, out, (hipStream_t)stream);
+    if (!workspace || !al16(workspace) || workspace_bytes < cam_xattn_workspace_bytes(H, Nc)) return NOMAS_EINVAL;
+    return launch_cam_xattn(q, Lq, H, cam, Nc, w_k, w_v, sm_scale, out, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

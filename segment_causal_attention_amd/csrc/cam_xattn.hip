@@ -8,15 +8,24 @@
 //   out_i = softmax_n(sm_scale <q_i, Kc_n>) . Vc_n                   (all n < Nc)
 //
 // HBM-bound: every query row is read once and its output written once; the
-// scores need only Nc <= 128 keys.  A workgroup (8 waves) owns one head and
-// 2048 query rows.  Its prologue builds Kc ([key][d]) and Vc^T ([d][key],
-// keys permuted per 16 as in the attention kernel) in LDS with MFMA:
-//   Kc^T (d x keys) = Wk_h^T (d x 64) . bf16(cam)^T (64 x keys).
-// Each wave then streams 32-query blocks: S^T = Kc . Q^T and O^T = Vc^T . P^T
-// on v_mfma_f32_32x32x16_bf16 with the query as the accumulator lane, an
-// online softmax over 32-key blocks of camera tokens (so registers do not grow
-// with Nc), and the next block's Q already in flight while the current one is
-// computed.
+// scores need only Nc <= 128 keys.  Two kernels.
+//  - cam_proj_kernel, one workgroup per head, builds the head's image in the
+//    caller's workspace: Kc ([key][d]) then Vc^T ([d][key], keys permuted
+//    per 16 as in the attention kernel), laid out byte for byte as the
+//    stream kernel keeps them in LDS, keys past Nc zero.  The projections run
+//    on MFMA, Kc^T (d x keys) = Wk_h^T (d x 64) . bf16(cam)^T (64 x keys),
+//    through a transposed copy of the head's weights in LDS.
+//  - cam_xattn_kernel streams the queries: a workgroup (8 waves) owns 256
+//    rows of one head, one 32-row block per wave, and the grid takes the
+//    heads of a row range next to one another, so the workgroups in flight
+//    read whole 4 KB token rows ([L][H][128]) rather than one head's 256 B
+//    slices 4 KB apart.  Each wave issues its query loads before the head's
+//    image is copied from L2 into LDS, then S^T = Kc . Q^T and
+//    O^T = Vc^T . P^T on v_mfma_f32_32x32x16_bf16 with the query as the
+//    accumulator lane.  All Nc scores of a row fit in registers, so the
+//    softmax takes the exact row maximum first (no running rescale); O^T is
+//    formed and stored in two halves of 64 channels (86 VGPRs at 72 camera
+//    tokens, five waves per SIMD).
 #include "common.hpp"
 
 namespace nomas {
@@ -26,11 +35,15 @@ typedef float cf32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t cu32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CAM_WAVES = 8;
-constexpr int CAM_ROWS = 2048;              // query rows per workgroup
+constexpr int CAM_ROWS = 32 * CAM_WAVES;    // query rows per stream workgroup: one 32-row block per wave
 constexpr int CAM_MAXK = NOMAS_MAX_CAM;     // 128 keys at most
 constexpr int CKSTR = D + 8;                // Kc row stride (bf16)
-constexpr int CVSTR = CAM_MAXK + 8;         // Vc^T row stride (bf16)
 constexpr int CWSTR = 64 + 8;               // W^T row stride (bf16)
+
+// Vc^T row stride (bf16) for nkb 32-key blocks, and the bf16 elements of one
+// head's image: Kc rows, then Vc^T rows
+__host__ __device__ constexpr int cam_vstr(int nkb) { return 32 * nkb + 8; }
+__host__ __device__ constexpr int cam_img_elems(int nkb) { return 32 * nkb * CKSTR + D * cam_vstr(nkb); }
 
 __device__ __forceinline__ int cvperm(int k) {
     int w = k & 15;
@@ -38,24 +51,27 @@ __device__ __forceinline__ int cvperm(int k) {
     return (k & ~15) + p;
 }
 
+// ---------------------------------------------------------------------------
+// projections: one workgroup per head
+
 template <int NKB>
-__global__ __launch_bounds__(512) void cam_xattn_kernel(const uint16_t* __restrict__ q, int64_t Lq, int H,
-                                                        const float* __restrict__ cam, int Nc,
-                                                        const uint16_t* __restrict__ wk,
-                                                        const uint16_t* __restrict__ wv, float scale_log2,
-                                                        uint16_t* __restrict__ out, int nblk) {
-    __shared__ __attribute__((aligned(16))) uint16_t Kc[CAM_MAXK * CKSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * CVSTR];
+__global__ __launch_bounds__(512) void cam_proj_kernel(int H, const float* __restrict__ cam, int Nc,
+                                                       const uint16_t* __restrict__ wk,
+                                                       const uint16_t* __restrict__ wv, uint16_t* __restrict__ imgs) {
+    constexpr int IMG = cam_img_elems(NKB);
+    constexpr int CVSTR = cam_vstr(NKB);
+    __shared__ __attribute__((aligned(16))) uint16_t img[IMG];
     __shared__ __attribute__((aligned(16))) uint16_t Wt[D * CWSTR];
+    uint16_t* Kc = img;
+    uint16_t* Vt = img + 32 * NKB * CKSTR;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
-    const int head = blockIdx.x / nblk;
-    const int64_t rbeg = (int64_t)(blockIdx.x - head * nblk) * CAM_ROWS;
-    const int64_t rend = min(rbeg + CAM_ROWS, Lq);
+    const int head = blockIdx.x;
+    for (int i = tid; i < IMG / 8; i += 512) reinterpret_cast<uint4*>(img)[i] = make_uint4(0, 0, 0, 0);
 
-    // ---- projections: K first, then V, through the transposed weight tile
+    // K first, then V, through the transposed weight tile
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const uint16_t* W = which ? wv : wk;
@@ -109,110 +125,146 @@ __global__ __launch_bounds__(512) void cam_xattn_kernel(const uint16_t* __restri
         }
         __syncthreads();
     }
+    uint4* dst = reinterpret_cast<uint4*>(imgs + (int64_t)head * IMG);
+    for (int i = tid; i < IMG / 8; i += 512) dst[i] = reinterpret_cast<const uint4*>(img)[i];
+}
 
-    // ---- stream 32-query blocks
-    const int64_t nrows = rend - rbeg;
-    const int nqb = (int)((nrows + 31) / 32);
-    uint4 qn[8];
-    auto load_q = [&](int b, uint4 (&dst)[8]) {
-        const int64_t row = rbeg + 32 * b + l32;
-        const uint4* src = reinterpret_cast<const uint4*>(q + (row * H + head) * D);
-        const bool ok = row < rend;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) dst[kk] = ok ? src[2 * kk + g] : make_uint4(0, 0, 0, 0);
-    };
-    int b = wave;
-    if (b < nqb) load_q(b, qn);
-    for (; b < nqb; b += CAM_WAVES) {
-        // keep the Kc / Vc^T operand reads inside the loop (re-read from LDS
-        // per block) instead of letting them be hoisted into registers
-        __asm__ volatile("" ::: "memory");
-        cbf16x8 qf[8];
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qf[kk] = __builtin_bit_cast(cbf16x8, cu32x4{qn[kk].x, qn[kk].y, qn[kk].z, qn[kk].w});
-        if (b + CAM_WAVES < nqb) load_q(b + CAM_WAVES, qn);
+// ---------------------------------------------------------------------------
+// query stream: one workgroup = 256 rows of one head, one 32-row block per wave
 
-        // online softmax over the 32-key blocks of the camera tokens
-        cf32x16 o[4];
+// One 32-query block against the image in LDS: S^T for every 32-key block
+// (lane = query l32, register r of block kb = key 32kb + 8(r/4) + 4g + r%4),
+// the exact row maximum, probabilities, O^T = Vc^T . P^T in two halves of 64
+// channels, each normalised and stored as soon as it is done.
+template <int NKB>
+__device__ __forceinline__ void cam_block(const uint4 (&qn)[8], const uint16_t* Kc, const uint16_t* Vt, int Nc,
+                                          float scale_log2, int g, int l32, uint16_t* dst, bool ok) {
+    constexpr int CVSTR = cam_vstr(NKB);
+    cf32x16 s[NKB];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-        float m = -INFINITY, lsum = 0.0f;
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const cbf16x8 qf = __builtin_bit_cast(cbf16x8, cu32x4{qn[kk].x, qn[kk].y, qn[kk].z, qn[kk].w});
+            const cbf16x8 ka = *reinterpret_cast<const cbf16x8*>(Kc + (32 * kb + l32) * CKSTR + 16 * kk + 8 * g);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf, s[kb], 0, 0, 0);
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= Nc) s[kb][r] = -INFINITY;
+            mx = fmaxf(mx, s[kb][r]);
+        }
+    const float nm = -half_max(mx) * scale_log2;
+    // probabilities as bf16 pairs; row sum of the fp32 values
+    uint32_t pk[NKB][8];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], scale_log2, nm));
+            lsum += p0 + p1;
+            pk[kb][r >> 1] = pack_bf16(p0, p1);
+        }
+    const float inv = 1.0f / half_sum(lsum);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        cf32x16 o[2];
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[d2][r] = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            cf32x16 s;
+            const cbf16x8 p0 = __builtin_bit_cast(cbf16x8, cu32x4{pk[kb][0], pk[kb][1], pk[kb][2], pk[kb][3]});
+            const cbf16x8 p1 = __builtin_bit_cast(cbf16x8, cu32x4{pk[kb][4], pk[kb][5], pk[kb][6], pk[kb][7]});
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const cbf16x8 ka = *reinterpret_cast<const cbf16x8*>(Kc + (32 * kb + l32) * CKSTR + 16 * kk + 8 * g);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s, 0, 0, 0);
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (key >= Nc) s[r] = -INFINITY;
-                mx = fmaxf(mx, s[r]);
-            }
-            mx = half_max(mx);
-            const float mn = mx * scale_log2;
-            if (__any(mn > m + 8.0f)) {
-                const float mnew = fmaxf(m, mn);
-                const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-                m = mnew;
-            }
-            const float nm = -m;
-            uint32_t pk[8];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, nm));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], scale_log2, nm));
-                lsum += p0 + p1;
-                pk[r >> 1] = pack_bf16(p0, p1);
-            }
-            const cbf16x8 p0 = __builtin_bit_cast(cbf16x8, cu32x4{pk[0], pk[1], pk[2], pk[3]});
-            const cbf16x8 p1 = __builtin_bit_cast(cbf16x8, cu32x4{pk[4], pk[5], pk[6], pk[7]});
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const uint16_t* vrow = Vt + (32 * db + l32) * CVSTR + 32 * kb + 8 * g;
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const cbf16x8*>(vrow), p0, o[db], 0, 0, 0);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const cbf16x8*>(vrow + 16), p1, o[db], 0, 0, 0);
+            for (int d2 = 0; d2 < 2; ++d2) {
+                const uint16_t* vrow = Vt + (32 * (2 * half + d2) + l32) * CVSTR + 32 * kb + 8 * g;
+                o[d2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const cbf16x8*>(vrow), p0, o[d2], 0, 0, 0);
+                o[d2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const cbf16x8*>(vrow + 16), p1, o[d2], 0, 0, 0);
             }
         }
-        lsum = half_sum(lsum);
-        const float inv = 1.0f / lsum;
-        const int64_t row = rbeg + 32 * b + l32;
-        if (row < rend) {
-            uint16_t* dst = out + (row * H + head) * D;
+        if (ok) {
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<uint2*>(dst + 32 * db + 8 * i + 4 * g) =
-                        make_uint2(pack_bf16(o[db][4 * i] * inv, o[db][4 * i + 1] * inv),
-                                   pack_bf16(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv));
+                    *reinterpret_cast<uint2*>(dst + 32 * (2 * half + d2) + 8 * i + 4 * g) =
+                        make_uint2(pack_bf16(o[d2][4 * i] * inv, o[d2][4 * i + 1] * inv),
+                                   pack_bf16(o[d2][4 * i + 2] * inv, o[d2][4 * i + 3] * inv));
         }
     }
 }
 
-int launch_cam_xattn(const uint16_t* q, int64_t Lq, int H, const float* cam, int Nc, const uint16_t* wk,
-                     const uint16_t* wv, float sm_scale, uint16_t* out, hipStream_t stream) {
-    const int nblk = (int)((Lq + CAM_ROWS - 1) / CAM_ROWS);
-    const dim3 grid((unsigned)((int64_t)nblk * H)), block(512);
-    const float c = (float)((double)sm_scale * 1.4426950408889634);
+template <int NKB>
+__global__ __launch_bounds__(512) void cam_xattn_kernel(const uint16_t* __restrict__ q, int64_t Lq, int H,
+                                                        int Nc, const uint16_t* __restrict__ imgs,
+                                                        float scale_log2, uint16_t* __restrict__ out) {
+    constexpr int IMG = cam_img_elems(NKB);
+    constexpr int CHUNKS = IMG / 8;                       // 16-byte chunks of the image
+    constexpr int CPT = (CHUNKS + 511) / 512;             // chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t img[IMG];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    // row range first, head fastest
+    const int rblk = blockIdx.x / H;
+    const int head = blockIdx.x - rblk * H;
+    // this lane's query row (channels 16kk + 8g .. +8), in flight first
+    const int64_t row = (int64_t)rblk * CAM_ROWS + 32 * wave + l32;
+    const bool ok = row < Lq;
+    uint4 qn[8];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(q + (row * H + head) * D);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qn[kk] = ok ? src[2 * kk + g] : make_uint4(0, 0, 0, 0);
+    }
+    // the head's image, from L2 into LDS
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(imgs + (int64_t)head * IMG);
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int i = tid + 512 * k;
+            if (i < CHUNKS) reinterpret_cast<uint4*>(img)[i] = src[i];
+        }
+    }
+    __syncthreads();
+    cam_block<NKB>(qn, img, img + 32 * NKB * CKSTR, Nc, scale_log2, g, l32, out + (row * H + head) * D, ok);
+}
+
+int64_t cam_xattn_workspace_bytes(int H, int Nc) {
     const int nkb = (Nc + 31) / 32;
-    switch (nkb) {
-        case 1: hipLaunchKernelGGL(cam_xattn_kernel<1>, grid, block, 0, stream, q, Lq, H, cam, Nc, wk, wv, c, out, nblk); break;
-        case 2: hipLaunchKernelGGL(cam_xattn_kernel<2>, grid, block, 0, stream, q, Lq, H, cam, Nc, wk, wv, c, out, nblk); break;
-        case 3: hipLaunchKernelGGL(cam_xattn_kernel<3>, grid, block, 0, stream, q, Lq, H, cam, Nc, wk, wv, c, out, nblk); break;
-        case 4: hipLaunchKernelGGL(cam_xattn_kernel<4>, grid, block, 0, stream, q, Lq, H, cam, Nc, wk, wv, c, out, nblk); break;
+    return (int64_t)H * cam_img_elems(nkb) * 2;
+}
+
+template <int NKB>
+static void launch_cam(const uint16_t* q, int64_t Lq, int H, const float* cam, int Nc, const uint16_t* wk,
+                       const uint16_t* wv, float c, uint16_t* out, uint16_t* imgs, hipStream_t stream) {
+    hipLaunchKernelGGL(cam_proj_kernel<NKB>, dim3((unsigned)H), dim3(512), 0, stream, H, cam, Nc, wk, wv, imgs);
+    const int64_t nrb = (Lq + CAM_ROWS - 1) / CAM_ROWS;
+    hipLaunchKernelGGL(cam_xattn_kernel<NKB>, dim3((unsigned)(nrb * H)), dim3(512), 0, stream, q, Lq, H, Nc, imgs, c,
+                       out);
+}
+
+int launch_cam_xattn(const uint16_t* q, int64_t Lq, int H, const float* cam, int Nc, const uint16_t* wk,
+                     const uint16_t* wv, float sm_scale, uint16_t* out, void* workspace, hipStream_t stream) {
+    const float c = (float)((double)sm_scale * 1.4426950408889634);
+    uint16_t* imgs = static_cast<uint16_t*>(workspace);
+    switch ((Nc + 31) / 32) {
+        case 1: launch_cam<1>(q, Lq, H, cam, Nc, wk, wv, c, out, imgs, stream); break;
+        case 2: launch_cam<2>(q, Lq, H, cam, Nc, wk, wv, c, out, imgs, stream); break;
+        case 3: launch_cam<3>(q, Lq, H, cam, Nc, wk, wv, c, out, imgs, stream); break;
+        case 4: launch_cam<4>(q, Lq, H, cam, Nc, wk, wv, c, out, imgs, stream); break;
         default: return NOMAS_EUNSUPPORTED;
     }
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;

@@ -219,9 +219,13 @@ void check_rejected_calls() {
     EXPECT(nomas_gqa_attn(F, F, F, 100, 4, 3, 0.088f, F, nullptr, FAKE, 1 << 30, nullptr) == NOMAS_EINVAL);
     EXPECT(nomas_w8a16_linear(F, 10, 96, C, S, 256, F, FAKE, 1 << 20, nullptr) == NOMAS_EUNSUPPORTED);
     EXPECT(nomas_w8a16_linear(F, 10, 128, C, S, 256, F, FAKE, 128 * 256 * 2 - 1, nullptr) == NOMAS_EINVAL);
-    EXPECT(nomas_cam_xattn(F, 10, 2, S, NOMAS_MAX_CAM + 1, F, F, 0.088f, F, nullptr) == NOMAS_EUNSUPPORTED);
-    EXPECT(nomas_cam_xattn(F, 10, 2, S, 0, F, F, 0.088f, F, nullptr) == NOMAS_EINVAL);
-    EXPECT(nomas_cam_xattn(F, 0, 2, S, 4, F, F, 0.088f, F, nullptr) == NOMAS_OK);     // nothing to do
+    const int64_t cw = nomas_cam_xattn_workspace(2, 72);
+    EXPECT(cw > 0 && nomas_cam_xattn_workspace(2, NOMAS_MAX_CAM + 1) == NOMAS_EUNSUPPORTED);
+    EXPECT(nomas_cam_xattn(F, 10, 2, S, NOMAS_MAX_CAM + 1, F, F, 0.088f, F, FAKE, cw, nullptr) == NOMAS_EUNSUPPORTED);
+    EXPECT(nomas_cam_xattn(F, 10, 2, S, 0, F, F, 0.088f, F, FAKE, cw, nullptr) == NOMAS_EINVAL);
+    EXPECT(nomas_cam_xattn(F, 10, 2, S, 72, F, F, 0.088f, F, FAKE, cw - 1, nullptr) == NOMAS_EINVAL);
+    EXPECT(nomas_cam_xattn(F, 10, 2, S, 72, F, F, 0.088f, F, nullptr, cw, nullptr) == NOMAS_EINVAL);
+    EXPECT(nomas_cam_xattn(F, 0, 2, S, 4, F, F, 0.088f, F, nullptr, 0, nullptr) == NOMAS_OK);     // nothing to do
 }
 
 }  // namespace

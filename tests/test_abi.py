@@ -126,11 +126,27 @@ def test_rope3d_and_cam_xattn_host_checks():
     sa, n = segs((16, 0, 2, 4, 6))
     assert L.nomas_rope3d(P(None), P(FAKE), sa, n, 2, None) == nomas.EINVAL
     assert L.nomas_rope3d(P(FAKE), P(FAKE), sa, n, 0, None) == nomas.EINVAL
-    assert L.nomas_cam_xattn(P(FAKE), 10, 2, P(FAKE), 0, P(FAKE), P(FAKE), 0.1, P(FAKE), None) == nomas.EINVAL
-    assert L.nomas_cam_xattn(P(FAKE), 10, 2, P(FAKE), nomas.MAX_CAM + 1, P(FAKE), P(FAKE), 0.1, P(FAKE),
-                             None) == nomas.EUNSUPPORTED
-    assert L.nomas_cam_xattn(P(FAKE), 10, 2, P(None), 5, P(FAKE), P(FAKE), 0.1, P(FAKE), None) == nomas.EINVAL
-    assert L.nomas_cam_xattn(P(FAKE), 0, 2, P(FAKE), 5, P(FAKE), P(FAKE), 0.1, P(FAKE), None) == nomas.OK
+    W = 1 << 30
+
+    def cam(Lq=10, H=2, c=FAKE, Nc=5, ws=FAKE, wsb=W):
+        return L.nomas_cam_xattn(P(FAKE), Lq, H, P(c), Nc, P(FAKE), P(FAKE), 0.1, P(FAKE), P(ws), wsb, None)
+
+    assert cam(Nc=0) == nomas.EINVAL
+    assert cam(Nc=nomas.MAX_CAM + 1) == nomas.EUNSUPPORTED
+    assert cam(c=None) == nomas.EINVAL
+    assert cam(Lq=0, ws=None, wsb=0) == nomas.OK                  # nothing to do, no workspace needed
+    assert cam(ws=None) == nomas.EINVAL
+    assert cam(ws=FAKE + 8) == nomas.EINVAL
+    need = L.nomas_cam_xattn_workspace(2, 5)
+    assert cam(wsb=need - 1) == nomas.EINVAL
+    # per head: Kc rows (32 per started block of 32 camera tokens, 136 bf16 each), then the 128 Vc^T
+    # rows of 32 bf16 per key block + 8
+    for H, Nc in ((2, 5), (16, 72), (3, 128), (1, 33)):
+        nkb = (Nc + 31) // 32
+        assert L.nomas_cam_xattn_workspace(H, Nc) == H * (32 * nkb * 136 + 128 * (32 * nkb + 8)) * 2
+    assert L.nomas_cam_xattn_workspace(0, 5) == nomas.EINVAL
+    assert L.nomas_cam_xattn_workspace(2, 0) == nomas.EINVAL
+    assert L.nomas_cam_xattn_workspace(2, nomas.MAX_CAM + 1) == nomas.EUNSUPPORTED
 
 
 @pytest.mark.parametrize("axis,npos", [(0, 400), (1, 22), (2, 40), (1, 1024)])
