@@ -38,8 +38,11 @@
  *      NOMAS_EUNSUPPORTED a size outside the library's fixed limits
  *      NOMAS_EHIP         a HIP runtime call or launch failed
  *    A fault inside a kernel surfaces at the caller's next synchronisation.
- *  - The only memory the library owns is a RoPE cos/sin table per device,
- *    built on first use and kept until the process ends.
+ *  - The only device memory the library owns is static: a RoPE cos/sin table
+ *    per device (uploaded on first use) and the scratch array of
+ *    nomas_w8a16_linear_noalloc.  Both belong to the loaded code object and
+ *    are released with it when the process ends; nomas_shutdown() drops the
+ *    host state that refers to them.
  *  - Token layout of a segment: its n_text text tokens first, then its
  *    T*Hg*Wg video tokens in (t, h, w) row-major order, t in [t0, t0+T).
  *    Text tokens are not rotated; video token (t, h, w) uses t as the
@@ -344,6 +347,18 @@ int64_t nomas_cam_xattn_workspace(int H, int Nc);
  * fl32(cos(p * 256^(-2i/d))).  Needs no GPU.
  */
 int nomas_rope_table(int axis, int npos, float* cos_out, float* sin_out);
+
+/*
+ * Drops the library's per-device host state: the "RoPE table uploaded" flag
+ * and the cached device addresses of its static arrays, for every device.
+ * The next call on a device uploads the table and looks the addresses up
+ * again.  Call it after resetting a device (hipDeviceReset reloads the code
+ * object, whose static arrays then start empty) or when the library should
+ * hold no state; no device memory is freed (there is none to free) and
+ * work already enqueued is unaffected.  It must not run concurrently with
+ * other calls of the library.  Host only; returns NOMAS_OK.
+ */
+int nomas_shutdown(void);
 
 /* Static description of an error code; never NULL. */
 const char* nomas_strerror(int code);

@@ -29,7 +29,7 @@ SYMBOLS = ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg
            "nomas_seg_attn_bwd", "nomas_seg_attn_bwd_workspace",
            "nomas_w8a16_linear", "nomas_w8a16_linear_workspace", "nomas_w8a16_linear_noalloc",
            "nomas_cam_tokens", "nomas_cam_xattn", "nomas_cam_xattn_workspace", "nomas_rope_table", "nomas_strerror",
-           "nomas_version")
+           "nomas_version", "nomas_shutdown")
 
 
 class NomasError(RuntimeError):
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.nomas_rope_table.argtypes = [_I, _I, _P, _P]
         L.nomas_strerror.argtypes = [_I]
         L.nomas_strerror.restype = ctypes.c_char_p
+        L.nomas_shutdown.argtypes = []
+        L.nomas_shutdown.restype = _I
         L.nomas_version.argtypes = []
         L.nomas_version.restype = ctypes.c_char_p
         for name in ("nomas_rope3d", "nomas_kv_quant_append", "nomas_seg_attn", "nomas_seg_attn_sel", "nomas_gqa_attn",
@@ -104,6 +106,11 @@ def strerror(code: int) -> str:
 
 def version() -> str:
     return lib().nomas_version().decode()
+
+
+def shutdown() -> None:
+    """Drop the library's per-device host state (nomas_shutdown)."""
+    _check(lib().nomas_shutdown(), "nomas_shutdown")
 
 
 def _check(rc: int, where: str):

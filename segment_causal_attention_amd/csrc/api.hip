@@ -24,6 +24,8 @@ int launch_w8a16(const uint16_t* x, int64_t M, int64_t K, const int8_t* codes, c
                  uint16_t* y, void* workspace, hipStream_t stream);
 int64_t w8a16_workspace_bytes(int64_t N, int64_t K);
 int w8a16_scratch(void** out);
+void w8a16_scratch_forget();
+void rope_tables_forget();
 int launch_seg_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                         const float* lse, const uint16_t* dout, const SegTable& st, int Ln, int H, float sm_scale,
                         float* dq, float* dk, float* dv, void* workspace, const RopeTables& rt, hipStream_t stream);
@@ -148,6 +150,12 @@ const char* nomas_strerror(int code) {
 }
 
 const char* nomas_version(void) { return "nomas 0.1 (gfx950)"; }
+
+int nomas_shutdown(void) {
+    rope_tables_forget();
+    w8a16_scratch_forget();
+    return NOMAS_OK;
+}
 
 int nomas_rope_table(int axis, int npos, float* cos_out, float* sin_out) {
     if (axis < 0 || axis > 2 || npos < 0 || !cos_out || !sin_out) return NOMAS_EINVAL;

@@ -51,6 +51,11 @@ bool upload(const T& sym, const void* src, size_t bytes, const void** addr) {
 
 }  // namespace
 
+void rope_tables_forget() {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (int d = 0; d < kMaxDevices; ++d) g_ready[d] = false;
+}
+
 int rope_tables(RopeTables* out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NOMAS_EHIP;

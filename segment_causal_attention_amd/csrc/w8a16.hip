@@ -200,6 +200,11 @@ std::mutex g_scratch_mu;
 void* g_scratch_ptr[kScratchDevices];
 }  // namespace
 
+void w8a16_scratch_forget() {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    for (int d = 0; d < kScratchDevices; ++d) g_scratch_ptr[d] = nullptr;
+}
+
 int w8a16_scratch(void** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return NOMAS_EHIP;

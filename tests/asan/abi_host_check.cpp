@@ -61,6 +61,7 @@ void check_messages() {
         EXPECT(s != nullptr && std::strlen(s) > 0);
     }
     EXPECT(std::strstr(nomas_version(), "gfx950") != nullptr);
+    EXPECT(nomas_shutdown() == NOMAS_OK && nomas_shutdown() == NOMAS_OK);
 }
 
 void check_rope_table() {

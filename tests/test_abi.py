@@ -43,6 +43,17 @@ def segs(*t):
     return nomas.seg_array(t)
 
 
+def test_shutdown_drops_host_state():
+    """nomas_shutdown needs no GPU, always succeeds and may be repeated; the
+    host-only entry points work after it."""
+    L = nomas.lib()
+    assert L.nomas_shutdown() == nomas.OK
+    assert L.nomas_shutdown() == nomas.OK
+    nomas.shutdown()
+    c, s = nomas.rope_table(0, 4)
+    assert c.shape == (4, 8) and abs(float(c[0, 0]) - 1.0) == 0.0
+
+
 def test_seg_attn_host_checks():
     L = nomas.lib()
     sa, n = segs((16, 0, 2, 4, 6))

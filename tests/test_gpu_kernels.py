@@ -394,6 +394,27 @@ def test_seg_attn_on_a_side_stream_without_workspace():
         assert torch.equal(o, ref)
 
 
+def test_calls_after_shutdown_are_bit_identical():
+    """After nomas_shutdown the next call uploads the RoPE tables again and
+    looks up the static scratch again; results are bit-identical."""
+    segs, Lc, H = [(16, 3, 2, 5, 7)], 90, 2
+    q, k, v, cache = _edge_inputs(segs, Lc, H)
+    a, la, _ = _run_gpu(q, k, v, segs, cache, Lc, H)
+    r1 = nomas.rope3d(dev16(k), segs)
+    x = dev16(synth.random_bf16(31, (100, 512)))
+    codes = dev(np.random.default_rng(32).integers(-127, 128, size=(256, 512), dtype=np.int8))
+    scale = dev(np.full(256, 0.01, np.float32))
+    y1 = nomas.w8a16_linear_noalloc(x, codes, scale, torch.empty((100, 256), dtype=torch.int16, device="cuda:0"))
+    torch.cuda.synchronize()
+    nomas.shutdown()
+    b, lb, _ = _run_gpu(q, k, v, segs, cache, Lc, H)
+    r2 = nomas.rope3d(dev16(k), segs)
+    y2 = nomas.w8a16_linear_noalloc(x, codes, scale, torch.empty((100, 256), dtype=torch.int16, device="cuda:0"))
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    assert torch.equal(r1, r2) and torch.equal(y1, y2)
+
+
 # ----------------------------------------------------------------------------
 # decoder window attention with grouped KV heads (nomas_gqa_attn)
 
