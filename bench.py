@@ -527,8 +527,8 @@ def workloads(only=None, cpu=True):
                            kv_quant_append=dict(ms=round(ms_q, 4), GBps=gbs(2 * 3 * elems + 2 * 4 * n * H, ms_q)),
                            hbm_peak_GBps=PEAK_HBM_GBS), cpu_b)
             if cpu and t < 4:
-                kr = oracle.bf16_round(oracle.rope3d(oracle.bf16_bits_to_f64(inp["k_new"][:, :1]), [seg]))[:, 0]
-                kq, ksc = oracle.quantise(kr)
+                k_rot_o = oracle.bf16_round(oracle.rope3d(oracle.bf16_bits_to_f64(inp["k_new"][:, :1]), [seg]))[:, 0]
+                kq, ksc = oracle.quantise(k_rot_o)
                 vq, vsc = oracle.quantise(oracle.bf16_bits_to_f64(inp["v_new"][:, 0]))
                 ohead.append((kq, vq, ksc, vsc))
             length = nomas.kv_quant_append(kr, v, *cache, length, stream=stream)
