@@ -40,3 +40,19 @@ def test_committed_traffic_summary_is_well_formed():
         t = json.load(fh)
     assert len(t["kernel_digest"]) == 16
     assert t["hbm_bytes_per_launch"] > 0
+
+
+def test_clock_summary_is_robust_to_dips():
+    """The bench's clock figure is the median of the SMU samples: single
+    readings dip far below the clock a long kernel runs at, and must not pull
+    the reported clock (or the fraction of the peak at that clock) down."""
+    import bench
+    cs = bench.ClockSampler.__new__(bench.ClockSampler)
+    cs._thread, cs._h = None, None
+    cs.samples = [1720.0] * 90 + [157.5] * 12 + [1748.0] * 10
+    cs.avg_samples = []
+    s = cs.stop()
+    assert s["median_mhz"] == 1720.0 and s["samples"] == 112
+    assert s["p10_mhz"] == 157.5 and s["p90_mhz"] == 1720.0     # sorted indices 11 and 100 of 112
+    cs.samples = []
+    assert cs.stop() is None
