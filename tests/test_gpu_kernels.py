@@ -498,3 +498,21 @@ def test_cam_xattn_matches_oracle(Lq, H, Nc):
     if Nc == 1:   # one camera token: every query returns its value vector
         _, Vc = oracle.cam_kv(cam, wk, wv, H)
         np.testing.assert_allclose(got, np.broadcast_to(Vc[0][None], got.shape), rtol=0, atol=1e-2)
+
+
+def test_cam_xattn_workspace_serves_consecutive_calls():
+    """One workspace sized for 128 camera tokens serves calls with 128, then
+    5, then 72 tokens: each call rebuilds the images it reads, so nothing of
+    an earlier call's larger image leaks into a later one."""
+    H, Lq = 2, 600
+    q = synth.random_bf16(311, (Lq, H, 128))
+    wk = synth.random_bf16(312, (64, H * 128), 1 / 8)
+    wv = synth.random_bf16(313, (64, H * 128), 1 / 8)
+    ws = torch.empty(nomas.cam_xattn_workspace(H, 128), dtype=torch.uint8, device="cuda:0")
+    qd, wkd, wvd = dev16(q), dev16(wk), dev16(wv)
+    for Nc in (128, 5, 72):
+        cam = oracle.cam_tokens(synth.camera_path(5, 8 + Nc, 4 * Nc)).astype(np.float32)
+        say("cam_xattn workspace reuse Nc", Nc)
+        out = nomas.cam_xattn(qd, dev(cam), wkd, wvd, sm_scale=SM, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(f64(out), oracle.cam_xattn(q, cam, wk, wv, SM), "cam_xattn reused workspace Nc=%d" % Nc)
