@@ -306,3 +306,15 @@ def random_bf16(seed: int, shape, scale: float = 1.0) -> np.ndarray:
     if scale != 1.0:
         x *= np.float32(scale)
     return to_bf16_bits(x).reshape(shape)
+
+
+def random_int8_cache(seed: int, H: int, L: int):
+    """Seeded INT8 cache contents for edge-case sizes: codes [H][L][128]
+    uniform in [-127, 127] and one positive fp32 scale per (head, token),
+    uniform in [2^-8, 2^-6) (values of the size N(0,1) rows quantise to).
+    Any such codes and scales are a valid cache; drawing them directly
+    avoids quantising millions of rows."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    codes = g.integers(-127, 128, size=(H, L, D), dtype=np.int8)
+    scale = (np.float32(2.0 ** -8) * (1.0 + 3.0 * g.random((H, L), dtype=np.float32))).astype(np.float32)
+    return codes, scale

@@ -252,6 +252,32 @@ def test_five_turns_growing_cache():
     assert length == cap
 
 
+def test_workspace_beyond_4gib():
+    """One head over an 8M-token INT8 cache (8,388,608 cached + 64 new
+    tokens): the tile images take 4.7 GB of workspace, so image addresses pass
+    2^32 bytes, and the call's single query tile runs as key-range parts.
+    All 64 rows against the oracle."""
+    Lc, H = 1 << 23, 1
+    segs = [(16, 5, 1, 4, 12)]                      # 64 new tokens: 16 text + 4 x 12 video
+    say("workspace beyond 4 GiB: cache", Lc, "heads", H)
+    kc, ks = synth.random_int8_cache(401, H, Lc)
+    vc, vs = synth.random_int8_cache(402, H, Lc)
+    q = synth.random_bf16(403, (64, H, 128))
+    k = synth.random_bf16(404, (64, H, 128))
+    v = synth.random_bf16(405, (64, H, 128))
+    need = nomas.seg_attn_workspace(segs, Lc, H)
+    say("workspace bytes", need)
+    assert need > (1 << 32)
+    lse = torch.empty((H, 64), dtype=torch.float32, device="cuda:0")
+    out = nomas.seg_attn(dev16(q), dev16(k), dev16(v), segs, dev(kc), dev(vc), dev(ks), dev(vs), cache_len=Lc,
+                         sm_scale=SM, lse=lse)
+    torch.cuda.synchronize()
+    say("oracle over", Lc + 64, "keys")
+    ref, lref = oracle.seg_attn(q, k, v, segs, kc, vc, ks, vs, Lc, SM)
+    assert_close(f64(out), ref, "8M-token cache, 4.7 GB workspace")
+    np.testing.assert_allclose(lse.cpu().numpy(), lref, rtol=0, atol=2.0 ** -8)
+
+
 def test_decoder_window():
     """One decoder window at 1280x704: 10 latent frames of 4x16x16 tubelets
     (10 x 44 x 80 = 35,200 tokens), 32 query heads over 8 KV heads."""
