@@ -86,6 +86,8 @@ CASES = [
     ("tile-aligned", [(64, 0, 0, 1, 1), (0, 0, 2, 8, 8), (0, 2, 1, 8, 8)], 2),
     # 40 small segments: long segment tables, one workgroup per segment
     ("forty-segments", [(1 + (i % 3), i, 1, 2 + (i % 2), 3) for i in range(40)], 2),
+    # the 64-segment limit
+    ("sixty-four-segments", [(i % 5, i, 1, 3, 2 + (i % 3)) for i in range(64)], 2),
 ]
 
 

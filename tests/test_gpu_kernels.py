@@ -144,6 +144,7 @@ EDGE = [
     ("two-seg-multi-tile", [(5, 0, 1, 3, 4), (40, 1, 3, 10, 9)], 0, 3),
     ("turn-shape-small", [(256, 18, 2, 22, 40)], 1760, 2),
     ("empty-segment-between", [(4, 0, 1, 2, 2), (0, 0, 0, 0, 0), (2, 1, 2, 3, 3)], 64, 2),
+    ("max-segments", [(i % 4, i, 1, 2, 2 + i % 3) for i in range(64)], 50, 2),   # the 64-segment limit
 ]
 
 
@@ -309,6 +310,10 @@ SEL = [
      [[(0, 10)], [], [(5, 77)], [(0, 77)], [(30, 31), (40, 77)]], 0),
     ("two-seg-shared-list", [(5, 0, 1, 3, 4), (40, 1, 3, 10, 9)], 130, 3, [[(3, 90)], [(3, 90)]], 0),
     ("empty-selection", [(7, 3, 2, 5, 9)], 130, 2, [[]], 0),
+    # the limits: 64 ranges in one list, and 64 segments (each with a list of its own: 64 key regions)
+    ("max-ranges", [(7, 3, 2, 5, 9)], 2000, 2, [[(30 * i, 30 * i + 11) for i in range(64)]], 0),
+    ("max-segments-own-lists", [(1 + i % 3, i, 1, 2, 3) for i in range(64)], 700, 2,
+     [[(10 * i, 10 * i + 7 + i % 5)] for i in range(64)], 0),
 ]
 
 
