@@ -142,6 +142,24 @@ class ClockSampler:
                           "timed steps"}
 
 
+def clock_fraction(clk, achieved_tflops):
+    """Adds the dense BF16 MFMA peak at the sampled clock (256 CUs x 4096 FLOP
+    per clock) and the kernel's fraction of it.  A median clock at which the
+    kernel would exceed that peak cannot be the clock it ran at (under a
+    profiler the SMU readings have stayed at an idle ~95 MHz): then both stay
+    None and a note says why."""
+    peak = round(256 * 4096 * clk["median_mhz"] * 1e6 / 1e12, 1)
+    if peak <= 0 or achieved_tflops > peak:
+        clk["peak_at_clock_tflops"] = None
+        clk["frac_at_clock"] = None
+        clk["note"] = ("median reading %.0f MHz is below the clock needed for the measured %.1f TFLOP/s: "
+                       "not the clock the kernel ran at" % (clk["median_mhz"], achieved_tflops))
+    else:
+        clk["peak_at_clock_tflops"] = peak
+        clk["frac_at_clock"] = round(achieved_tflops / peak, 4)
+    return clk
+
+
 def copy_calibration():
     """A plain device copy of a known size, for scaling FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -260,11 +278,11 @@ def main():
     log("step %.3f ms, nomas_seg_attn %.3f ms (%.1f TFLOP/s, %.1f%% of peak)"
         % (ms_step, attn_ms, achieved, 100 * achieved / PEAK_BF16_TFLOPS))
     if clk:
-        # dense BF16 MFMA: 256 CUs x 4096 FLOP per clock at the measured clock
-        clk["peak_at_clock_tflops"] = round(256 * 4096 * clk["median_mhz"] * 1e6 / 1e12, 1)
-        clk["frac_at_clock"] = round(achieved / clk["peak_at_clock_tflops"], 4)
-        log("shader clock %.0f MHz (median of %d samples, p10 %.0f, p90 %.0f): %.1f%% of the peak at that clock"
-            % (clk["median_mhz"], clk["samples"], clk["p10_mhz"], clk["p90_mhz"], 100 * clk["frac_at_clock"]))
+        clock_fraction(clk, achieved)
+        log("shader clock %.0f MHz (median of %d samples, p10 %.0f, p90 %.0f): %s"
+            % (clk["median_mhz"], clk["samples"], clk["p10_mhz"], clk["p90_mhz"],
+               "%.1f%% of the peak at that clock" % (100 * clk["frac_at_clock"]) if clk["frac_at_clock"] is not None
+               else clk["note"]))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -56,3 +56,13 @@ def test_clock_summary_is_robust_to_dips():
     assert s["p10_mhz"] == 157.5 and s["p90_mhz"] == 1720.0     # sorted indices 11 and 100 of 112
     cs.samples = []
     assert cs.stop() is None
+
+
+def test_clock_fraction_rejects_impossible_clock():
+    """A clock at which the measured rate would exceed the MFMA peak is not
+    the clock the kernel ran at; the bench line then gives no fraction."""
+    import bench
+    ok = bench.clock_fraction({"median_mhz": 1720.0}, 1294.3)
+    assert ok["peak_at_clock_tflops"] == 1803.6 and abs(ok["frac_at_clock"] - 1294.3 / 1803.6) < 1e-4
+    bad = bench.clock_fraction({"median_mhz": 95.0}, 1291.5)
+    assert bad["frac_at_clock"] is None and bad["peak_at_clock_tflops"] is None and "95 MHz" in bad["note"]
