@@ -235,6 +235,7 @@ struct AttnArgs {
     int32_t grp;                    // query heads per key/value head (head h reads KV head h / grp)
     int32_t nsplit;                 // key-range parts of a split query tile
     int32_t nmain;                  // blocks [0, nmain): whole query tiles; the rest split into nsplit parts
+    int32_t xcd_runs;               // 1: each of the 8 XCDs takes a contiguous run of units (see below)
     float scale_log2;               // sm_scale * log2(e)
     int32_t tile0[NOMAS_MAX_SEGS + 1];   // first query tile of each new segment
     int32_t order[NOMAS_MAX_SEGS];       // segments in launch order (most keys first)
@@ -421,15 +422,23 @@ __global__ __launch_bounds__(NT) void seg_attn_kernel(const AttnArgs A) {
     // share a key range run side by side.  The segments with the most keys
     // go first (packed calls: the last segment), so that the grid does not
     // end on a few long workgroups.
+    // Workgroup b is dispatched to XCD b % 8.  With xcd_runs, index w of n
+    // equal-work units runs unit (w % 8) * (n / 8) + w / 8, so each XCD walks
+    // a contiguous run of units (about two heads at 16 heads) and its CUs
+    // stream the same head's tile images through its own L2.
+    auto runs = [&](int w, int n) {
+        const int q8 = n >> 3;
+        return (A.xcd_runs && w < 8 * q8) ? (w & 7) * q8 + (w >> 3) : w;
+    };
     int unit, split, parts;
     if ((int)blockIdx.x < A.nmain) {
-        unit = blockIdx.x;
+        unit = runs(blockIdx.x, A.nmain);
         split = 0;
         parts = 1;
     } else {
         const int t = blockIdx.x - A.nmain, r = A.ntq * A.H - A.nmain;
         split = t / r;
-        unit = A.nmain + (t - split * r);
+        unit = A.nmain + (A.nmain > 0 ? t - split * r : runs(t - split * r, r));
         parts = A.nsplit;
     }
     unit = __builtin_amdgcn_readfirstlane(unit);
@@ -895,6 +904,7 @@ int launch_seg_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
     A.grp = H / Hkv;
     A.nsplit = nsplit;
     A.nmain = (int32_t)sp.main;
+    A.xcd_runs = segs.n == 1 ? 1 : 0;       // one segment: every query tile sees the same keys
     A.f0 = split_f0(sp, query_tiles(segs), Ln);
     A.nf = (int64_t)Ln * H - A.f0;
     if (nsplit > 1) {
