@@ -345,8 +345,9 @@ def workloads(only=None, cpu=True):
                   16 heads are split over 8 GPUs (median of 5 calls)
       decoder-window  gqa_attn over one 10-latent-frame decoder window at
                   1280x704 (35,200 tokens, 32 query / 8 KV heads; median of 5)
-      w8a16-qkv, w8a16-ffn-up  INT8-weight linear layers of one 12 s segment
-                  (63,360 x 2048 -> 6144 and -> 8192; median of 10), with the
+      w8a16-qkv, w8a16-ffn-up, w8a16-ffn-down, w8a16-out  INT8-weight linear
+                  layers of one 12 s segment (63,360 x 2048 -> 6144, 2048 -> 8192,
+                  8192 -> 2048, 2048 -> 2048; median of 10), with the
                   dequantisation pass alone and torch's BF16 matmul on the
                   dequantised weights as context
       train-fwd, train-bwd  segment-forcing training: 22 packed 3 s turns
@@ -568,10 +569,11 @@ def workloads(only=None, cpu=True):
         del q, k, v, out, ws
 
     if want("w8a16"):
-        # ---- INT8-weight linear layers of one 12 s segment (63,360 tokens, hidden 2048)
-        for name, N in (("w8a16-qkv", 6144), ("w8a16-ffn-up", 8192)):
+        # ---- INT8-weight linear layers of one 12 s segment (63,360 tokens, hidden 2048, FFN 8192)
+        for name, K, N in (("w8a16-qkv", 2048, 6144), ("w8a16-ffn-up", 2048, 8192), ("w8a16-ffn-down", 8192, 2048),
+                           ("w8a16-out", 2048, 2048)):
             log("workload " + name)
-            M, K = 63360, 2048
+            M = 63360
             x = d16(synth.random_bf16(601, (M, K)))
             g = np.random.default_rng(602)
             codes = torch.from_numpy(g.integers(-127, 128, size=(N, K), dtype=np.int8)).to(dev)

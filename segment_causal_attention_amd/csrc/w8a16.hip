@@ -39,6 +39,7 @@ constexpr int GK = 64;              // K per step
 constexpr int GNT = 512;            // threads (8 waves)
 constexpr int GTILE = GT * GK * 2;  // bytes of one operand tile (32 KB)
 constexpr int GSTAGE = 2 * GTILE;   // x tile then W tile
+constexpr int GGROUP = 8;           // row panels walked together by the tile order
 
 // ---------------------------------------------------------------------------
 // dequantisation: one thread = 16 weights of one output channel
@@ -95,16 +96,21 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * GSTAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
-    // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8).  Tile
+    // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8).  Index
     // t = (b % 8) * ceil(nb / 8) + b / 8 gives each XCD a contiguous run of
-    // tiles, row panel by row panel, so an x panel is read into one XCD's L2.
+    // the tile order, which walks groups of GGROUP row panels column by column:
+    // the ~32 tiles an XCD holds at once span 8 row panels and 4 column panels,
+    // so each K step's x and W slices are fetched into its L2 once for 4 or 8
+    // tiles (12 MB per round at N = 8192, against 33 MB for one row panel).
     const int nb = G.ntm * G.ntn;
     const int per = (nb + 7) / 8;
     const int b = blockIdx.x;
     int tile = (b % 8) * per + b / 8;
     if ((b % 8) >= nb % 8 && nb % 8 != 0) tile -= (b % 8) - nb % 8;     // XCDs past the remainder hold one fewer
-    const int tm = __builtin_amdgcn_readfirstlane(tile / G.ntn);
-    const int tn = __builtin_amdgcn_readfirstlane(tile - tm * G.ntn);
+    const int span = GGROUP * G.ntn, grp = tile / span, fm = grp * GGROUP;
+    const int gm = min(G.ntm - fm, GGROUP), rr = tile - grp * span;     // the last group may hold fewer rows
+    const int tm = __builtin_amdgcn_readfirstlane(fm + rr % gm);
+    const int tn = __builtin_amdgcn_readfirstlane(rr / gm);
     const int m0 = tm * GT, n0 = tn * GT;
     const int wm = 64 * (wave & 3), wn = 128 * (wave >> 2);
     const int nsteps = G.K / GK;
