@@ -12,11 +12,14 @@
 // matrix and vector instructions of a SIMD largely serialise, so weights
 // converted inside the loop would cost MFMA time.
 //
-// GEMM shape.  A workgroup (8 waves, 2 per SIMD) computes a 256 x 256 tile of
-// y; wave w owns rows 64 (w % 4) .. +64 and columns 128 (w / 4) .. +128 as
-// 2 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (A = x rows, B = W rows, both
-// k-contiguous).  K advances in steps of 64: the step's x tile (256 rows) and
-// W tile (256 rows), 128 bytes per row, are copied into LDS by buffer-to-LDS
+// GEMM shape.  A workgroup (8 waves, 2 per SIMD) computes a 384 x 256 tile of
+// y; wave w owns rows 96 (w % 4) .. +96 and columns 128 (w / 4) .. +128 as
+// 3 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (A = x rows, B = W rows, both
+// k-contiguous; 234 VGPRs).  Seven 16-byte fragment reads from LDS feed twelve
+// products, against six for eight with 64 x 128 wave tiles: the LDS bytes per
+// FLOP that bound a power-limited clock fall by a fifth.  K advances in steps
+// of 64: the step's x tile (384 rows) and W tile (256 rows), 128 bytes per
+// row, are copied into LDS (2 stages x 80 KB) by buffer-to-LDS
 // DMA, 16-byte chunk c of row r landing at chunk c ^ ((r / 2) % 8) of the
 // row.  A row is 128 bytes, half of the 64 four-byte banks, so rows 2i and
 // 2i+1 cover the two halves; the swizzle by r / 2 spreads the 16 rows that a
@@ -34,11 +37,13 @@ typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
 typedef float gf32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t gu32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GT = 256;             // tile rows (x) and columns (W rows) per workgroup
+constexpr int GT = 256;             // tile columns (W rows) per workgroup
+constexpr int GTM = 384;            // tile rows (x) per workgroup
 constexpr int GK = 64;              // K per step
 constexpr int GNT = 512;            // threads (8 waves)
 constexpr int GTILE = GT * GK * 2;  // bytes of one operand tile (32 KB)
-constexpr int GSTAGE = 2 * GTILE;   // x tile then W tile
+constexpr int GTILEX = GTM * GK * 2; // bytes of the x tile (48 KB)
+constexpr int GSTAGE = GTILEX + GTILE;   // x tile then W tile
 constexpr int GGROUP = 8;           // row panels walked together by the tile order
 
 // ---------------------------------------------------------------------------
@@ -101,7 +106,8 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     // the tile order, which walks groups of GGROUP row panels column by column:
     // the ~32 tiles an XCD holds at once span 8 row panels and 4 column panels,
     // so each K step's x and W slices are fetched into its L2 once for 4 or 8
-    // tiles (12 MB per round at N = 8192, against 33 MB for one row panel).
+    // tiles (8 x and 4 W panels per round, against 1 x and 32 W panels when an
+    // XCD walks one row panel at a time).
     const int nb = G.ntm * G.ntn;
     const int per = (nb + 7) / 8;
     const int b = blockIdx.x;
@@ -111,8 +117,8 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     const int gm = min(G.ntm - fm, GGROUP), rr = tile - grp * span;     // the last group may hold fewer rows
     const int tm = __builtin_amdgcn_readfirstlane(fm + rr % gm);
     const int tn = __builtin_amdgcn_readfirstlane(rr / gm);
-    const int m0 = tm * GT, n0 = tn * GT;
-    const int wm = 64 * (wave & 3), wn = 128 * (wave >> 2);
+    const int m0 = tm * GTM, n0 = tn * GT;
+    const int wm = 96 * (wave & 3), wn = 128 * (wave >> 2);
     const int nsteps = G.K / GK;
     const uint32_t rowb = (uint32_t)G.K * 2;                    // bytes per row of x and of W
 
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     const uint64_t xb = (uint64_t)(uintptr_t)G.x, wbp = (uint64_t)(uintptr_t)G.w;
     const gu32x4 rx = {(uint32_t)xb, (uint32_t)(xb >> 32) & 0xffffu, (uint32_t)G.M * rowb, 0x00020000u};
     const gu32x4 rw = {(uint32_t)wbp, (uint32_t)(wbp >> 32) & 0xffffu, (uint32_t)G.N * rowb, 0x00020000u};
-    // wave w copies 8-row groups w, w+8, w+16, w+24 of the x tile and of the W tile
+    // wave w copies 8-row groups w, w+8, ..., w+40 of the x tile and w, ..., w+24 of the W tile
     const int wv = __builtin_amdgcn_readfirstlane(wave);       // wave-uniform, for scalar DMA operands
     // lane l of a 1 KB copy lands at row 8 grp + l/8, position l%8 of the row,
     // which holds chunk (l%8) ^ ((row / 2) % 8) = (l%8) ^ (l/16 + 4 (grp % 2));
@@ -130,16 +136,20 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     auto copy_step = [&](int t, int st) {
         const uint32_t kb = (uint32_t)t * (GK * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 6; ++i) {
             const int grp = wv + 8 * i;
             g_dma(lds0 + st * GSTAGE + 1024 * grp, voff, rx, (uint32_t)(m0 + 8 * grp) * rowb + kb);
-            g_dma(lds0 + st * GSTAGE + GTILE + 1024 * grp, voff, rw, (uint32_t)(n0 + 8 * grp) * rowb + kb);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int grp = wv + 8 * i;
+            g_dma(lds0 + st * GSTAGE + GTILEX + 1024 * grp, voff, rw, (uint32_t)(n0 + 8 * grp) * rowb + kb);
         }
     };
 
-    gf32x16 acc[2][4];
+    gf32x16 acc[3][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 3; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -154,20 +164,20 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
         lds_barrier();
         if (t + 1 < nsteps) copy_step(t + 1, (t + 1) & 1);
         const uint8_t* xt = lds + (t & 1) * GSTAGE;
-        const uint8_t* wt = xt + GTILE;
+        const uint8_t* wt = xt + GTILEX;
 #pragma unroll
         for (int kk = 0; kk < GK / 16; ++kk) {
             // raised wave priority over the first half of the step's products
             // (-1 to -3% on the model shapes)
             if (kk == 0) __builtin_amdgcn_s_setprio(2);
             if (kk == 2) __builtin_amdgcn_s_setprio(0);
-            gbf16x8 a[2], b[4];
+            gbf16x8 a[3], b[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = g_frag(xt, wm + 32 * i + l32, 2 * kk + g);
+            for (int i = 0; i < 3; ++i) a[i] = g_frag(xt, wm + 32 * i + l32, 2 * kk + g);
 #pragma unroll
             for (int j = 0; j < 4; ++j) b[j] = g_frag(wt, wn + 32 * j + l32, 2 * kk + g);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 3; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
 
     // acc[i][j] lane: column n0 + wn + 32 j + l32, rows m0 + wm + 32 i + 8 r4 + 4 g + r%4
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 3; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int n = n0 + wn + 32 * j + l32;
@@ -231,8 +241,8 @@ int launch_w8a16(const uint16_t* x, int64_t M, int64_t K, const int8_t* codes, c
     hipLaunchKernelGGL(w8_dequant_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, codes, scale,
                        wb, N, (int)K);
     if (M > 0) {
-        GemmArgs G{x, wb, y, (int32_t)M, (int32_t)N, (int32_t)K, (int32_t)((M + GT - 1) / GT), (int32_t)(N / GT)};
-        const int64_t blocks = ((M + GT - 1) / GT) * (N / GT);
+        GemmArgs G{x, wb, y, (int32_t)M, (int32_t)N, (int32_t)K, (int32_t)((M + GTM - 1) / GTM), (int32_t)(N / GT)};
+        const int64_t blocks = ((M + GTM - 1) / GTM) * (N / GT);
         hipLaunchKernelGGL(w8a16_gemm_kernel, dim3((unsigned)blocks), dim3(GNT), 0, stream, G);
     }
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
