@@ -24,9 +24,11 @@
 // row.  A row is 128 bytes, half of the 64 four-byte banks, so rows 2i and
 // 2i+1 cover the two halves; the swizzle by r / 2 spreads the 16 rows that a
 // ds_read_b128 serves per cycle over all 16 groups of 4 banks, free of
-// conflicts.  Two stages: step t+1
-// is copied into the stage step t-1 left while step t computes.  Reads of
+// conflicts.  With NS stages, step t+NS-1 is copied into the stage step t-1
+// left while step t computes (2 stages for the big tiles).  Reads of
 // x past row M come back as zeros (buffer range checking); stores stop at M.
+// Rows that would fill only a quarter or less of a last round of big tiles
+// (and calls too small to fill one) take 128 x 128 tiles from the same code.
 #include <mutex>
 
 #include "common.hpp"
@@ -37,13 +39,8 @@ typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
 typedef float gf32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t gu32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GT = 256;             // tile columns (W rows) per workgroup
-constexpr int GTM = 384;            // tile rows (x) per workgroup
 constexpr int GK = 64;              // K per step
-constexpr int GNT = 512;            // threads (8 waves)
-constexpr int GTILE = GT * GK * 2;  // bytes of one operand tile (32 KB)
-constexpr int GTILEX = GTM * GK * 2; // bytes of the x tile (48 KB)
-constexpr int GSTAGE = GTILEX + GTILE;   // x tile then W tile
+constexpr int GNT = 512;            // threads (8 waves: 4 along the tile's rows, 2 along its columns)
 constexpr int GGROUP = 8;           // row panels walked together by the tile order
 
 // ---------------------------------------------------------------------------
@@ -97,8 +94,18 @@ __device__ __forceinline__ gbf16x8 g_frag(const uint8_t* tile, int row, int ch) 
     return *reinterpret_cast<const gbf16x8*>(tile + row * (GK * 2) + 16 * (ch ^ ((row >> 1) & 7)));
 }
 
+// TM x TN tile per workgroup with NS LDS stages: 384 x 256 (96 x 128 per
+// wave, 2 stages) for the bulk of a call, 128 x 128 (32 x 64 per wave) for
+// rows that would leave the last round of big tiles mostly idle; a small
+// tile's step computes too briefly to hide one copy's latency, so it keeps
+// 4 stages (3 steps in flight).
+template <int TM, int TN, int NS>
 __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * GSTAGE];
+    constexpr int XB = TM * GK * 2;                 // bytes of the x tile of a step
+    constexpr int STAGE = (TM + TN) * GK * 2;       // x tile then W tile
+    constexpr int WMB = TM / 128, WNB = TN / 64;    // 32 x 32 accumulator blocks per wave
+    constexpr int PER = TM / 64 + TN / 64;          // DMA instructions per wave and step
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8).  Index
@@ -117,8 +124,8 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     const int gm = min(G.ntm - fm, GGROUP), rr = tile - grp * span;     // the last group may hold fewer rows
     const int tm = __builtin_amdgcn_readfirstlane(fm + rr % gm);
     const int tn = __builtin_amdgcn_readfirstlane(rr / gm);
-    const int m0 = tm * GTM, n0 = tn * GT;
-    const int wm = 96 * (wave & 3), wn = 128 * (wave >> 2);
+    const int m0 = tm * TM, n0 = tn * TN;
+    const int wm = (TM / 4) * (wave & 3), wn = (TN / 2) * (wave >> 2);
     const int nsteps = G.K / GK;
     const uint32_t rowb = (uint32_t)G.K * 2;                    // bytes per row of x and of W
 
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     const uint64_t xb = (uint64_t)(uintptr_t)G.x, wbp = (uint64_t)(uintptr_t)G.w;
     const gu32x4 rx = {(uint32_t)xb, (uint32_t)(xb >> 32) & 0xffffu, (uint32_t)G.M * rowb, 0x00020000u};
     const gu32x4 rw = {(uint32_t)wbp, (uint32_t)(wbp >> 32) & 0xffffu, (uint32_t)G.N * rowb, 0x00020000u};
-    // wave w copies 8-row groups w, w+8, ..., w+40 of the x tile and w, ..., w+24 of the W tile
+    // wave w copies 8-row groups w, w+8, ... of the x tile and of the W tile
     const int wv = __builtin_amdgcn_readfirstlane(wave);       // wave-uniform, for scalar DMA operands
     // lane l of a 1 KB copy lands at row 8 grp + l/8, position l%8 of the row,
     // which holds chunk (l%8) ^ ((row / 2) % 8) = (l%8) ^ (l/16 + 4 (grp % 2));
@@ -136,59 +143,63 @@ __global__ __launch_bounds__(GNT) void w8a16_gemm_kernel(const GemmArgs G) {
     auto copy_step = [&](int t, int st) {
         const uint32_t kb = (uint32_t)t * (GK * 2);
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
+        for (int i = 0; i < TM / 64; ++i) {
             const int grp = wv + 8 * i;
-            g_dma(lds0 + st * GSTAGE + 1024 * grp, voff, rx, (uint32_t)(m0 + 8 * grp) * rowb + kb);
+            g_dma(lds0 + st * STAGE + 1024 * grp, voff, rx, (uint32_t)(m0 + 8 * grp) * rowb + kb);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < TN / 64; ++i) {
             const int grp = wv + 8 * i;
-            g_dma(lds0 + st * GSTAGE + GTILEX + 1024 * grp, voff, rw, (uint32_t)(n0 + 8 * grp) * rowb + kb);
+            g_dma(lds0 + st * STAGE + XB + 1024 * grp, voff, rw, (uint32_t)(n0 + 8 * grp) * rowb + kb);
         }
     };
 
-    gf32x16 acc[3][4];
+    gf32x16 acc[WMB][WNB];
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < WMB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < WNB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    copy_step(0, 0);
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nsteps) copy_step(p, p);
     for (int t = 0; t < nsteps; ++t) {
-        // this wave's copies of step t are in; after the barrier every wave's
-        // are, and every wave is past its reads of step t-1, whose stage step
-        // t+1 now fills while step t computes
-        g_wait<0>();
+        // this wave's copies of step t are in once at most the NS - 2 later
+        // steps' copies are outstanding (near the end: none, conservatively);
+        // after the barrier every wave's are, and every wave is past its reads
+        // of step t-1, whose stage step t+NS-1 now fills
+        if (t + NS - 2 < nsteps) g_wait<(NS - 2) * PER>();
+        else g_wait<0>();
         lds_barrier();
-        if (t + 1 < nsteps) copy_step(t + 1, (t + 1) & 1);
-        const uint8_t* xt = lds + (t & 1) * GSTAGE;
-        const uint8_t* wt = xt + GTILEX;
+        if (t + NS - 1 < nsteps) copy_step(t + NS - 1, (t + NS - 1) % NS);
+        const uint8_t* xt = lds + (t % NS) * STAGE;
+        const uint8_t* wt = xt + XB;
 #pragma unroll
         for (int kk = 0; kk < GK / 16; ++kk) {
             // raised wave priority over the first half of the step's products
             // (-1 to -3% on the model shapes)
             if (kk == 0) __builtin_amdgcn_s_setprio(2);
             if (kk == 2) __builtin_amdgcn_s_setprio(0);
-            gbf16x8 a[3], b[4];
+            gbf16x8 a[WMB], b[WNB];
 #pragma unroll
-            for (int i = 0; i < 3; ++i) a[i] = g_frag(xt, wm + 32 * i + l32, 2 * kk + g);
+            for (int i = 0; i < WMB; ++i) a[i] = g_frag(xt, wm + 32 * i + l32, 2 * kk + g);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = g_frag(wt, wn + 32 * j + l32, 2 * kk + g);
+            for (int j = 0; j < WNB; ++j) b[j] = g_frag(wt, wn + 32 * j + l32, 2 * kk + g);
 #pragma unroll
-            for (int i = 0; i < 3; ++i)
+            for (int i = 0; i < WMB; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < WNB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
 
     // acc[i][j] lane: column n0 + wn + 32 j + l32, rows m0 + wm + 32 i + 8 r4 + 4 g + r%4
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < WMB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < WNB; ++j) {
             const int n = n0 + wn + 32 * j + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -234,6 +245,21 @@ int w8a16_scratch(void** out) {
     return NOMAS_OK;
 }
 
+namespace {
+int dev_current() {
+    int d = 0;
+    return hipGetDevice(&d) == hipSuccess ? d : 0;
+}
+
+template <int TM, int TN, int NS>
+void gemm_launch(const uint16_t* x, const uint16_t* wb, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                 hipStream_t stream) {
+    const int64_t ntm = (M + TM - 1) / TM, ntn = N / TN;
+    const GemmArgs G{x, wb, y, (int32_t)M, (int32_t)N, (int32_t)K, (int32_t)ntm, (int32_t)ntn};
+    hipLaunchKernelGGL((w8a16_gemm_kernel<TM, TN, NS>), dim3((unsigned)(ntm * ntn)), dim3(GNT), 0, stream, G);
+}
+}  // namespace
+
 int launch_w8a16(const uint16_t* x, int64_t M, int64_t K, const int8_t* codes, const float* scale, int64_t N,
                  uint16_t* y, void* workspace, hipStream_t stream) {
     uint16_t* wb = static_cast<uint16_t*>(workspace);
@@ -241,9 +267,18 @@ int launch_w8a16(const uint16_t* x, int64_t M, int64_t K, const int8_t* codes, c
     hipLaunchKernelGGL(w8_dequant_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, codes, scale,
                        wb, N, (int)K);
     if (M > 0) {
-        GemmArgs G{x, wb, y, (int32_t)M, (int32_t)N, (int32_t)K, (int32_t)((M + GTM - 1) / GTM), (int32_t)(N / GT)};
-        const int64_t blocks = ((M + GTM - 1) / GTM) * (N / GT);
-        hipLaunchKernelGGL(w8a16_gemm_kernel, dim3((unsigned)blocks), dim3(GNT), 0, stream, G);
+        // Big tiles for the whole row panels that fill complete rounds of the
+        // device's CUs (one workgroup per CU); when the last round would be at
+        // most a quarter full, the rows after those panels go to 128 x 128
+        // tiles instead, about a sixth of a big tile's time each.  Every
+        // output is still summed over K in one workgroup, in the same order.
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev_current()) != hipSuccess || cus < 1)
+            return NOMAS_EHIP;
+        const int64_t ntn = N / 256, nb = ((M + 383) / 384) * ntn, tail = nb % cus;
+        const int64_t mmain = (tail > 0 && 4 * tail <= cus) ? ((nb - tail) / ntn) * 384 : M;
+        if (mmain > 0) gemm_launch<384, 256, 2>(x, wb, y, mmain, N, K, stream);
+        if (mmain < M) gemm_launch<128, 128, 4>(x + mmain * K, wb, y + mmain * N, M - mmain, N, K, stream);
     }
     return hipGetLastError() == hipSuccess ? NOMAS_OK : NOMAS_EHIP;
 }

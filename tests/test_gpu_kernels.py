@@ -471,16 +471,20 @@ def test_w8a16_linear_matches_oracle(M, K, N):
     assert_close(f64(y), ref, "w8a16 M=%d K=%d N=%d" % (M, K, N))
 
 
-def test_w8a16_linear_model_shape_sampled():
-    """The FFN up projection of one 12 s segment: 63,360 tokens x 2048 -> 8192,
-    sampled rows (including the ragged last tile) against the oracle."""
-    M, K, N = 63360, 2048, 8192
-    x, codes, s = _w8_inputs(M, K, N, 777)
+@pytest.mark.parametrize("K,N", [(2048, 8192), (2048, 2048)], ids=["ffn-up", "out-proj"])
+def test_w8a16_linear_model_shape_sampled(K, N):
+    """Linear layers of one 12 s segment, 63,360 tokens: the FFN up projection
+    (2048 -> 8192, big tiles throughout) and the output projection (2048 ->
+    2048: its last round of big tiles would be 40 of 256 tiles, so rows from
+    61,440 on take the small tiles).  Sampled rows on both sides of that
+    boundary and the ragged last tile against the oracle."""
+    M = 63360
+    x, codes, s = _w8_inputs(M, K, N, 777 + N)
     y = nomas.w8a16_linear(dev16(x), dev(codes), dev(s))
     torch.cuda.synchronize()
-    rows = np.array(sorted(set(range(0, M, 997)) | set(range(M - 40, M))))
+    rows = np.array(sorted(set(range(0, M, 997)) | set(range(61430, 61450)) | set(range(M - 40, M))))
     ref = oracle.w8a16_linear(x, codes, s, rows=rows)
-    assert_close(f64(y)[rows], ref, "w8a16 model shape")
+    assert_close(f64(y)[rows], ref, "w8a16 model shape K=%d N=%d" % (K, N))
 
 
 # ----------------------------------------------------------------------------
