@@ -48,6 +48,23 @@ def assert_close(got, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2):
     return e, r
 
 
+def assert_bf16_output(got, ref, what, rel_l2=REL_L2):
+    """Bar for a result that the kernel rounds once to bf16 from an fp32 sum
+    (the W8A16 linear layer): each element within 2^-7 |ref| (twice the
+    half-ulp bound 2^-8 |ref| of one bf16 rounding) plus 10^-4 of the
+    largest |ref| for the fp32 accumulation, and rel-L2 <= rel_l2.  An
+    absolute bar does not fit here: outputs of magnitude 8 or more already
+    round by up to 2^-5."""
+    assert np.all(np.isfinite(got)), "%s: non-finite output" % what
+    d = np.abs(got - ref)
+    bound = 2.0 ** -7 * np.abs(ref) + 1e-4 * float(np.abs(ref).max())
+    worst = float((d / bound).max()) if d.size else 0.0
+    e, r = errs(got, ref) if d.size else (0.0, 0.0)
+    say("%s: max-abs %.3e rel-L2 %.3e, worst error / element bound %.3f" % (what, e, r, worst))
+    assert worst <= 1.0 and r <= rel_l2, "%s: max-abs %.3e rel-L2 %.3e worst/bound %.3f" % (what, e, r, worst)
+    return e, r
+
+
 def cache_tensors(H, cap):
     kc = torch.zeros((H, cap, 128), dtype=torch.int8, device=DEV)
     vc = torch.zeros((H, cap, 128), dtype=torch.int8, device=DEV)
