@@ -4,7 +4,9 @@ Besides the hand-picked edge cases of the other GPU tests, each entry point
 runs on configurations drawn from a fixed generator: segment mixes with
 empty, text-only and ragged video segments, cache lengths from none to a few
 hundred tokens, forced key-range parts, history selections, 1 to 3 heads,
-and linear-layer shapes around the GEMM's tile sizes.  The bars are those of
+linear-layer shapes around the GEMM's tile sizes, and random lengths, head
+counts, offsets and camera-token counts for the RoPE, quantise-and-append,
+camera and grouped-head entry points.  The bars are those of
 the hand-picked cases (the helpers are shared with them)."""
 import math
 
@@ -15,7 +17,7 @@ import torch
 import oracle
 import segment_causal_attention_amd as nomas
 import synth
-from gpu_util import assert_bf16_output, dev, dev16, f64, say
+from gpu_util import SM, assert_bf16_output, assert_close, bits, cache_tensors, dev, dev16, f64, say
 from test_gpu_bwd import _close3, _grads_gpu
 from test_gpu_kernels import _check_case
 
@@ -110,3 +112,79 @@ def test_w8a16_random_shapes(M, K, N):
     assert tuple(y.shape) == (M, N)
     if M:
         assert_bf16_output(f64(y), oracle.w8a16_linear(x, codes, s), "w8a16 M=%d K=%d N=%d" % (M, K, N))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_rope3d_random_configs(seed):
+    """Bit-level, as the hand-picked rope3d cases: at most one bf16 ulp from
+    the oracle's float64 rotation rounded once, in under 1e-5 of the values."""
+    rng = np.random.default_rng(9900 + seed)
+    segs = _random_segs(rng, 5)
+    H = int(rng.integers(1, 17))
+    L = sum(s[0] + s[2] * s[3] * s[4] for s in segs)
+    x = synth.random_bf16(9910 + seed, (L, H, 128), 3.0)
+    say("rope3d random-%d L %d H %d segs %s" % (seed, L, H, segs))
+    y = nomas.rope3d(dev16(x), segs)
+    torch.cuda.synchronize()
+    ref = oracle.f64_to_bf16_bits(oracle.bf16_round(oracle.rope3d(oracle.bf16_bits_to_f64(x), segs)))
+    got = bits(y)
+    diff = got != ref
+    if diff.any():
+        assert np.abs(got[diff].astype(np.int32) - ref[diff].astype(np.int32)).max() <= 1
+    assert diff.mean() < 1e-5
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_kv_quant_append_random_configs(seed):
+    """Bit-exact codes and scales, appended at a random offset of a cache
+    with room to spare; entries outside the appended range untouched."""
+    rng = np.random.default_rng(9920 + seed)
+    L, H = int(rng.integers(1, 3000)), int(rng.integers(1, 17))
+    start = int(rng.integers(0, 500))
+    cap = start + L + int(rng.integers(0, 40))
+    k = synth.random_bf16(9930 + seed, (L, H, 128), float(rng.choice([1e-3, 1.0, 30.0])))
+    v = synth.random_bf16(9940 + seed, (L, H, 128))
+    say("kv_quant_append random-%d L %d H %d start %d cap %d" % (seed, L, H, start, cap))
+    kc, vc, ks, vs = cache_tensors(H, cap)
+    kc.fill_(55)
+    vs.fill_(-2.0)
+    assert nomas.kv_quant_append(dev16(k), dev16(v), kc, vc, ks, vs, start) == start + L
+    torch.cuda.synchronize()
+    for src, codes, scales in ((k, kc, ks), (v, vc, vs)):
+        qo, so = oracle.quantise(oracle.bf16_bits_to_f64(src))
+        assert np.array_equal(codes.cpu().numpy()[:, start:start + L].transpose(1, 0, 2), qo)
+        assert np.array_equal(scales.cpu().numpy()[:, start:start + L].T.view(np.uint32), so.view(np.uint32))
+    assert torch.all(kc[:, :start] == 55) and torch.all(kc[:, start + L:] == 55)
+    assert torch.all(vs[:, :start] == -2.0) and torch.all(vs[:, start + L:] == -2.0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cam_xattn_random_configs(seed):
+    rng = np.random.default_rng(9950 + seed)
+    Lq, H, Nc = int(rng.integers(1, 5000)), int(rng.integers(1, 5)), int(rng.integers(1, 129))
+    q = synth.random_bf16(9960 + seed, (Lq, H, 128))
+    wk = synth.random_bf16(9970 + seed, (64, H * 128), 1 / 8)
+    wv = synth.random_bf16(9980 + seed, (64, H * 128), 1 / 8)
+    cam = oracle.cam_tokens(synth.camera_path(seed, 7, 4 * Nc)).astype(np.float32)
+    say("cam_xattn random-%d Lq %d H %d Nc %d" % (seed, Lq, H, Nc))
+    out = nomas.cam_xattn(dev16(q), dev(cam), dev16(wk), dev16(wv), sm_scale=SM)
+    torch.cuda.synchronize()
+    assert_close(f64(out), oracle.cam_xattn(q, cam, wk, wv, SM), "cam_xattn random-%d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_gqa_attn_random_configs(seed):
+    rng = np.random.default_rng(9990 + seed)
+    Hkv = int(rng.integers(1, 5))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+    L = int(rng.integers(1, 2500))
+    q = synth.random_bf16(10000 + seed, (L, Hq, 128))
+    k = synth.random_bf16(10010 + seed, (L, Hkv, 128))
+    v = synth.random_bf16(10020 + seed, (L, Hkv, 128))
+    say("gqa_attn random-%d L %d Hq %d Hkv %d" % (seed, L, Hq, Hkv))
+    lse = torch.empty((Hq, L), dtype=torch.float32, device="cuda:0")
+    out = nomas.gqa_attn(dev16(q), dev16(k), dev16(v), sm_scale=SM, lse=lse)
+    torch.cuda.synchronize()
+    ref, lref = oracle.gqa_attn(q, k, v, SM)
+    assert_close(f64(out), ref, "gqa random-%d" % seed)
+    np.testing.assert_allclose(lse.cpu().numpy(), lref, rtol=0, atol=2.0 ** -8)
