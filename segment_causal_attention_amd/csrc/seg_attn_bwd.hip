@@ -284,9 +284,12 @@ constexpr int KFD = 1;              // the same for dK/dV (its registers hold P 
 // ---- dQ: lane = query --------------------------------------------------------
 //
 // Per key tile and wave (32 queries x 64 keys, 48 products): the products of
-// key block 0 (S^T and dP^T alternating), those of key block 1 with the dS of
-// block 0 in their slots, the dQ^T products of block 0 with the dS of block 1
-// (two scores per slot), then the dQ^T products of block 1.
+// key block 0 (S^T and dP^T alternating) with the dS of the previous tile's
+// block 1 in their slots, those of key block 1 with the dS of block 0 in
+// theirs, then the dQ^T products of the previous tile's block 1 and of this
+// tile's block 0: one score per slot and stage throughout, so that the
+// vector work of each score hides behind a product.  Tiles are copied two
+// ahead, so the previous tile's buffer is still intact.
 
 __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[KBUF * KIMG];
@@ -330,43 +333,61 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
     f16v negd;              // -D: the initial dP^T accumulator, so that dP - D comes out of the products
 #pragma unroll
     for (int r = 0; r < 16; ++r) negd[r] = -dd;
+    // The fourth buffer starts zeroed: the first tile's products for "the
+    // previous tile's block 1" read it, with dS = 0, before any tile lands there.
+    {
+        uint4* z = reinterpret_cast<uint4*>(lds + (KBUF - 1) * KIMG);
+        for (int i = tid; i < KIMG / 16; i += NT) z[i] = make_uint4(0, 0, 0, 0);
+    }
     copy(0);
     copy(1);
-    copy(2);
-    // tile j lives in buffer j % 4; the loop is unrolled by 4 so that every
-    // LDS operand address is the lane's base plus an immediate offset
+    // Block 1 of a tile is finished in the next tile's slots, so its scores
+    // (s[1], dp[1]) and then its dS (pk[8..15]) carry over; before the first
+    // tile they give dS = 0 (2^(-1e30 c - lse) = 0, times dP - D = 0).
+    f16v s[2], dp[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        s[1][r] = -1e30f;
+        dp[1][r] = 0.0f;
+    }
+    uint32_t pk[16];
+    float tx[8];
+    float pe = 0.0f;
+    // score e (0..31; block e / 16, register e % 16) through stage st:
+    // 0: x = S c - lse2;  1: x = 2^x;  2: dS = x (dP - D), packed in pairs
+    auto stage = [&](int st, int e) {
+        const int kb = e >> 4, r = e & 15, i8 = e & 7;
+        if (st == 0) {
+            tx[i8] = fmaf(s[kb][r], c, -lse2);
+        } else if (st == 1) {
+            tx[i8] = __builtin_amdgcn_exp2f(tx[i8]);
+        } else {
+            const float v = tx[i8] * dp[kb][r];
+            if (r & 1) pk[e >> 1] = pack_bf16(pe, v);
+            else pe = v;
+        }
+    };
+    // tile j lives in buffer j % 4, tile j-1 (whose block 1 is finished here)
+    // in the one before; the loop is unrolled by 4 so that every LDS operand
+    // address is the lane's base plus an immediate offset
     auto tile_step = [&](int j, auto bufc) {
         constexpr int bi = decltype(bufc)::value;
-        // this wave's copies of tile j have landed once at most those of tiles j+1, j+2 are in flight
-        if (wv < KIMG_KB % NW) dma_wait<2 * ((KIMG_KB + NW - 1) / NW)>();
-        else dma_wait<2 * (KIMG_KB / NW)>();
+        constexpr int bp = (bi + KBUF - 1) % KBUF;
+        // this wave's copies of tile j have landed once at most those of tile j+1 are in flight
+        if (wv < KIMG_KB % NW) dma_wait<(KIMG_KB + NW - 1) / NW>();
+        else dma_wait<KIMG_KB / NW>();
         lds_barrier();
-        copy(j + 3);        // into the buffer of tile j-1, which every wave has finished
+        copy(j + 2);        // into the buffer of tile j-2, which every wave has finished
         const uint8_t* K = lds + bi * KIMG;
-        // operand of product n: 0-31 S^T / dP^T of key blocks 0 and 1
-        // (even n: K rows, odd n: V rows; channel step (n % 16) / 2), 32-47
-        // dQ^T: channel block (n - 32) % 4, 16-key chunk (n - 32) / 4
+        const uint8_t* Kp = lds + bp * KIMG;
+        // operand of product n: 0-31 S^T / dP^T of key blocks 0 and 1 of tile j
+        // (even n: K rows, odd n: V rows; channel step (n % 16) / 2); 32-39
+        // dQ^T of tile j-1's block 1 (channel block (n - 32) % 4, 16-key chunk
+        // 2 + (n - 32) / 4); 40-47 dQ^T of tile j's block 0 (chunk (n - 40) / 4)
         auto afrag = [&](int n) {
             if (n < 32) return rowfrag(K + ((n & 1) ? KI_V : 0), 32 * (n >> 4) + l32, (n & 15) >> 1, g);
-            return trfrag(K, 32 * ((n - 32) & 3), (n - 32) >> 2, lane);
-        };
-        f16v s[2], dp[2];
-        uint32_t pk[16];
-        float tx[8];
-        float pe = 0.0f;
-        // score e (0..31; block e / 16, register e % 16) through stage st:
-        // 0: x = S c - lse2;  1: x = 2^x;  2: dS = x (dP - D), packed in pairs
-        auto stage = [&](int st, int e) {
-            const int kb = e >> 4, r = e & 15, i8 = e & 7;
-            if (st == 0) {
-                tx[i8] = fmaf(s[kb][r], c, -lse2);
-            } else if (st == 1) {
-                tx[i8] = __builtin_amdgcn_exp2f(tx[i8]);
-            } else {
-                const float v = tx[i8] * dp[kb][r];
-                if (r & 1) pk[e >> 1] = pack_bf16(pe, v);
-                else pe = v;
-            }
+            if (n < 40) return trfrag(Kp, 32 * ((n - 32) & 3), 2 + ((n - 32) >> 2), lane);
+            return trfrag(K, 32 * ((n - 40) & 3), (n - 40) >> 2, lane);
         };
         b8 fr[48];
 #pragma unroll
@@ -378,25 +399,26 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
             // raised wave priority over the S^T / dP^T products (-1% measured)
             if (n == 0) __builtin_amdgcn_s_setprio(2);
             if (n == 32) __builtin_amdgcn_s_setprio(0);
+            // vector work first, one score per slot and stage: tile j-1's
+            // block 1 in slots 0-17, tile j's block 0 in slots 16-33.  It reads
+            // s[1] and dp[1] before this slot's product restarts their chains.
+#pragma unroll
+            for (int st = 0; st < 3; ++st) {
+                const int e1 = n - st;
+                if (e1 >= 0 && e1 < 16) stage(st, 16 + e1);
+                const int e0 = n - 16 - st;
+                if (e0 >= 0 && e0 < 16) stage(st, e0);
+            }
             if (n < 32) {
                 const int kb = n >> 4, m = n & 15;
                 if (m & 1) dp[kb] = mma(fr[n], df[m >> 1], m < 2 ? negd : dp[kb]);
                 else s[kb] = mma(fr[n], qf[m >> 1], m < 2 ? zero : s[kb]);
-            } else {
+            } else if (n < 40) {
                 const int m = n - 32;
+                acc[m & 3] = mma(fr[n], chunk4(pk + 8 + 4 * (m >> 2)), acc[m & 3]);
+            } else {
+                const int m = n - 40;
                 acc[m & 3] = mma(fr[n], chunk4(pk + 4 * (m >> 2)), acc[m & 3]);
-            }
-            // dS of block 0 in slots 16-33 (one score per slot), of block 1 in
-            // slots 32-41 (two per slot)
-#pragma unroll
-            for (int st = 0; st < 3; ++st) {
-                const int e0 = n - 16 - st;
-                if (e0 >= 0 && e0 < 16) stage(st, e0);
-                const int e1 = 2 * (n - 32 - st);
-                if (e1 >= 0 && e1 < 16) {
-                    stage(st, 16 + e1);
-                    stage(st, 17 + e1);
-                }
             }
             SLOT();
         }
@@ -406,6 +428,17 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(const BwdArgs A) {
         if (j + 1 < nk) tile_step(j + 1, std::integral_constant<int, 1>{});
         if (j + 2 < nk) tile_step(j + 2, std::integral_constant<int, 2>{});
         if (j + 3 < nk) tile_step(j + 3, std::integral_constant<int, 3>{});
+    }
+    // the last tile's block 1: its dS and dQ^T products
+    {
+        const uint8_t* Kl = lds + ((nk - 1) % KBUF) * KIMG;
+#pragma unroll
+        for (int e1 = 0; e1 < 16; ++e1)
+#pragma unroll
+            for (int st = 0; st < 3; ++st) stage(st, 16 + e1);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[m & 3] = mma(trfrag(Kl, 32 * (m & 3), 2 + (m >> 2), lane), chunk4(pk + 8 + 4 * (m >> 2)), acc[m & 3]);
     }
     dma_wait<0>();
 
